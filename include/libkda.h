@@ -1,0 +1,173 @@
+/*
+ * libkda -- Kimi Delta Attention (KDA) forward pass on AMD Instinct MI355X
+ * (gfx950), C ABI.
+ *
+ * THE OPERATION.  Per (sequence, head) the library runs the KDA recurrence with
+ * an fp32 state S of d_v rows (value channels) by d_k columns (key channels):
+ *
+ *   S~_t = S_{t-1} Diag(alpha_t),  alpha_t = exp(log_alpha_t)  (per key channel)
+ *   e_t  = beta_t (v_t - S~_t k_t)                              (prediction error)
+ *   S_t  = S~_t + e_t k_t^T                                     (write)
+ *   o_t  = S_t q_t                                              (readout)
+ *
+ * Sources: "KDA derivation summary" page (hn.213312.xyz article 49085909),
+ * sect. 3 (predict / error / write, readout S_t|q_t>) and sect. 5 (per-column,
+ * i.e. per-key-channel, decay D_t applied before the prediction); "Kimi K3
+ * notes 1: KDA" page (jaimeyzzz.com), sect. 4 and the summary box of sect. 5
+ * (the same update written for the transposed d_k x d_v state).  There is no
+ * query scale and no normaliser; the readout uses the post-write state.
+ *
+ * Two schedules of this one recurrence (same page, sect. 6): the chunkwise
+ * prefill (kda_chunk_fwd*) and the token-by-token decode step
+ * (kda_recurrent_step*).  Both give the recurrence's result up to floating
+ * point rounding.
+ *
+ * LAYOUTS (row-major, last index fastest; "token-major"):
+ *   q, k, log_alpha : [B, T, H, dk]        v, out : [B, T, H, dv]
+ *   beta            : [B, T, H]            S0, S_final, S : [B, H, dv, dk]
+ * bf16 tensors are IEEE bfloat16 (the upper half of an IEEE float32);
+ * log_alpha, beta and every state are fp32.  In the *_f32 entry points q, k,
+ * v and out are fp32 as well.
+ *
+ * OWNERSHIP AND EXECUTION.  Every pointer is device memory owned by the
+ * caller.  The library allocates nothing, keeps no mutable global state and is
+ * thread-safe.  Work is enqueued asynchronously on `stream` (a hipStream_t
+ * passed as void*; NULL is the default stream).  KDA_OK means "validated and
+ * enqueued"; faults inside a kernel surface at the caller's next
+ * synchronisation of that stream.
+ *
+ * ERRORS.  Status codes only; the library never aborts and throws nothing
+ * across the ABI.  All argument checks run before any HIP call, so an invalid
+ * call has no side effect.  kda_last_error() gives a message for the calling
+ * thread's last failed call.
+ *
+ * SUPPORTED SHAPES.  dk, dv in {16, 32, 64, 128}; C in {16, 32, 64} (bf16
+ * entry points), C in {16, 32} plus C = 64 for dk <= 64 (fp32 entry points).
+ * B, T, H, N >= 0 (a batch with no tokens only writes S_final).  Pointers to
+ * q, k, v, out, log_alpha, S0, S_final and S must be 16-byte aligned; beta
+ * 4-byte aligned.
+ *
+ * VALUE PRECONDITIONS (documented, not checked): log_alpha finite and <= 0;
+ * beta in [0, 1]; q and k L2-normalised by the caller ("Kimi K3 notes 1"
+ * page, sect. 4: q, k pass a feature map and an L2 normalisation first).
+ * The chunk kernels factor the intra-chunk decay relative to 16-token
+ * sub-blocks; they need every key channel to decay by less than 80 nats
+ * (e^-80) inside any 16-token sub-block of the chunk grid, which holds
+ * whenever log_alpha >= -5.
+ */
+#ifndef LIBKDA_H
+#define LIBKDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL_POINTER = 1,  /* a required pointer is NULL */
+    KDA_ERR_BAD_SHAPE = 2,     /* negative size, H < 1, inconsistent sizes */
+    KDA_ERR_UNSUPPORTED = 3,   /* dk, dv or C outside the supported set */
+    KDA_ERR_MISALIGNED = 4,    /* pointer alignment below what the loads need */
+    KDA_ERR_HIP = 5,           /* the HIP runtime refused the launch */
+    KDA_ERR_ALIASING = 6       /* out overlaps an input, or S_final partially overlaps S0 */
+} kda_status_t;
+
+/*
+ * Chunkwise prefill, bf16 inputs ("KDA derivation summary" page, sect. 6,
+ * chunk mode; the chunk skeleton of the "Linear/sparse attention tutorial"
+ * page, sect. 6.2).  Inside each chunk of C tokens the kernel forms the
+ * cumulative log-decay, the strictly lower-triangular K K^T system whose
+ * solution corrects each token's provisional error, the causal Q K^T block,
+ * and hands the fp32 state to the next chunk.
+ *
+ *   q, k     bf16 [B,T,H,dk]  (L2-normalised rows)
+ *   v        bf16 [B,T,H,dv]
+ *   log_alpha fp32 [B,T,H,dk], natural log of the per-channel decay (<= 0)
+ *   beta     fp32 [B,T,H]
+ *   S0       fp32 [B,H,dv,dk] incoming state; NULL = zero state
+ *   out      bf16 [B,T,H,dv]  o_t (round-to-nearest-even from fp32)
+ *   S_final  fp32 [B,H,dv,dk] state after token T-1; NULL = not written.
+ *            May be the same pointer as S0 (in-place continuation).
+ *   C        chunk length; T need not be a multiple of C.
+ */
+kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v,
+                           const float *log_alpha, const float *beta,
+                           const float *S0, void *out, float *S_final,
+                           int B, int T, int H, int dk, int dv, int C,
+                           void *stream);
+
+/* Same as kda_chunk_fwd with fp32 q, k, v and out (all arithmetic in fp32). */
+kda_status_t kda_chunk_fwd_f32(const float *q, const float *k, const float *v,
+                               const float *log_alpha, const float *beta,
+                               const float *S0, float *out, float *S_final,
+                               int B, int T, int H, int dk, int dv, int C,
+                               void *stream);
+
+/*
+ * Chunkwise prefill over N sequences packed along the token axis of one
+ * [1, T_total, H, d] stream.  Sequence n owns tokens
+ * [cu_seqlens[n], cu_seqlens[n+1]); its chunk grid starts at its first token
+ * and its partial last chunk is padded with identity tokens (k = 0, beta = 0,
+ * log_alpha = 0, which leave the state unchanged).  S0 / S_final are
+ * [N, H, dv, dk].  cu_seqlens is DEVICE memory, int32 [N+1]; precondition
+ * (not checked on the device): cu_seqlens[0] = 0, non-decreasing,
+ * cu_seqlens[N] = T_total.  kda_check_cu_seqlens_host() checks a host copy.
+ */
+kda_status_t kda_chunk_fwd_varlen(const void *q, const void *k, const void *v,
+                                  const float *log_alpha, const float *beta,
+                                  const float *S0, void *out, float *S_final,
+                                  const int32_t *cu_seqlens, int N, int T_total,
+                                  int H, int dk, int dv, int C, void *stream);
+
+/* fp32 q, k, v, out variant of kda_chunk_fwd_varlen. */
+kda_status_t kda_chunk_fwd_varlen_f32(const float *q, const float *k, const float *v,
+                                      const float *log_alpha, const float *beta,
+                                      const float *S0, float *out, float *S_final,
+                                      const int32_t *cu_seqlens, int N, int T_total,
+                                      int H, int dk, int dv, int C, void *stream);
+
+/*
+ * One decode step ("KDA derivation summary" page, sect. 6, fused recurrent
+ * mode; "Linear/sparse attention tutorial" page, sect. 8.1: a step reads and
+ * writes only the fixed-size state).  Advances N sequences by one token each:
+ *
+ *   q, k      bf16 [N,H,dk];  v, out bf16 [N,H,dv]
+ *   log_alpha fp32 [N,H,dk];  beta fp32 [N,H]
+ *   S         fp32 [N,H,dv,dk], updated IN PLACE from S_{t-1} to S_t.
+ *
+ * Each state row is read once and written once.
+ */
+kda_status_t kda_recurrent_step(const void *q, const void *k, const void *v,
+                                const float *log_alpha, const float *beta,
+                                float *S, void *out,
+                                int N, int H, int dk, int dv, void *stream);
+
+/* fp32 q, k, v, out variant of kda_recurrent_step. */
+kda_status_t kda_recurrent_step_f32(const float *q, const float *k, const float *v,
+                                    const float *log_alpha, const float *beta,
+                                    float *S, float *out,
+                                    int N, int H, int dk, int dv, void *stream);
+
+/*
+ * Host-side check of a cu_seqlens array held in HOST memory: N >= 0,
+ * cu[0] = 0, non-decreasing, cu[N] = T_total.  Returns KDA_OK or
+ * KDA_ERR_BAD_SHAPE / KDA_ERR_NULL_POINTER.
+ */
+kda_status_t kda_check_cu_seqlens_host(const int32_t *cu_seqlens_host, int N, int T_total);
+
+/* Static name of a status code. */
+const char *kda_status_string(kda_status_t status);
+
+/* Message describing the calling thread's last failed call ("" if none). */
+const char *kda_last_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBKDA_H */

@@ -1,0 +1,209 @@
+"""Python binding for libkda, the MI355X (gfx950) Kimi Delta Attention forward.
+
+The functions named ``kda_*`` mirror the C ABI of ``include/libkda.h`` one to
+one: they only marshal arguments (tensor -> device pointer, stream -> handle)
+and turn a non-OK status into :class:`KdaError`.  Every step of the
+computation runs in the HIP kernels of ``libkda.so``; there is no fallback.
+If the library has not been built, importing this package still works but the
+first call raises, naming the build command.
+
+Convenience wrappers (``chunk_fwd``, ``chunk_fwd_varlen``, ``recurrent_step``)
+infer sizes from tensor shapes and allocate outputs with torch; torch is used
+here for device memory and streams only.
+
+Layouts (token-major, last index fastest): q, k, log_alpha [B, T, H, dk];
+v, out [B, T, H, dv]; beta [B, T, H]; states [B, H, dv, dk] (fp32).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "KdaError", "library_path", "load",
+    "kda_chunk_fwd", "kda_chunk_fwd_f32", "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_f32",
+    "kda_recurrent_step", "kda_recurrent_step_f32", "kda_check_cu_seqlens_host",
+    "kda_status_string", "kda_last_error", "kda_version",
+    "chunk_fwd", "chunk_fwd_varlen", "recurrent_step",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkda.so")
+_lib = None
+
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL_POINTER", 2: "KDA_ERR_BAD_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
+          4: "KDA_ERR_MISALIGNED", 5: "KDA_ERR_HIP", 6: "KDA_ERR_ALIASING"}
+
+
+class KdaError(RuntimeError):
+    """A libkda call returned a status other than KDA_OK."""
+
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libkda.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built; run `python -m kimi_delta_attention_fwd_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    chunk = [P] * 8 + [I] * 6 + [P]
+    varlen = [P] * 9 + [I] * 6 + [P]
+    step = [P] * 7 + [I] * 4 + [P]
+    for name, args in (("kda_chunk_fwd", chunk), ("kda_chunk_fwd_f32", chunk),
+                       ("kda_chunk_fwd_varlen", varlen), ("kda_chunk_fwd_varlen_f32", varlen),
+                       ("kda_recurrent_step", step), ("kda_recurrent_step_f32", step)):
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = I
+    lib.kda_check_cu_seqlens_host.argtypes = [P, I, I]
+    lib.kda_check_cu_seqlens_host.restype = I
+    lib.kda_status_string.argtypes = [I]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = I
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    """Device pointer of a tensor (or an int address, or None -> NULL)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise KdaError(fn, status, load().kda_last_error().decode())
+
+
+# --- the C ABI, one to one -------------------------------------------------------------------
+def kda_chunk_fwd(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, dk, dv, C, stream=None):
+    _check("kda_chunk_fwd", load().kda_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_final),
+        B, T, H, dk, dv, C, _stream(stream)))
+
+
+def kda_chunk_fwd_f32(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, dk, dv, C, stream=None):
+    _check("kda_chunk_fwd_f32", load().kda_chunk_fwd_f32(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_final),
+        B, T, H, dk, dv, C, _stream(stream)))
+
+
+def kda_chunk_fwd_varlen(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N, T_total, H, dk, dv, C,
+                         stream=None):
+    _check("kda_chunk_fwd_varlen", load().kda_chunk_fwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_final),
+        _ptr(cu_seqlens), N, T_total, H, dk, dv, C, _stream(stream)))
+
+
+def kda_chunk_fwd_varlen_f32(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N, T_total, H, dk, dv,
+                             C, stream=None):
+    _check("kda_chunk_fwd_varlen_f32", load().kda_chunk_fwd_varlen_f32(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_final),
+        _ptr(cu_seqlens), N, T_total, H, dk, dv, C, _stream(stream)))
+
+
+def kda_recurrent_step(q, k, v, log_alpha, beta, S, out, N, H, dk, dv, stream=None):
+    _check("kda_recurrent_step", load().kda_recurrent_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(out), N, H, dk, dv,
+        _stream(stream)))
+
+
+def kda_recurrent_step_f32(q, k, v, log_alpha, beta, S, out, N, H, dk, dv, stream=None):
+    _check("kda_recurrent_step_f32", load().kda_recurrent_step_f32(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(out), N, H, dk, dv,
+        _stream(stream)))
+
+
+def kda_check_cu_seqlens_host(cu_seqlens_host, N, T_total) -> int:
+    """Check a host (CPU) int32 cu_seqlens; returns the status code."""
+    return load().kda_check_cu_seqlens_host(_ptr(cu_seqlens_host), N, T_total)
+
+
+def kda_status_string(status: int) -> str:
+    return load().kda_status_string(status).decode()
+
+
+def kda_last_error() -> str:
+    return load().kda_last_error().decode()
+
+
+def kda_version() -> int:
+    return load().kda_version()
+
+
+# --- convenience wrappers: sizes from shapes, outputs allocated with torch ---------------------
+def _mode(q):
+    import torch
+    if q.dtype == torch.bfloat16:
+        return False
+    if q.dtype == torch.float32:
+        return True
+    raise TypeError(f"q, k, v must be bfloat16 or float32, got {q.dtype}")
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, S0=None, C=64, output_final_state=True, stream=None):
+    """Chunk prefill of a dense batch.  Returns ``(out, S_final or None)``."""
+    import torch
+    f32 = _mode(q)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    sf = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device) if output_final_state else None
+    fn = kda_chunk_fwd_f32 if f32 else kda_chunk_fwd
+    fn(q, k, v, log_alpha, beta, S0, out, sf, B, T, H, dk, dv, C, stream)
+    return out, sf
+
+
+def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, C=64, output_final_state=True, stream=None):
+    """Chunk prefill of N packed sequences ([1, T_total, H, d] tensors, device cu_seqlens [N+1])."""
+    import torch
+    f32 = _mode(q)
+    _, T_total, H, dk = q.shape
+    dv = v.shape[-1]
+    N = cu_seqlens.shape[0] - 1
+    out = torch.empty((1, T_total, H, dv), dtype=q.dtype, device=q.device)
+    sf = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device) if output_final_state else None
+    fn = kda_chunk_fwd_varlen_f32 if f32 else kda_chunk_fwd_varlen
+    fn(q, k, v, log_alpha, beta, S0, out, sf, cu_seqlens, N, T_total, H, dk, dv, C, stream)
+    return out, sf
+
+
+def recurrent_step(q, k, v, log_alpha, beta, S, out=None, stream=None):
+    """One decode step on [N, H, d] tensors; S [N, H, dv, dk] fp32 is updated in place."""
+    import torch
+    f32 = _mode(q)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    fn = kda_recurrent_step_f32 if f32 else kda_recurrent_step
+    fn(q, k, v, log_alpha, beta, S, out, N, H, dk, dv, stream)
+    return out

@@ -1,0 +1,297 @@
+// libkda C ABI: argument validation and dispatch to the HIP kernels.
+//
+// Every check below runs before the first HIP call, so a rejected call has no
+// side effect and needs no GPU.  The operation, layouts and error codes are
+// documented in include/libkda.h.
+#include "libkda.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "kda_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kda_status_t fail(kda_status_t st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+kda_status_t ok()
+{
+    g_err[0] = '\0';
+    return KDA_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+bool supported_c(int c) { return c == 16 || c == 32 || c == 64; }
+
+// Byte ranges [p, p + n) overlap (empty ranges never do).
+bool overlap(const void *a, uint64_t na, const void *b, uint64_t nb)
+{
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+struct Buf {
+    const void *p;
+    uint64_t bytes;
+    const char *name;
+};
+
+// out and the state output must not overlap any input (S0 excluded from `ins`); the
+// state output may alias S0 only as the identical pointer.
+kda_status_t check_aliasing(const Buf &out, const Buf *ins, int nin, const Buf &sfin, const Buf &s0)
+{
+    for (int i = 0; i < nin; ++i) {
+        if (overlap(out.p, out.bytes, ins[i].p, ins[i].bytes))
+            return fail(KDA_ERR_ALIASING, "%s overlaps input %s", out.name, ins[i].name);
+        if (overlap(sfin.p, sfin.bytes, ins[i].p, ins[i].bytes))
+            return fail(KDA_ERR_ALIASING, "%s overlaps input %s", sfin.name, ins[i].name);
+    }
+    if (overlap(out.p, out.bytes, sfin.p, sfin.bytes))
+        return fail(KDA_ERR_ALIASING, "%s overlaps %s", out.name, sfin.name);
+    if (overlap(out.p, out.bytes, s0.p, s0.bytes))
+        return fail(KDA_ERR_ALIASING, "%s overlaps %s", out.name, s0.name);
+    if (sfin.p != s0.p && overlap(sfin.p, sfin.bytes, s0.p, s0.bytes))
+        return fail(KDA_ERR_ALIASING, "%s partially overlaps %s (only identical pointers may alias)",
+                    sfin.name, s0.name);
+    return KDA_OK;
+}
+
+// Value-block width of the chunk kernel: the widest block that still gives
+// every compute unit a workgroup (256 CUs), else the narrowest that fits.
+// KDA_CHUNK_BV overrides the choice for tuning.
+int choose_bv(bool f32, int dk, int dv, int C, long nheads)
+{
+    if (const char *env = std::getenv("KDA_CHUNK_BV")) {
+        const int bv = std::atoi(env);
+        if ((bv == 16 || bv == 32 || bv == 64) && bv <= dv && kda::chunk_fits(f32, dk, bv, C)) return bv;
+    }
+    for (int bv : {64, 32, 16})
+        if (bv <= dv && kda::chunk_fits(f32, dk, bv, C) && nheads * (dv / bv) >= 256) return bv;
+    for (int bv : {16, 32, 64})
+        if (bv <= dv && kda::chunk_fits(f32, dk, bv, C)) return bv;
+    return 0;
+}
+
+hipError_t dispatch_chunk(bool f32, const kda::ChunkArgs &a)
+{
+    switch (a.dk) {
+    case 16: return f32 ? kda::launch_chunk_f32_16(a) : kda::launch_chunk_bf16_16(a);
+    case 32: return f32 ? kda::launch_chunk_f32_32(a) : kda::launch_chunk_bf16_32(a);
+    case 64: return f32 ? kda::launch_chunk_f32_64(a) : kda::launch_chunk_bf16_64(a);
+    case 128: return f32 ? kda::launch_chunk_f32_128(a) : kda::launch_chunk_bf16_128(a);
+    default: return hipErrorInvalidConfiguration;
+    }
+}
+
+// Shared body of the four chunk entry points.  For the dense layout nseq = B
+// and each sequence has T tokens; for the packed layout nseq = N, the stream
+// holds T_total tokens and cu_seqlens (device memory) delimits the sequences.
+kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, const void *v,
+                          const float *log_alpha, const float *beta, const float *S0, void *out,
+                          float *S_final, const int32_t *cu_seqlens, int nseq, int T, int T_total,
+                          int H, int dk, int dv, int C, void *stream)
+{
+    if (nseq < 0 || T < 0 || T_total < 0)
+        return fail(KDA_ERR_BAD_SHAPE, "negative size (sequences %d, T %d, T_total %d)", nseq, T, T_total);
+    if (H < 1) return fail(KDA_ERR_BAD_SHAPE, "H must be >= 1 (got %d)", H);
+    if (!supported_d(dk) || !supported_d(dv))
+        return fail(KDA_ERR_UNSUPPORTED, "dk and dv must be 16, 32, 64 or 128 (got %d, %d)", dk, dv);
+    if (!supported_c(C)) return fail(KDA_ERR_UNSUPPORTED, "C must be 16, 32 or 64 (got %d)", C);
+
+    const uint64_t ntok = varlen ? (uint64_t)T_total : (uint64_t)nseq * (uint64_t)T;
+    const uint64_t nheads = (uint64_t)nseq * (uint64_t)H;
+    if (ntok * (uint64_t)H * 128u > (uint64_t)1 << 60 || nheads * 8u > (uint64_t)INT32_MAX)
+        return fail(KDA_ERR_BAD_SHAPE, "problem too large");
+    const uint64_t es = f32 ? 4 : 2;
+    const uint64_t nk = ntok * H * dk, nv = ntok * H * dv, nb = ntok * H, ns = nheads * dv * dk;
+
+    if (ntok > 0 && (!q || !k || !v || !log_alpha || !beta || !out))
+        return fail(KDA_ERR_NULL_POINTER, "q, k, v, log_alpha, beta and out are required when there are tokens");
+    if (varlen && nseq > 0 && !cu_seqlens) return fail(KDA_ERR_NULL_POINTER, "cu_seqlens is required");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(log_alpha, 16))
+        return fail(KDA_ERR_MISALIGNED, "q, k, v, out and log_alpha must be 16-byte aligned");
+    if (!aligned(S0, 16) || !aligned(S_final, 16))
+        return fail(KDA_ERR_MISALIGNED, "S0 and S_final must be 16-byte aligned");
+    if (!aligned(beta, 4) || !aligned(cu_seqlens, 4))
+        return fail(KDA_ERR_MISALIGNED, "beta and cu_seqlens must be 4-byte aligned");
+
+    const Buf ins[] = {{q, nk * es, "q"}, {k, nk * es, "k"}, {v, nv * es, "v"},
+                       {log_alpha, nk * 4, "log_alpha"}, {beta, nb * 4, "beta"},
+                       {cu_seqlens, varlen ? (uint64_t)(nseq + 1) * 4 : 0, "cu_seqlens"}};
+    kda_status_t st = check_aliasing(Buf{out, nv * es, "out"}, ins, 6,
+                                     Buf{S_final, S_final ? ns * 4 : 0, "S_final"},
+                                     Buf{S0, S0 ? ns * 4 : 0, "S0"});
+    if (st != KDA_OK) return st;
+
+    const int BV = choose_bv(f32, dk, dv, C, (long)nheads);
+    if (BV == 0)
+        return fail(KDA_ERR_UNSUPPORTED, "no %s kernel fits LDS for dk=%d, dv=%d, C=%d",
+                    f32 ? "fp32" : "bf16", dk, dv, C);
+    if (nheads == 0 || (ntok == 0 && !S_final)) return ok();
+
+    kda::ChunkArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_alpha = log_alpha;
+    a.beta = beta;
+    a.S0 = S0;
+    a.out = out;
+    a.S_final = S_final;
+    a.cu_seqlens = varlen ? cu_seqlens : nullptr;
+    a.nseq = nseq;
+    a.T = varlen ? 0 : T;
+    a.H = H;
+    a.dk = dk;
+    a.dv = dv;
+    a.C = C;
+    a.BV = BV;
+    a.stream = (hipStream_t)stream;
+    const hipError_t e = dispatch_chunk(f32, a);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "chunk kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+kda_status_t step_common(bool f32, const void *q, const void *k, const void *v, const float *log_alpha,
+                         const float *beta, float *S, void *out, int N, int H, int dk, int dv, void *stream)
+{
+    if (N < 0) return fail(KDA_ERR_BAD_SHAPE, "N must be >= 0 (got %d)", N);
+    if (H < 1) return fail(KDA_ERR_BAD_SHAPE, "H must be >= 1 (got %d)", H);
+    if (!supported_d(dk) || !supported_d(dv))
+        return fail(KDA_ERR_UNSUPPORTED, "dk and dv must be 16, 32, 64 or 128 (got %d, %d)", dk, dv);
+    const uint64_t nheads = (uint64_t)N * (uint64_t)H;
+    if (nheads > (uint64_t)INT32_MAX) return fail(KDA_ERR_BAD_SHAPE, "problem too large");
+    if (nheads == 0) return ok();
+    if (!q || !k || !v || !log_alpha || !beta || !S || !out)
+        return fail(KDA_ERR_NULL_POINTER, "q, k, v, log_alpha, beta, S and out are required");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(log_alpha, 16) || !aligned(S, 16))
+        return fail(KDA_ERR_MISALIGNED, "q, k, v, out, log_alpha and S must be 16-byte aligned");
+    if (!aligned(beta, 4)) return fail(KDA_ERR_MISALIGNED, "beta must be 4-byte aligned");
+    const uint64_t es = f32 ? 4 : 2;
+    const Buf ins[] = {{q, nheads * dk * es, "q"}, {k, nheads * dk * es, "k"}, {v, nheads * dv * es, "v"},
+                       {log_alpha, nheads * dk * 4, "log_alpha"}, {beta, nheads * 4, "beta"}};
+    const Buf sb{S, nheads * dv * dk * 4, "S"};
+    kda_status_t st = check_aliasing(Buf{out, nheads * dv * es, "out"}, ins, 5, sb, sb);
+    if (st != KDA_OK) return st;
+
+    kda::DecodeArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_alpha = log_alpha;
+    a.beta = beta;
+    a.S = S;
+    a.out = out;
+    a.N = N;
+    a.H = H;
+    a.dk = dk;
+    a.dv = dv;
+    a.stream = (hipStream_t)stream;
+    const hipError_t e = kda::launch_decode(a, f32);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                           const float *beta, const float *S0, void *out, float *S_final, int B, int T,
+                           int H, int dk, int dv, int C, void *stream)
+{
+    return chunk_common(false, false, q, k, v, log_alpha, beta, S0, out, S_final, nullptr, B, T, 0, H, dk,
+                        dv, C, stream);
+}
+
+kda_status_t kda_chunk_fwd_f32(const float *q, const float *k, const float *v, const float *log_alpha,
+                               const float *beta, const float *S0, float *out, float *S_final, int B,
+                               int T, int H, int dk, int dv, int C, void *stream)
+{
+    return chunk_common(true, false, q, k, v, log_alpha, beta, S0, out, S_final, nullptr, B, T, 0, H, dk,
+                        dv, C, stream);
+}
+
+kda_status_t kda_chunk_fwd_varlen(const void *q, const void *k, const void *v, const float *log_alpha,
+                                  const float *beta, const float *S0, void *out, float *S_final,
+                                  const int32_t *cu_seqlens, int N, int T_total, int H, int dk, int dv,
+                                  int C, void *stream)
+{
+    return chunk_common(false, true, q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N, 0, T_total,
+                        H, dk, dv, C, stream);
+}
+
+kda_status_t kda_chunk_fwd_varlen_f32(const float *q, const float *k, const float *v,
+                                      const float *log_alpha, const float *beta, const float *S0,
+                                      float *out, float *S_final, const int32_t *cu_seqlens, int N,
+                                      int T_total, int H, int dk, int dv, int C, void *stream)
+{
+    return chunk_common(true, true, q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N, 0, T_total,
+                        H, dk, dv, C, stream);
+}
+
+kda_status_t kda_recurrent_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                                const float *beta, float *S, void *out, int N, int H, int dk, int dv,
+                                void *stream)
+{
+    return step_common(false, q, k, v, log_alpha, beta, S, out, N, H, dk, dv, stream);
+}
+
+kda_status_t kda_recurrent_step_f32(const float *q, const float *k, const float *v, const float *log_alpha,
+                                    const float *beta, float *S, float *out, int N, int H, int dk, int dv,
+                                    void *stream)
+{
+    return step_common(true, q, k, v, log_alpha, beta, S, out, N, H, dk, dv, stream);
+}
+
+kda_status_t kda_check_cu_seqlens_host(const int32_t *cu, int N, int T_total)
+{
+    if (N < 0 || T_total < 0) return fail(KDA_ERR_BAD_SHAPE, "negative N or T_total");
+    if (!cu) return fail(KDA_ERR_NULL_POINTER, "cu_seqlens is NULL");
+    if (cu[0] != 0) return fail(KDA_ERR_BAD_SHAPE, "cu_seqlens[0] = %d, expected 0", cu[0]);
+    for (int n = 0; n < N; ++n)
+        if (cu[n + 1] < cu[n])
+            return fail(KDA_ERR_BAD_SHAPE, "cu_seqlens decreases at %d (%d -> %d)", n, cu[n], cu[n + 1]);
+    if (cu[N] != T_total)
+        return fail(KDA_ERR_BAD_SHAPE, "cu_seqlens[N] = %d, expected T_total = %d", cu[N], T_total);
+    return ok();
+}
+
+const char *kda_status_string(kda_status_t s)
+{
+    switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_NULL_POINTER: return "KDA_ERR_NULL_POINTER";
+    case KDA_ERR_BAD_SHAPE: return "KDA_ERR_BAD_SHAPE";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    case KDA_ERR_ALIASING: return "KDA_ERR_ALIASING";
+    default: return "KDA_ERR_UNKNOWN";
+    }
+}
+
+const char *kda_last_error(void) { return g_err; }
+
+int kda_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// KDA decode step for gfx950: one token per (sequence, head), state in place.
+//
+// Per state row i (a value channel; the row's DK entries are key channels):
+//   s~   = s (.) alpha                 decay, alpha = exp(log_alpha)
+//   p    = <s~, k>                     prediction of v_i
+//   e    = beta (v_i - p)              error
+//   s'   = s~ + e k                    write
+//   o_i  = <s', q>                     readout
+// ("KDA derivation summary" page, sect. 3 and 5; the fused recurrent mode of
+// sect. 6; a step only reads and writes the fixed-size state, "Linear/sparse
+// attention tutorial" page, sect. 8.1.)
+//
+// The state dominates the traffic (64 KiB per head at d = 128 against < 1 KiB
+// of token data), so the kernel is a streaming kernel: each row is read once
+// and written once with 16-byte accesses, every lane keeps all of its rows in
+// flight before computing, and the two row reductions use DPP within groups
+// of DK/16 lanes.
+#pragma once
+
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+template <typename In, int DK>
+__global__ void __launch_bounds__(256)
+decode_step_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
+                   const float *__restrict__ log_alpha, const float *__restrict__ beta,
+                   float *__restrict__ S, In *__restrict__ out, int dv)
+{
+    typedef In In4 __attribute__((ext_vector_type(4)));
+    constexpr int LPR = DK / 16;          // lanes per state row, 16 floats (4 x float4) each
+    constexpr int RPP = 256 / LPR;        // rows per pass of the workgroup
+    constexpr int MAXP = (128 + RPP - 1) / RPP;
+    const long head = blockIdx.x;
+    const int tid = threadIdx.x, sub = tid % LPR, rloc = tid / LPR;
+
+    // this lane's channels: float4 index f_u = sub + LPR u, channels 4 f_u .. 4 f_u + 3
+    f32x4 a[4], kk[4], qq[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const long c = head * DK + 4 * (sub + LPR * u);
+        const f32x4 la = *(const f32x4 *)(log_alpha + c);
+        const In4 kv = *(const In4 *)(k + c);
+        const In4 qv = *(const In4 *)(q + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            a[u][j] = __expf(la[j]);
+            kk[u][j] = tof(kv[j]);
+            qq[u][j] = tof(qv[j]);
+        }
+    }
+    const float b = beta[head];
+
+    f32x4 s[MAXP][4];
+    float vi[MAXP];
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+        const int row = p * RPP + rloc;
+        if (row < dv) {
+            const float *src = S + (head * dv + row) * DK + 4 * sub;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s[p][u] = *(const f32x4 *)(src + 4 * LPR * u);
+            vi[p] = tof(v[head * dv + row]);
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+        const int row = p * RPP + rloc;
+        if (row < dv) {
+            float pred = 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    s[p][u][j] *= a[u][j];
+                    pred += s[p][u][j] * kk[u][j];
+                }
+            pred = group_sum<LPR>(pred);
+            const float e = b * (vi[p] - pred);
+            float o = 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    s[p][u][j] += e * kk[u][j];
+                    o += s[p][u][j] * qq[u][j];
+                }
+            o = group_sum<LPR>(o);
+            float *dst = S + (head * dv + row) * DK + 4 * sub;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) *(f32x4 *)(dst + 4 * LPR * u) = s[p][u];
+            if (sub == 0) out[head * dv + row] = fromf<In>(o);
+        }
+    }
+}
+
+template <typename In, int DK>
+hipError_t launch_decode_t(const DecodeArgs &a)
+{
+    const int grid = a.N * a.H;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_step_kernel<In, DK>), dim3(grid), dim3(256), 0, a.stream,
+                       (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S,
+                       (In *)a.out, a.dv);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -1,0 +1,115 @@
+// Device-side helpers shared by the libkda kernels (gfx950 / CDNA4 only):
+// bf16 <-> fp32 conversion, 16x16 MFMA tile products, DPP lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float tof(bf16 x) { return (float)x; }
+__device__ __forceinline__ float tof(float x) { return x; }
+
+template <typename T> __device__ __forceinline__ T fromf(float x);
+template <> __device__ __forceinline__ float fromf<float>(float x) { return x; }
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+template <> __device__ __forceinline__ bf16 fromf<bf16>(float x) { return (bf16)x; }
+
+// ---------------------------------------------------------------------------
+// 16x16 MFMA tiles.  For every variant used here the output tile is held in
+// the same "accumulator layout": lane l owns D[4*(l>>4) + i][l & 15], i=0..3.
+// Operands: lane l supplies A[l & 15][k0 + KPL*(l>>4) + 0..KPL-1] and
+// B[k0 + KPL*(l>>4) + 0..KPL-1][l & 15].
+// ---------------------------------------------------------------------------
+template <typename OpT, int KS> struct Mma;
+
+template <> struct Mma<bf16, 32> {   // v_mfma_f32_16x16x32_bf16
+    static constexpr int KPL = 8;
+    typedef bf16x8 frag;
+    static __device__ __forceinline__ f32x4 run(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct Mma<bf16, 16> {   // v_mfma_f32_16x16x16_bf16
+    static constexpr int KPL = 4;
+    typedef bf16x4 frag;
+    static __device__ __forceinline__ f32x4 run(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                         __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+    }
+};
+
+template <> struct Mma<float, 4> {   // v_mfma_f32_16x16x4_f32
+    static constexpr int KPL = 1;
+    typedef float frag;
+    static __device__ __forceinline__ f32x4 run(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// Contraction step used for a contraction of length KL.
+template <typename OpT, int KL> struct KStep {
+    static constexpr int value = sizeof(OpT) == 4 ? 4 : (KL % 32 == 0 ? 32 : 16);
+};
+
+// acc[m][n] += sum_{k < KL} A[m][k] * Bt[n][k] over one 16x16 tile, with A and
+// Bt both row-major in LDS (k contiguous).  `a` / `bt` point at the tile's
+// first row; pa / pb are row pitches in elements.  Contraction steps starting
+// at k0 >= kmax are skipped (used for triangular operands).
+template <typename OpT, int KL>
+__device__ __forceinline__ f32x4 mma_tile(f32x4 acc, const OpT *a, int pa, const OpT *bt, int pb,
+                                          int lane, int kmax = KL) {
+    constexpr int KS = KStep<OpT, KL>::value;
+    typedef Mma<OpT, KS> M;
+    const int r = lane & 15, ko = (lane >> 4) * M::KPL;
+    const OpT *pa_ = a + r * pa + ko;
+    const OpT *pb_ = bt + r * pb + ko;
+#pragma unroll
+    for (int k0 = 0; k0 < KL; k0 += KS) {
+        if (k0 < kmax)
+            acc = M::run(*(const typename M::frag *)(pa_ + k0), *(const typename M::frag *)(pb_ + k0), acc);
+    }
+    return acc;
+}
+
+// fp32 16x16xKL product with general strides (used for the small triangular
+// inverse, where one operand is read column-wise): acc[m][n] += sum_k
+// A[m*ars + k*acs] * B[k*brs + n*bcs].
+template <int KL>
+__device__ __forceinline__ f32x4 mma_f32_strided(f32x4 acc, const float *A, int ars, int acs,
+                                                 const float *B, int brs, int bcs, int lane) {
+    const int r = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int k0 = 0; k0 < KL; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * ars + (k0 + kq) * acs],
+                                                   B[(k0 + kq) * brs + r * bcs], acc, 0, 0, 0);
+    return acc;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------------------
+// Sum over aligned groups of G lanes (G in {1, 2, 4, 8}) with DPP; every lane
+// of the group receives the group's sum.
+// ---------------------------------------------------------------------------
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (G >= 2)   // quad_perm [1,0,3,2]: lane ^ 1
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+    if constexpr (G >= 4)   // quad_perm [2,3,0,1]: lane ^ 2
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
+    if constexpr (G >= 8)   // row_half_mirror: lane i <-> 7 - i inside each group of 8
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, true));
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+    return x;
+}
+
+}  // namespace kda

@@ -1,0 +1,47 @@
+// Internal launcher interface between the C ABI (kda_api.cpp, host only) and
+// the kernel translation units.  Not part of the public API.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+namespace kda {
+
+struct ChunkArgs {
+    const void *q, *k, *v;
+    const float *log_alpha, *beta, *S0;
+    void *out;
+    float *S_final;
+    const int *cu_seqlens;   // device; NULL for the dense [B, T, H, d] layout
+    int nseq, T, H, dk, dv, C, BV;
+    hipStream_t stream;
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *log_alpha, *beta;
+    float *S;
+    void *out;
+    int N, H, dk, dv;
+    hipStream_t stream;
+};
+
+// Chunk prefill launchers, one per (input type, dk); BV in {16, 32, 64},
+// C in {16, 32, 64}.  Defined in kda_chunk_inst.hip.
+hipError_t launch_chunk_bf16_16(const ChunkArgs &);
+hipError_t launch_chunk_bf16_32(const ChunkArgs &);
+hipError_t launch_chunk_bf16_64(const ChunkArgs &);
+hipError_t launch_chunk_bf16_128(const ChunkArgs &);
+hipError_t launch_chunk_f32_16(const ChunkArgs &);
+hipError_t launch_chunk_f32_32(const ChunkArgs &);
+hipError_t launch_chunk_f32_64(const ChunkArgs &);
+hipError_t launch_chunk_f32_128(const ChunkArgs &);
+
+// Whether the (input type, dk, BV, C) kernel fits the 160 KiB of LDS of a
+// gfx950 workgroup (and is therefore instantiated).  Defined next to the
+// launchers; pure host code, no HIP call.
+bool chunk_fits(bool f32, int dk, int BV, int C);
+
+// Decode step launcher.  Defined in kda_decode.hip.
+hipError_t launch_decode(const DecodeArgs &, bool f32);
+
+}  // namespace kda

@@ -1,0 +1,166 @@
+"""C ABI of libkda on the CPU: the library loads, exports every function the
+public header declares, and rejects invalid calls with the documented status
+codes before any HIP call (no GPU needed).  No test here launches a kernel.
+
+The pointers below are fake device addresses: validation only looks at their
+values (NULL, alignment, overlap), never dereferences them.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libkda.h")
+
+kda = pytest.importorskip("kimi_delta_attention_fwd_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return kda.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("kda_chunk_fwd", "kda_chunk_fwd_f32", "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_f32",
+              "kda_recurrent_step", "kda_recurrent_step_f32", "kda_status_string", "kda_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in libkda.h but not exported"
+
+
+def test_status_strings_and_version(lib):
+    for code, name in kda.STATUS.items():
+        assert kda.kda_status_string(code) == name
+    assert kda.kda_status_string(99) == "KDA_ERR_UNKNOWN"
+    assert kda.kda_version() >= 100
+
+
+A = 0x7F0000000000  # fake, 256-byte aligned "device" base address
+MB = 1 << 20
+
+
+def chunk(lib, f32=False, q=A, k=A + 64 * MB, v=A + 128 * MB, la=A + 192 * MB, beta=A + 256 * MB, S0=None,
+          out=A + 320 * MB, Sf=A + 384 * MB, B=2, T=100, H=4, dk=64, dv=64, C=64):
+    fn = lib.kda_chunk_fwd_f32 if f32 else lib.kda_chunk_fwd
+    return fn(q, k, v, la, beta, S0, out, Sf, B, T, H, dk, dv, C, None)
+
+
+def varlen(lib, cu=A + 448 * MB, N=3, T_total=100, **kw):
+    args = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, la=A + 192 * MB, beta=A + 256 * MB, S0=None,
+                out=A + 320 * MB, Sf=A + 384 * MB, H=4, dk=64, dv=64, C=64)
+    args.update(kw)
+    return lib.kda_chunk_fwd_varlen(args["q"], args["k"], args["v"], args["la"], args["beta"], args["S0"],
+                                    args["out"], args["Sf"], cu, N, T_total, args["H"], args["dk"],
+                                    args["dv"], args["C"], None)
+
+
+def step(lib, q=A, k=A + MB, v=A + 2 * MB, la=A + 3 * MB, beta=A + 4 * MB, S=A + 8 * MB, out=A + 64 * MB,
+         N=4, H=2, dk=128, dv=128):
+    return lib.kda_recurrent_step(q, k, v, la, beta, S, out, N, H, dk, dv, None)
+
+
+def test_chunk_rejects_bad_shapes(lib):
+    assert chunk(lib, B=-1) == 2
+    assert chunk(lib, T=-5) == 2
+    assert chunk(lib, H=0) == 2
+    assert "H must be" in kda.kda_last_error()
+
+
+@pytest.mark.parametrize("dk,dv,C", [(8, 64, 64), (64, 96, 64), (256, 64, 64), (64, 64, 48), (64, 64, 128),
+                                     (64, 64, 8)])
+def test_chunk_rejects_unsupported_sizes(lib, dk, dv, C):
+    assert chunk(lib, dk=dk, dv=dv, C=C) == 3
+
+
+def test_chunk_fp32_mode_rejects_configs_that_do_not_fit_lds(lib):
+    # fp32 operands at dk = 128, C = 64 need more than the 160 KiB of LDS
+    assert chunk(lib, f32=True, dk=128, dv=128, C=64) == 3
+    assert "LDS" in kda.kda_last_error()
+
+
+def test_chunk_rejects_null_pointers(lib):
+    assert chunk(lib, q=None) == 1
+    assert chunk(lib, beta=None) == 1
+    assert chunk(lib, out=None) == 1
+
+
+def test_chunk_rejects_misaligned_pointers(lib):
+    assert chunk(lib, q=A + 2) == 4
+    assert chunk(lib, la=A + 192 * MB + 4) == 4
+    assert chunk(lib, S0=A + 500 * MB + 8) == 4
+    assert chunk(lib, beta=A + 256 * MB + 2) == 4
+
+
+def test_chunk_rejects_aliasing(lib):
+    assert chunk(lib, out=A + 16) == 6                      # out inside q
+    assert chunk(lib, Sf=A + 64 * MB) == 6                  # S_final on k
+    S0 = A + 500 * MB
+    assert chunk(lib, S0=S0, Sf=S0 + 256) == 6              # partial overlap of S0 / S_final
+    assert "identical" in kda.kda_last_error()
+
+
+def test_chunk_zero_work_calls_succeed_without_a_gpu(lib):
+    # no sequences: nothing to launch
+    assert chunk(lib, B=0) == 0
+    # no tokens and no final state requested: nothing to launch
+    assert chunk(lib, T=0, Sf=None, q=None, k=None, v=None, la=None, beta=None, out=None) == 0
+    assert kda.kda_last_error() == ""
+
+
+def test_varlen_validation(lib):
+    assert varlen(lib, cu=None) == 1
+    assert varlen(lib, cu=A + 448 * MB + 2) == 4
+    assert varlen(lib, N=-1) == 2
+    assert varlen(lib, N=0, T_total=0, q=None, k=None, v=None, la=None, beta=None, out=None) == 0
+
+
+def test_check_cu_seqlens_host(lib):
+    good = np.array([0, 5, 5, 12], dtype=np.int32)
+    assert kda.kda_check_cu_seqlens_host(good.ctypes.data, 3, 12) == 0
+    assert kda.kda_check_cu_seqlens_host(good.ctypes.data, 3, 13) == 2
+    bad = np.array([0, 5, 4, 12], dtype=np.int32)
+    assert kda.kda_check_cu_seqlens_host(bad.ctypes.data, 3, 12) == 2
+    assert "decreases" in kda.kda_last_error()
+    start = np.array([1, 5], dtype=np.int32)
+    assert kda.kda_check_cu_seqlens_host(start.ctypes.data, 1, 5) == 2
+    assert kda.kda_check_cu_seqlens_host(None, 1, 5) == 1
+
+
+def test_step_validation(lib):
+    assert step(lib, N=-1) == 2
+    assert step(lib, H=0) == 2
+    assert step(lib, dk=48) == 3
+    assert step(lib, S=None) == 1
+    assert step(lib, S=A + 8 * MB + 4) == 4
+    assert step(lib, out=A + 8 * MB) == 6                   # out inside S
+    assert step(lib, N=0) == 0
+
+
+def test_binding_raises_kda_error(lib):
+    with pytest.raises(kda.KdaError) as ei:
+        kda.kda_chunk_fwd(A, A + 64 * MB, A + 128 * MB, A + 192 * MB, A + 256 * MB, None, A + 320 * MB, None,
+                          1, 10, 1, 64, 64, 24, stream=0)
+    assert ei.value.status == 3
+
+
+def test_chunk_allows_in_place_state_continuation(lib):
+    # S_final == S0 is allowed; validation passes and only the launch is left.  B = 0 keeps
+    # the call launch-free on a machine without a GPU.
+    S0 = A + 500 * MB
+    assert chunk(lib, S0=S0, Sf=S0, B=0) == 0

@@ -1,0 +1,352 @@
+"""GPU parity: libkda (through its C ABI) against the float64 oracle.
+
+Every test feeds the HIP path and the oracle the very same seeded inputs (the
+oracle gets an exact float64 copy of the bf16 / fp32 tensors the GPU reads)
+and compares element by element with the normwise relative error
+    max_i |gpu_i - ref_i| / max_i |ref_i|
+computed separately for the outputs and the final states.  Bars: 2e-2 for bf16
+inputs (fp32 accumulation), 1e-4 for fp32 inputs.
+
+Reduced shapes span several chunks and 16-row tiles with a ragged tail; the
+full-size workloads (the same launch configurations bench.py times) are checked
+on sampled heads, which the oracle recomputes from their whole token history.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import kda_synth
+import oracle
+
+kda = pytest.importorskip("kimi_delta_attention_fwd_amd")
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+f64 = kda_synth.to_f64
+
+
+def note(msg):
+    print(msg, flush=True)
+
+
+def rel(gpu, ref):
+    return float(np.max(np.abs(gpu - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    if not os.path.exists(kda.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    kda.load()
+    return torch.device("cuda:0")
+
+
+def gpu_chunk(p, C, final=True):
+    out, sf = kda.chunk_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S0=p.S0, C=C, output_final_state=final)
+    torch.cuda.synchronize()
+    return out, sf
+
+
+def oracle_dense(p):
+    return oracle.forward(f64(p.q), f64(p.k), f64(p.v), f64(p.log_alpha), f64(p.beta), S0=f64(p.S0))
+
+
+def sampled(p, pairs):
+    """(b, h) pairs of a dense batch, packed as an oracle batch of single heads."""
+    def pick(t):
+        if t is None:
+            return None
+        return torch.stack([t[b, :, h] for b, h in pairs]).unsqueeze(2)
+    S0 = None if p.S0 is None else torch.stack([p.S0[b, h] for b, h in pairs]).unsqueeze(1)
+    return oracle.forward(f64(pick(p.q)), f64(pick(p.k)), f64(pick(p.v)), f64(pick(p.log_alpha)),
+                          f64(torch.stack([p.beta[b, :, h] for b, h in pairs]).unsqueeze(2)), S0=f64(S0))
+
+
+def assert_close(name, out, sf, o_ref, s_ref, tol):
+    e_o = rel(out, o_ref)
+    e_s = rel(sf, s_ref) if s_ref is not None else 0.0
+    note(f"  {name}: out rel err {e_o:.3e}, S_final rel err {e_s:.3e} (bar {tol:g})")
+    assert np.all(np.isfinite(out)) and (sf is None or np.all(np.isfinite(sf)))
+    assert e_o < tol, f"{name}: output error {e_o}"
+    assert e_s < tol, f"{name}: state error {e_s}"
+
+
+# ---------------------------------------------------------------- small full-oracle cases
+def test_tiny_fp32_workload(dev):
+    w = kda_synth.WORKLOADS["tiny"]
+    note("case tiny: B1 H1 T64 d16 fp32 C16")
+    p = kda_synth.workload("tiny", device=dev)
+    out, sf = gpu_chunk(p, w["C"])
+    o_ref, s_ref = oracle_dense(p)
+    assert_close("tiny", f64(out), f64(sf), o_ref, s_ref, TOL["f32"])
+
+
+def test_small_bf16_workload(dev):
+    w = kda_synth.WORKLOADS["small"]
+    note("case small: B2 H4 T1024 d64 bf16 C64, S0 ~ N(0, 0.1)")
+    p = kda_synth.workload("small", device=dev)
+    out, sf = gpu_chunk(p, w["C"])
+    o_ref, s_ref = oracle_dense(p)
+    assert_close("small", f64(out), f64(sf), o_ref, s_ref, TOL["bf16"])
+
+
+SHAPES = [
+    # B, T, H, dk, dv, C, dtype
+    (2, 200, 3, 128, 128, 64, "bf16"),   # ragged tail, 6 heads (no XCD remap)
+    (1, 333, 8, 128, 128, 64, "bf16"),   # 8 heads (XCD remap on), 5 full chunks + 13 tokens
+    (2, 100, 2, 64, 32, 32, "bf16"),
+    (1, 77, 2, 32, 64, 16, "bf16"),
+    (2, 50, 2, 16, 16, 16, "bf16"),
+    (1, 130, 2, 64, 128, 64, "bf16"),   # dk != dv
+    (1, 70, 1, 128, 16, 32, "bf16"),
+    (1, 100, 2, 64, 64, 64, "f32"),
+    (2, 90, 2, 128, 128, 32, "f32"),
+    (1, 70, 3, 32, 16, 16, "f32"),
+    (1, 129, 2, 16, 64, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("with_s0", [False, True])
+@pytest.mark.parametrize("B,T,H,dk,dv,C,dtype", SHAPES)
+def test_chunk_shapes(dev, B, T, H, dk, dv, C, dtype, with_s0):
+    note(f"case chunk B{B} T{T} H{H} dk{dk} dv{dv} C{C} {dtype} S0={with_s0}")
+    p = kda_synth.prefill(B, T, H, dk, dv, dtype=dtype, s0_sigma=0.1 if with_s0 else None,
+                          seed=1000 + T + dk + dv + C, device=dev)
+    out, sf = gpu_chunk(p, C)
+    o_ref, s_ref = oracle_dense(p)
+    assert_close("chunk", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+
+
+def test_chunk_matches_across_chunk_sizes(dev):
+    """The chunk length is a schedule choice only: C = 16, 32, 64 agree."""
+    note("case chunk-size invariance B1 T300 H2 d64 bf16")
+    p = kda_synth.prefill(1, 300, 2, 64, 64, dtype="bf16", s0_sigma=0.1, seed=77, device=dev)
+    o_ref, s_ref = oracle_dense(p)
+    for C in (16, 32, 64):
+        out, sf = gpu_chunk(p, C)
+        assert_close(f"C={C}", f64(out), f64(sf), o_ref, s_ref, TOL["bf16"])
+
+
+def test_chunk_edge_cases(dev):
+    note("case edge: T=0 copies S0, T=1, in-place S_final == S0, no S_final")
+    p = kda_synth.prefill(2, 0, 3, 64, 64, dtype="bf16", s0_sigma=0.1, seed=5, device=dev)
+    out, sf = gpu_chunk(p, 64)
+    assert out.shape[1] == 0 and torch.equal(sf, p.S0)
+    p = kda_synth.prefill(2, 0, 3, 64, 64, dtype="bf16", s0_sigma=None, seed=5, device=dev)
+    _, sf = gpu_chunk(p, 64)
+    assert torch.count_nonzero(sf) == 0
+    p = kda_synth.prefill(2, 1, 3, 64, 64, dtype="bf16", s0_sigma=0.1, seed=6, device=dev)
+    out, sf = gpu_chunk(p, 64)
+    o_ref, s_ref = oracle_dense(p)
+    assert_close("T=1", f64(out), f64(sf), o_ref, s_ref, TOL["bf16"])
+    # in place: S_final is the S0 buffer
+    p = kda_synth.prefill(1, 150, 2, 128, 128, dtype="bf16", s0_sigma=0.1, seed=8, device=dev)
+    o_ref, s_ref = oracle_dense(p)
+    S = p.S0.clone()
+    out = torch.empty_like(p.v)
+    kda.kda_chunk_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S, out, S, 1, 150, 2, 128, 128, 64)
+    torch.cuda.synchronize()
+    assert_close("in-place", f64(out), f64(S), o_ref, s_ref, TOL["bf16"])
+    out2, none = gpu_chunk(p, 64, final=False)
+    assert none is None and torch.equal(out2, out)
+
+
+def test_chunk_decay_at_precondition_edge(dev):
+    """log_alpha = -4.9 in every channel: 78 nats of decay per 16-token block,
+    just inside the kernel's documented range."""
+    note("case strong decay: log_alpha = -4.9, B1 T200 H2 d128 bf16")
+    p = kda_synth.prefill(1, 200, 2, 128, 128, dtype="bf16", s0_sigma=0.1, seed=9, device=dev)
+    p.log_alpha.fill_(-4.9)
+    out, sf = gpu_chunk(p, 64)
+    o_ref, s_ref = oracle_dense(p)
+    assert_close("log_alpha=-4.9", f64(out), f64(sf), o_ref, s_ref, TOL["bf16"])
+    note("case mixed decay: half the channels at -4.5, the rest ~ -softplus(N(-4,1.5))")
+    p = kda_synth.prefill(1, 200, 2, 128, 128, dtype="bf16", s0_sigma=0.1, seed=10, device=dev)
+    p.log_alpha[..., ::2] = -4.5
+    out, sf = gpu_chunk(p, 64)
+    o_ref, s_ref = oracle_dense(p)
+    assert_close("mixed decay", f64(out), f64(sf), o_ref, s_ref, TOL["bf16"])
+
+
+def test_chunk_guard_bands_untouched(dev):
+    """Outputs written through interior pointers of larger buffers: the bands
+    around out and S_final keep their sentinel values (no out-of-bounds stores)."""
+    note("case guard bands B2 T150 H3 d64 bf16")
+    B, T, H, dk, dv = 2, 150, 3, 64, 64
+    p = kda_synth.prefill(B, T, H, dk, dv, dtype="bf16", s0_sigma=0.1, seed=12, device=dev)
+    pad = 4096
+    n_out, n_s = B * T * H * dv, B * H * dv * dk
+    big_out = torch.full((n_out + 2 * pad,), 7.0, dtype=torch.bfloat16, device=dev)
+    big_s = torch.full((n_s + 2 * pad,), -3.0, dtype=torch.float32, device=dev)
+    out = big_out[pad:pad + n_out].view(B, T, H, dv)
+    sf = big_s[pad:pad + n_s].view(B, H, dv, dk)
+    kda.kda_chunk_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out, sf, B, T, H, dk, dv, 64)
+    torch.cuda.synchronize()
+    assert torch.all(big_out[:pad] == 7.0) and torch.all(big_out[pad + n_out:] == 7.0)
+    assert torch.all(big_s[:pad] == -3.0) and torch.all(big_s[pad + n_s:] == -3.0)
+    o_ref, s_ref = oracle_dense(p)
+    assert_close("guarded", f64(out), f64(sf), o_ref, s_ref, TOL["bf16"])
+
+
+def test_chunk_is_deterministic(dev):
+    note("case determinism B2 T500 H8 d128 bf16 (two runs, bitwise)")
+    p = kda_synth.prefill(2, 500, 8, 128, 128, dtype="bf16", s0_sigma=0.1, seed=13, device=dev)
+    o1, s1 = gpu_chunk(p, 64)
+    o2, s2 = gpu_chunk(p, 64)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+# ---------------------------------------------------------------- packed variable length
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_varlen_small(dev, dtype):
+    lengths = [5, 0, 64, 130, 1, 77]
+    note(f"case varlen lengths {lengths} H3 d64 {dtype} C32")
+    p = kda_synth.prefill_varlen(lengths, 3, 64, 64, dtype=dtype, s0_sigma=0.1, seed=21, device=dev)
+    out, sf = kda.chunk_fwd_varlen(p.q, p.k, p.v, p.log_alpha, p.beta, p.cu_seqlens, S0=p.S0, C=32)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.forward_varlen(f64(p.q), f64(p.k), f64(p.v), f64(p.log_alpha), f64(p.beta),
+                                         np.array(p.cu_host), S0=f64(p.S0))
+    assert_close("varlen", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+
+
+def test_varlen_equals_dense_per_sequence(dev):
+    """A packed stream gives each sequence exactly what a dense call on that
+    sequence alone gives (same kernel, same chunk grid)."""
+    lengths = [100, 64, 37]
+    note(f"case varlen vs dense lengths {lengths} H2 d128 bf16")
+    p = kda_synth.prefill_varlen(lengths, 2, 128, 128, dtype="bf16", s0_sigma=0.1, seed=22, device=dev)
+    out, sf = kda.chunk_fwd_varlen(p.q, p.k, p.v, p.log_alpha, p.beta, p.cu_seqlens, S0=p.S0, C=64)
+    for n, L in enumerate(lengths):
+        a, b = p.cu_host[n], p.cu_host[n + 1]
+        o_n, s_n = kda.chunk_fwd(p.q[:, a:b].contiguous(), p.k[:, a:b].contiguous(), p.v[:, a:b].contiguous(),
+                                 p.log_alpha[:, a:b].contiguous(), p.beta[:, a:b].contiguous(),
+                                 S0=p.S0[n:n + 1].contiguous(), C=64)
+        torch.cuda.synchronize()
+        assert torch.equal(out[:, a:b], o_n) and torch.equal(sf[n:n + 1], s_n)
+
+
+def test_varlen_workload_sampled(dev):
+    w = kda_synth.WORKLOADS["varlen"]
+    note("case varlen workload: 8 sequences U[2048,16384] x H16 d128 bf16 C64 (sampled heads)")
+    p = kda_synth.workload("varlen", device=dev)
+    out, sf = kda.chunk_fwd_varlen(p.q, p.k, p.v, p.log_alpha, p.beta, p.cu_seqlens, S0=p.S0, C=w["C"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(sf).all()
+    errs_o, errs_s = [], []
+    for n in range(len(p.cu_host) - 1):
+        a, b = p.cu_host[n], p.cu_host[n + 1]
+        h = (5 * n + 3) % w["H"]
+        sl = lambda t: t[:, a:b, h:h + 1]
+        o_ref, s_ref = oracle.forward(f64(sl(p.q)), f64(sl(p.k)), f64(sl(p.v)), f64(sl(p.log_alpha)),
+                                      f64(p.beta[:, a:b, h:h + 1]), S0=f64(p.S0[n:n + 1, h:h + 1]))
+        errs_o.append(rel(f64(out[:, a:b, h:h + 1]), o_ref))
+        errs_s.append(rel(f64(sf[n:n + 1, h:h + 1]), s_ref))
+    note(f"  varlen sampled: worst out rel err {max(errs_o):.3e}, worst S rel err {max(errs_s):.3e}")
+    assert max(errs_o) < TOL["bf16"] and max(errs_s) < TOL["bf16"]
+
+
+# ---------------------------------------------------------------- full-size prefill workloads
+def test_mid_workload_sampled(dev):
+    w = kda_synth.WORKLOADS["mid"]
+    note("case mid workload: B4 H32 T8192 d128 bf16 C64 (8 sampled heads)")
+    p = kda_synth.workload("mid", device=dev)
+    out, sf = gpu_chunk(p, w["C"])
+    assert torch.isfinite(out.float()).all() and torch.isfinite(sf).all()
+    pairs = [(0, 0), (0, 31), (1, 7), (1, 16), (2, 3), (2, 25), (3, 12), (3, 30)]
+    o_ref, s_ref = sampled(p, pairs)
+    o_gpu = np.stack([f64(out[b, :, h]) for b, h in pairs])[:, :, None]
+    s_gpu = np.stack([f64(sf[b, h]) for b, h in pairs])[:, None]
+    assert_close("mid sampled", o_gpu, s_gpu, o_ref, s_ref, TOL["bf16"])
+
+
+def test_long_workload_sampled(dev):
+    w = kda_synth.WORKLOADS["long"]
+    note("case long workload: B1 H16 T65536 d128 bf16 C64, S0 in (3 sampled heads)")
+    p = kda_synth.workload("long", device=dev)
+    out, sf = gpu_chunk(p, w["C"])
+    assert torch.isfinite(out.float()).all() and torch.isfinite(sf).all()
+    pairs = [(0, 0), (0, 9), (0, 15)]
+    o_ref, s_ref = sampled(p, pairs)
+    o_gpu = np.stack([f64(out[b, :, h]) for b, h in pairs])[:, :, None]
+    s_gpu = np.stack([f64(sf[b, h]) for b, h in pairs])[:, None]
+    assert_close("long sampled", o_gpu, s_gpu, o_ref, s_ref, TOL["bf16"])
+
+
+# ---------------------------------------------------------------- decode step
+@pytest.mark.parametrize("N,H,dk,dv,dtype", [(3, 2, 64, 32, "bf16"), (2, 3, 128, 128, "bf16"),
+                                             (4, 1, 16, 128, "f32"), (2, 2, 32, 64, "f32"),
+                                             (5, 2, 128, 16, "f32")])
+def test_decode_steps(dev, N, H, dk, dv, dtype):
+    steps = 40
+    note(f"case decode N{N} H{H} dk{dk} dv{dv} {dtype} x{steps} steps")
+    d = kda_synth.decode(N, H, dk, dv, steps, dtype=dtype, seed=31 + dk + dv, device=dev, step_block=8)
+    S = d.S0.clone()
+    outs = []
+    for t in range(steps):
+        outs.append(kda.recurrent_step(d.q[t], d.k[t], d.v[t], d.log_alpha[t], d.beta[t], S))
+    torch.cuda.synchronize()
+    out = torch.stack(outs, dim=1)   # [N, steps, H, dv]
+    o_ref, s_ref = oracle.forward(f64(d.q.transpose(0, 1)), f64(d.k.transpose(0, 1)), f64(d.v.transpose(0, 1)),
+                                  f64(d.log_alpha.transpose(0, 1)), f64(d.beta.transpose(0, 1)), S0=f64(d.S0))
+    assert_close("decode", f64(out), f64(S), o_ref, s_ref, TOL[dtype])
+
+
+def test_decode_workload_sampled(dev):
+    w = kda_synth.WORKLOADS["decode"]
+    note("case decode workload: 256 seq x H32 d128 bf16, 1024 steps (16 sampled heads, every step)")
+    d = kda_synth.decode(w["N"], w["H"], w["dk"], w["dv"], w["steps"], device=dev)
+    S = d.S0.clone()
+    heads = [(n, h) for n, h in zip(range(3, 256, 16), range(0, 32, 2))]
+    out_s = torch.empty((len(heads), w["steps"], w["dv"]), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((w["N"], w["H"], w["dv"]), dtype=torch.bfloat16, device=dev)
+    ni = torch.tensor([n for n, _ in heads], device=dev)
+    hi = torch.tensor([h for _, h in heads], device=dev)
+    for t in range(w["steps"]):
+        kda.recurrent_step(d.q[t], d.k[t], d.v[t], d.log_alpha[t], d.beta[t], S, out=out)
+        out_s[:, t] = out[ni, hi]
+    torch.cuda.synchronize()
+    assert torch.isfinite(S).all()
+    pick = lambda t: t[:, ni, hi].transpose(0, 1).unsqueeze(2)      # [n, steps, 1, d]
+    o_ref, s_ref = oracle.forward(f64(pick(d.q)), f64(pick(d.k)), f64(pick(d.v)), f64(pick(d.log_alpha)),
+                                  f64(d.beta[:, ni, hi].transpose(0, 1).unsqueeze(2)),
+                                  S0=f64(d.S0[ni, hi].unsqueeze(1)))
+    assert_close("decode sampled", f64(out_s)[:, :, None], f64(S[ni, hi]).reshape(len(heads), 1, w["dv"], w["dk"]),
+                 o_ref, s_ref, TOL["bf16"])
+
+
+def test_decode_equals_chunk_prefill_on_same_stream(dev):
+    """Both schedules of the one recurrence on the same token stream: decode
+    steps and one chunk prefill agree with each other and with the oracle."""
+    N, H, dk, dv, steps = 16, 4, 128, 128, 200
+    note(f"case decode vs chunk prefill: N{N} H{H} d128 bf16, {steps} tokens")
+    d = kda_synth.decode(N, H, dk, dv, steps, seed=41, device=dev, step_block=50)
+    S = d.S0.clone()
+    outs = [kda.recurrent_step(d.q[t], d.k[t], d.v[t], d.log_alpha[t], d.beta[t], S) for t in range(steps)]
+    dec = torch.stack(outs, dim=1)
+    tm = lambda t: t.transpose(0, 1).contiguous()
+    pre, sf = kda.chunk_fwd(tm(d.q), tm(d.k), tm(d.v), tm(d.log_alpha), tm(d.beta), S0=d.S0, C=64)
+    torch.cuda.synchronize()
+    e_o = rel(f64(dec), f64(pre))
+    e_s = rel(f64(S), f64(sf))
+    note(f"  decode vs prefill: out rel diff {e_o:.3e}, state rel diff {e_s:.3e}")
+    assert e_o < TOL["bf16"] and e_s < TOL["bf16"]
+    o_ref, s_ref = oracle.forward(f64(tm(d.q)), f64(tm(d.k)), f64(tm(d.v)), f64(tm(d.log_alpha)),
+                                  f64(tm(d.beta)), S0=f64(d.S0))
+    assert_close("decode", f64(dec), f64(S), o_ref, s_ref, TOL["bf16"])
+    assert_close("prefill", f64(pre), f64(sf), o_ref, s_ref, TOL["bf16"])
+
+
+def test_decode_is_deterministic(dev):
+    note("case decode determinism N8 H4 d128")
+    d = kda_synth.decode(8, 4, 128, 128, 3, seed=51, device=dev, step_block=3)
+    S1, S2 = d.S0.clone(), d.S0.clone()
+    o1 = [kda.recurrent_step(d.q[t], d.k[t], d.v[t], d.log_alpha[t], d.beta[t], S1) for t in range(3)]
+    o2 = [kda.recurrent_step(d.q[t], d.k[t], d.v[t], d.log_alpha[t], d.beta[t], S2) for t in range(3)]
+    torch.cuda.synchronize()
+    assert torch.equal(S1, S2) and all(torch.equal(a, b) for a, b in zip(o1, o2))
