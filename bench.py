@@ -1,0 +1,318 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA forward hot path on one MI355X; prints one JSON line.
+
+A step is one chunk prefill of the mid workload (B=4, H=32, T=8192,
+dk=dv=128, bf16 q/k/v, fp32 gates and state, C=64) through the C ABI
+(kda_chunk_fwd), with every input already resident in HBM.  `value` is
+prefill tokens/s (a token = one position of one sequence, all 32 heads).
+
+Extra fields measure the other entry points on their own workloads:
+  decode        256 sequences x 32 heads, 1024 one-token steps (steps/s)
+  long_context  B=1, H=16, T=65536 with an initial state (tokens/s)
+  varlen        8 packed sequences of U[2048, 16384] tokens x 16 heads (tokens/s)
+
+roofline: the chunk kernel against HBM bandwidth.  `achieved` is the
+algorithmic bytes of one launch (one read of every input, one write of
+every output and final state) divided by the kernel's average duration,
+measured with HIP events recorded around each launch on the stream the
+kernel runs on.  `traffic` is the HBM bytes per launch from rocprofv3
+FETCH_SIZE / WRITE_SIZE counters (scaled by the same counters on a plain
+copy kernel), taken from profiles/traffic.json when that file was made from
+the current kernel sources, else null.
+
+cpu_baseline: the float64 CPU oracle on a bounded sample of the same
+workload (whole heads, a prefix of their tokens), OpenMP over heads.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s & decode steps/s on 1 MI355X; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+KERNEL_SOURCES = ["kimi_delta_attention_fwd_amd/csrc/kda_chunk.h",
+                  "kimi_delta_attention_fwd_amd/csrc/kda_device.h",
+                  "kimi_delta_attention_fwd_amd/csrc/kda_decode.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_bytes(ntok_heads, dk, dv, nheads, in_bytes=2, s0=False, sfinal=True):
+    """Algorithmic HBM bytes of one prefill launch: q, k (dk each) and v (dv) in
+    the input type, log_alpha (dk) and beta in fp32, out (dv) in the input type,
+    plus the fp32 states read / written."""
+    per_tok = in_bytes * (2 * dk + dv) + 4 * dk + 4 + in_bytes * dv
+    state = 4 * dk * dv * nheads
+    return ntok_heads * per_tok + (state if s0 else 0) + (state if sfinal else 0)
+
+
+def prefill_flops(ntok_heads, dk, dv, C):
+    """Useful flops per token-head: the three state contractions (6 dk dv) and
+    the four triangular C x C products (2 C (dk + dv))."""
+    return ntok_heads * (6 * dk * dv + 2 * C * (dk + dv))
+
+
+def decode_bytes(nheads, dk, dv, in_bytes=2):
+    """One decode step: the fp32 state read and written once, plus q, k, v,
+    log_alpha, beta and out."""
+    return nheads * (8 * dk * dv + in_bytes * (2 * dk + dv) + 4 * dk + 4 + in_bytes * dv)
+
+
+def load_traffic(kernel: str, workload: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    entry = data.get("kernels", {}).get(kernel, {}).get(workload)
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def time_launches(launch, stream, steps, warmup, torch):
+    """Run `warmup` untimed launches, then exactly `steps` timed ones.
+    Returns (wall seconds over the steps, mean kernel ms from HIP events)."""
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
+    return wall, kms
+
+
+def bench_prefill(args, torch, kda, kda_synth, stream):
+    w = kda_synth.WORKLOADS["mid"]
+    p = kda_synth.workload("mid", device="cuda")
+    B, T, H, dk, dv, C = w["B"], w["T"], w["H"], w["dk"], w["dv"], w["C"]
+    out = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device="cuda")
+    sf = torch.empty((B, H, dv, dk), dtype=torch.float32, device="cuda")
+    h = stream.cuda_stream
+
+    def launch():
+        kda.kda_chunk_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, None, out, sf, B, T, H, dk, dv, C, h)
+
+    wall, kms = time_launches(launch, stream, args.steps, args.warmup, torch)
+    nth = B * T * H
+    nbytes = prefill_bytes(nth, dk, dv, B * H, s0=False, sfinal=True)
+    flops = prefill_flops(nth, dk, dv, C)
+    res = dict(wall=wall, kernel_ms=kms, tokens=B * T, bytes=nbytes, flops=flops, inputs=p,
+               config=dict(workload="mid prefill: B=4 H=32 T=8192 dk=dv=128 bf16 C=64, zero S0, S_final written",
+                           global_batch=B, seq_len=T, heads=H, dk=dk, dv=dv, chunk=C))
+    return res
+
+
+def bench_decode(args, torch, kda, kda_synth, stream):
+    w = kda_synth.WORKLOADS["decode"]
+    N, H, dk, dv, steps = w["N"], w["H"], w["dk"], w["dv"], w["steps"]
+    if args.decode_steps:
+        steps = min(steps, args.decode_steps)
+    d = kda_synth.decode(N, H, dk, dv, steps, device="cuda")
+    S = d.S0.clone()
+    out = torch.empty((N, H, dv), dtype=torch.bfloat16, device="cuda")
+    h = stream.cuda_stream
+    Sw = d.S0.clone()
+    for t in range(min(8, steps)):   # warm-up on a scratch copy of the state
+        kda.kda_recurrent_step(d.q[t], d.k[t], d.v[t], d.log_alpha[t], d.beta[t], Sw, out, N, H, dk, dv, h)
+    del Sw
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for t in range(steps):
+        starts[t].record(stream)
+        kda.kda_recurrent_step(d.q[t], d.k[t], d.v[t], d.log_alpha[t], d.beta[t], S, out, N, H, dk, dv, h)
+        ends[t].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    kms = sum(times) / steps
+    nbytes = decode_bytes(N * H, dk, dv)
+    del d, S
+    return dict(
+        workload="decode: 256 sequences x H=32, dk=dv=128, bf16 q/k/v, fp32 state, 1024 steps",
+        steps_per_s=steps / wall, tokens_per_s=N * steps / wall, ms_per_step=wall * 1e3 / steps,
+        kernel_ms_mean=kms, kernel_ms_median=times[steps // 2],
+        roofline=dict(bound="hbm", achieved=round(nbytes / (kms * 1e-3) / 1e9, 1), peak=HBM_PEAK_GBS,
+                      unit="GB/s", frac=round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      traffic=load_traffic("decode_step", "decode"), algorithmic_bytes=nbytes))
+
+
+def bench_long(args, torch, kda, kda_synth, stream, steps=3):
+    w = kda_synth.WORKLOADS["long"]
+    p = kda_synth.workload("long", device="cuda")
+    B, T, H, dk, dv, C = w["B"], w["T"], w["H"], w["dk"], w["dv"], w["C"]
+    out = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device="cuda")
+    sf = torch.empty((B, H, dv, dk), dtype=torch.float32, device="cuda")
+    h = stream.cuda_stream
+
+    def launch():
+        kda.kda_chunk_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out, sf, B, T, H, dk, dv, C, h)
+
+    wall, kms = time_launches(launch, stream, steps, 1, torch)
+    nbytes = prefill_bytes(B * T * H, dk, dv, B * H, s0=True, sfinal=True)
+    del p, out, sf
+    return dict(workload="long prefill: B=1 H=16 T=65536 dk=dv=128 bf16 C=64, S0 in, S_final out",
+                tokens_per_s=B * T * steps / wall, kernel_ms=kms,
+                hbm_gbs=round(nbytes / (kms * 1e-3) / 1e9, 1),
+                hbm_frac=round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+
+
+def bench_varlen(args, torch, kda, kda_synth, stream, steps=3):
+    w = kda_synth.WORKLOADS["varlen"]
+    p = kda_synth.workload("varlen", device="cuda")
+    Tt = p.cu_host[-1]
+    N = len(p.cu_host) - 1
+    H, dk, dv, C = w["H"], w["dk"], w["dv"], w["C"]
+    out = torch.empty((1, Tt, H, dv), dtype=torch.bfloat16, device="cuda")
+    sf = torch.empty((N, H, dv, dk), dtype=torch.float32, device="cuda")
+    h = stream.cuda_stream
+
+    def launch():
+        kda.kda_chunk_fwd_varlen(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out, sf, p.cu_seqlens, N, Tt, H, dk,
+                                 dv, C, h)
+
+    wall, kms = time_launches(launch, stream, steps, 1, torch)
+    nbytes = prefill_bytes(Tt * H, dk, dv, N * H, s0=True, sfinal=True)
+    del p, out, sf
+    return dict(workload=f"varlen prefill: {N} packed sequences (T_total={Tt}) x H=16 dk=dv=128 bf16 C=64",
+                tokens_per_s=Tt * steps / wall, kernel_ms=kms,
+                hbm_gbs=round(nbytes / (kms * 1e-3) / 1e9, 1),
+                hbm_frac=round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+
+
+def cpu_baseline(p, H_total, kda_synth, target_s=12.0):
+    """Float64 oracle on whole heads of the mid workload, a prefix of their
+    tokens, sized to about `target_s` seconds of CPU work."""
+    import numpy as np
+    import torch
+
+    import oracle
+    threads = oracle.max_threads()
+    B, T, H, dk = p.q.shape
+    nh = min(B * H, max(1, threads))
+    pairs = [(i % B, (i * 7) % H) for i in range(nh)]
+
+    def run(tok):
+        pick = lambda t: torch.stack([t[b, :tok, h] for b, h in pairs]).unsqueeze(2)
+        args = [kda_synth.to_f64(pick(x)) for x in (p.q, p.k, p.v, p.log_alpha)]
+        beta = kda_synth.to_f64(torch.stack([p.beta[b, :tok, h] for b, h in pairs]).unsqueeze(2))
+        t0 = time.perf_counter()
+        oracle.forward(*args, beta)
+        return time.perf_counter() - t0
+
+    tok = 256
+    dt = run(tok)
+    tok = int(min(T, max(256, tok * target_s / max(dt, 1e-3))))
+    dt = run(tok)
+    token_heads_per_s = nh * tok / dt
+    return dict(value=round(token_heads_per_s / H_total, 2), unit="tokens/s", cores=min(threads, nh),
+                kind="oracle",
+                sample=f"{nh} whole heads of the mid workload, first {tok} tokens each "
+                       f"({nh * tok} token-heads in {dt:.1f} s, float64 recurrence, OpenMP over heads); "
+                       f"value = token-heads/s divided by H={H_total}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="only the mid prefill (profiling runs)")
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="fewer decode steps (profiling runs; the default is the workload's 1024)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device copy three times, so hardware counters can be "
+                         "scaled by a kernel of known traffic")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(this build runs on a single MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kda_synth
+    import kimi_delta_attention_fwd_amd as kda
+    if not os.path.exists(kda.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    kda.load()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    pre = bench_prefill(args, torch, kda, kda_synth, stream)
+    ach = pre["bytes"] / (pre["kernel_ms"] * 1e-3) / 1e9
+    tfl = pre["flops"] / (pre["kernel_ms"] * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(pre["tokens"] * args.steps / pre["wall"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["wall"] * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": pre["config"],
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic("chunk_fwd", "mid"),
+                     "kernel": "chunk_fwd_kernel<bf16,128,64,64>",
+                     "kernel_ms": round(pre["kernel_ms"], 4), "algorithmic_bytes": pre["bytes"],
+                     "mfma_tflops": round(tfl, 2), "mfma_frac": round(tfl / BF16_PEAK_TFLOPS, 4),
+                     "kernel_source_hash": kernel_source_hash()},
+    }
+    p_mid = pre.pop("inputs")
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(p_mid, kda_synth.WORKLOADS["mid"]["H"], kda_synth)
+    del p_mid
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        result["decode"] = bench_decode(args, torch, kda, kda_synth, stream)
+        torch.cuda.empty_cache()
+        result["long_context"] = bench_long(args, torch, kda, kda_synth, stream)
+        torch.cuda.empty_cache()
+        result["varlen"] = bench_varlen(args, torch, kda, kda_synth, stream)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

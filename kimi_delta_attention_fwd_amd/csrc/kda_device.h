@@ -68,15 +68,72 @@ template <typename OpT, int KL>
 __device__ __forceinline__ f32x4 mma_tile(f32x4 acc, const OpT *a, int pa, const OpT *bt, int pb,
                                           int lane, int kmax = KL) {
     constexpr int KS = KStep<OpT, KL>::value;
+    constexpr int NS = KL / KS;
     typedef Mma<OpT, KS> M;
+    typedef typename M::frag frag;
     const int r = lane & 15, ko = (lane >> 4) * M::KPL;
     const OpT *pa_ = a + r * pa + ko;
     const OpT *pb_ = bt + r * pb + ko;
+    // all operand fragments first, so the LDS latencies overlap, then the chain
+    frag fa[NS], fb[NS];
 #pragma unroll
-    for (int k0 = 0; k0 < KL; k0 += KS) {
-        if (k0 < kmax)
-            acc = M::run(*(const typename M::frag *)(pa_ + k0), *(const typename M::frag *)(pb_ + k0), acc);
+    for (int s = 0; s < NS; ++s) {
+        if (s * KS < kmax) {
+            fa[s] = *(const frag *)(pa_ + s * KS);
+            fb[s] = *(const frag *)(pb_ + s * KS);
+        }
     }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        if (s * KS < kmax) acc = M::run(fa[s], fb[s], acc);
+    return acc;
+}
+
+// The MFMA operand fragments of one 16-row panel (16 x KL), loaded once from
+// LDS and reused for several tiles.  Lane l holds row (l & 15) and, for each
+// contraction step s, KPL consecutive k starting at s*KS + KPL*(l >> 4).
+template <typename OpT, int KL>
+struct Panel {
+    static constexpr int KS = KStep<OpT, KL>::value;
+    static constexpr int NS = KL / KS;
+    typedef Mma<OpT, KS> M;
+    typename M::frag f[NS];
+
+    // rows of a row-major array; steps starting at k >= kmax are not loaded
+    __device__ __forceinline__ void load(const OpT *rows, int pitch, int lane, int kmax = KL) {
+        const OpT *p = rows + (lane & 15) * pitch + (lane >> 4) * M::KPL;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            if (s * KS < kmax) f[s] = *(const typename M::frag *)(p + s * KS);
+    }
+    // rows row0.. of an array stored with swz_index() below
+    __device__ __forceinline__ void load_swz(const OpT *base, int row0, int pitch, int mask, int lane) {
+        const int row = row0 + (lane & 15);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int col = s * KS + (lane >> 4) * M::KPL;
+            f[s] = *(const typename M::frag *)(base + swz_index(row, col, pitch, mask));
+        }
+    }
+    // element (row, col) of a 16-byte-chunk XOR-swizzled array: chunk col/V is
+    // stored at chunk (col/V) ^ ((row >> 2) & mask), V = 16 bytes of OpT.  The
+    // swizzle spreads the transposed writes of four consecutive rows over
+    // different banks.
+    static __device__ __forceinline__ int swz_index(int row, int col, int pitch, int mask) {
+        constexpr int V = 16 / (int)sizeof(OpT);
+        return row * pitch + (((col / V) ^ ((row >> 2) & mask)) * V) + (col % V);
+    }
+};
+
+// acc += A B^T over one 16x16 tile from two preloaded panels (A rows, B rows);
+// contraction steps starting at k >= kmax are skipped.
+template <typename OpT, int KL>
+__device__ __forceinline__ f32x4 mma(f32x4 acc, const Panel<OpT, KL> &a, const Panel<OpT, KL> &b,
+                                     int kmax = KL) {
+    typedef Panel<OpT, KL> P;
+#pragma unroll
+    for (int s = 0; s < P::NS; ++s)
+        if (s * P::KS < kmax) acc = P::M::run(a.f[s], b.f[s], acc);
     return acc;
 }
 

@@ -174,6 +174,19 @@ def test_chunk_decay_at_precondition_edge(dev):
     assert_close("mixed decay", f64(out), f64(sf), o_ref, s_ref, TOL["bf16"])
 
 
+def test_chunk_mixes_fast_and_sub_block_paths(dev):
+    """Strong decay only in some chunks: those take the sub-block path, the
+    others the fast path, inside one sequence (and in fp32 mode)."""
+    for dtype, tol in (("bf16", TOL["bf16"]), ("f32", TOL["f32"])):
+        note(f"case mixed paths: B2 T300 H2 d64 {dtype}, tokens 70..100 and 250..260 at log_alpha = -3.5")
+        p = kda_synth.prefill(2, 300, 2, 64, 64, dtype=dtype, s0_sigma=0.1, seed=14, device=dev)
+        p.log_alpha[:, 70:100] = -3.5
+        p.log_alpha[1, 250:260, 1, :32] = -3.5
+        out, sf = gpu_chunk(p, 64 if dtype == "bf16" else 32)
+        o_ref, s_ref = oracle_dense(p)
+        assert_close(f"mixed paths {dtype}", f64(out), f64(sf), o_ref, s_ref, tol)
+
+
 def test_chunk_guard_bands_untouched(dev):
     """Outputs written through interior pointers of larger buffers: the bands
     around out and S_final keep their sentinel values (no out-of-bounds stores)."""
