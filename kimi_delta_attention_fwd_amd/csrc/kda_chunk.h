@@ -66,6 +66,8 @@ struct ChunkCfg {
     static constexpr int SWZ = C * (int)sizeof(OpT) / 16 - 1;   // chunk XOR mask of the swizzled Ktil^T
     static constexpr int VE = 16 / (int)sizeof(In);  // elements per 16-byte vector of v / out
     static constexpr int PV = BV + VE;               // pitch of the staged V tile
+    // pitch of the staged output tile (padded when it still fits the R^T slot)
+    static constexpr int PO = (C * (BV + VE) <= BV * (C + PADE)) ? BV + VE : BV;
     static constexpr int NPAIR = NB * (NB + 1) / 2;  // (I, J <= I) column-operand tiles
     // element-wise phase: each thread owns RS rows x 4 channels
     static constexpr int NCG = DK / 4;
@@ -91,6 +93,8 @@ struct ChunkCfg {
     static constexpr size_t SZ_G = SZ_GA > SZ_GB ? SZ_GA : SZ_GB;
     static constexpr size_t SZ_S = al(size_t(BV) * PK * sizeof(OpT));
     static constexpr size_t SZ_CC = al(size_t(C) * PC * sizeof(OpT));
+    static constexpr int PX = 20;                    // pitch of a wave's 16x16 fp32 substitution scratch
+    static constexpr size_t SZ_X = al(size_t(NW) * 16 * PX * sizeof(float));
     static constexpr size_t SZ_V = al(size_t(C) * PV * sizeof(In));
     static constexpr size_t SZ_SEG = al(size_t(NSEG) * DK * sizeof(float));
     static constexpr size_t SZ_BETA = al(size_t(C) * sizeof(float));
@@ -98,21 +102,23 @@ struct ChunkCfg {
     static constexpr size_t SZ_FLAG = 16;
     static constexpr size_t SZ_A = al(size_t(C) * PA * sizeof(float));
     static constexpr size_t SZ_VT = al(size_t(BV) * PC * sizeof(OpT));
-    static constexpr size_t SZ_U = SZ_A > 2 * SZ_VT ? SZ_A : 2 * SZ_VT;
+    // segment sums live in the E^T slot when they fit (they are dead by the time E^T is written)
+    static constexpr bool SEG_IN_ET = SZ_SEG <= SZ_VT;
 
     static constexpr size_t O_KR = 0, O_QR = SZ_KR, O_KCOL = 2 * SZ_KR;
     static constexpr size_t O_KBAR = 0, O_QBAR = SZ_KR, O_KHAT = 2 * SZ_KR, O_KTT = 3 * SZ_KR;
     static constexpr size_t O_S = SZ_G;
-    static constexpr size_t O_T = O_S + SZ_S;
-    static constexpr size_t O_P = O_T + SZ_CC;
+    static constexpr size_t O_X = O_S + SZ_S;
+    static constexpr size_t O_P = O_X + SZ_X;
     static constexpr size_t O_V = O_P + SZ_CC;
-    static constexpr size_t O_SEG = O_V + SZ_V;
-    static constexpr size_t O_BETA = O_SEG + SZ_SEG;
+    static constexpr size_t O_SEGX = O_V + SZ_V;                         // segment sums, when not in E^T
+    static constexpr size_t O_BETA = O_SEGX + (SEG_IN_ET ? 0 : SZ_SEG);
     static constexpr size_t O_GL = O_BETA + SZ_BETA;
     static constexpr size_t O_FLAG = O_GL + SZ_GL;
-    static constexpr size_t O_U = O_FLAG + SZ_FLAG;
-    static constexpr size_t O_A = O_U, O_RT = O_U, O_ET = O_U + SZ_VT, O_O = O_U;
-    static constexpr size_t LDS = O_U + SZ_U;
+    static constexpr size_t O_A = O_FLAG + SZ_FLAG;
+    static constexpr size_t O_RT = O_A + SZ_A, O_ET = O_RT + SZ_VT, O_O = O_RT;
+    static constexpr size_t O_SEG = SEG_IN_ET ? O_ET : O_SEGX;
+    static constexpr size_t LDS = O_ET + SZ_VT;
     static constexpr bool fits = LDS <= 160 * 1024;
 
     static_assert(C % 16 == 0 && C <= 64, "chunk length");
@@ -185,7 +191,11 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     typedef typename K::OpT OpT;
     typedef In In4 __attribute__((ext_vector_type(4)));
     constexpr int NB = K::NB, NBV = K::NBV, RS = K::RS, PK = K::PK, PC = K::PC, PA = K::PA;
-    constexpr int PV = K::PV, VE = K::VE;
+    constexpr int PV = K::PV, VE = K::VE, PO = K::PO;
+    // one bf16 MFMA shape for the whole kernel (16x16x32 unless a contraction is only 16 long)
+    constexpr int KSB = sizeof(OpT) == 4 ? 4 : ((DK % 32 == 0 && C % 32 == 0) ? 32 : 16);
+    typedef Panel<OpT, DK, KSB> PanelK;
+    typedef Panel<OpT, C, KSB> PanelC;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[K::LDS];
     OpT *sKr = (OpT *)(smem + K::O_KR);
@@ -196,7 +206,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     OpT *sKhat = (OpT *)(smem + K::O_KHAT);
     OpT *sKtT = (OpT *)(smem + K::O_KTT);
     OpT *sS = (OpT *)(smem + K::O_S);
-    OpT *sT = (OpT *)(smem + K::O_T);
+    float *sX = (float *)(smem + K::O_X);
     OpT *sP = (OpT *)(smem + K::O_P);
     In *sV = (In *)(smem + K::O_V);
     float *sSeg = (float *)(smem + K::O_SEG);
@@ -238,13 +248,10 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     const bool ew = tid < K::NACT;
     const int c0 = 4 * cg, r0 = seg * RS, blk = r0 / 16;
 
-    // The upper (J > I) 16x16 tiles of T and P are zero and never rewritten.
+    // The upper (J > I) 16x16 tiles of P are zero and never rewritten.
     for (int idx = tid; idx < C * C; idx += K::NT) {
         const int r = idx / C, j = idx % C;
-        if (j / 16 > r / 16) {
-            sT[r * PC + j] = fromf<OpT>(0.f);
-            sP[r * PC + j] = fromf<OpT>(0.f);
-        }
+        if (j / 16 > r / 16) sP[r * PC + j] = fromf<OpT>(0.f);
     }
     if (tid < 2) sFlag[tid] = 0;
 
@@ -312,7 +319,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             const int idx = tid + u * K::NT;
             if (idx < K::NVCH) {
                 const int r = idx / (BV / VE), cc = idx % (BV / VE);
-                if (r < nv) *(f32x4 *)(ob + tv + r * HDV + cc * VE) = *(const f32x4 *)(sO + r * BV + cc * VE);
+                if (r < nv) *(f32x4 *)(ob + tv + r * HDV + cc * VE) = *(const f32x4 *)(sO + r * PO + cc * VE);
             }
         }
     };
@@ -486,12 +493,12 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             for (int J = 0; J < NB; ++J) {
                 const int owner = (HW >= NB) ? J : (NB == 4) ? ((J < 2 ? J : 3 - J) % HW) : (J % HW);
                 if (owner != hw) continue;
-                Panel<OpT, DK> cp;
+                PanelK cp;
                 if (fast) cp.load(sKhat + 16 * J * PK, PK, lane);
 #pragma unroll
                 for (int I = J; I < NB; ++I) {
                     if (!fast) cp.load(sKcol + pair_index(I, J) * 16 * PK, PK, lane);
-                    Panel<OpT, DK> rp;
+                    PanelK rp;
                     rp.load(fast ? ((isA ? sKbar : sQbar) + 16 * I * PK) : ((isA ? sKr : sQr) + 16 * I * PK), PK, lane);
                     const f32x4 acc = mma(zero4(), cp, rp);   // acc[i] = X[16I + n][16J + 4g + i]
                     const int r = 16 * I + n, j0 = 16 * J + 4 * g;
@@ -511,23 +518,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         }
         __syncthreads();
 
-        // ---- (4) diagonal blocks of T = (I + A)^{-1}; the sub-block path meanwhile turns
-        //      Kr / Qr / Kd into the inter-chunk operands Kbar, Qbar, Ktil^T
-        if (wave == 0) {
-            const int b = min(lane >> 4, NB - 1), j = lane & 15;
-            float *Ab = sA + 16 * b * PA + 16 * b;
-            float acol[16], x[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acol[i] = Ab[i * PA + j];
-            inv_unit_lower16(acol, x, j);
-            if ((lane >> 4) < NB) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    Ab[i * PA + j] = x[i];
-                    sT[(16 * b + i) * PC + 16 * b + j] = fromf<OpT>(x[i]);
-                }
-            }
-        }
+        // ---- (4) sub-block path only: turn Kr / Qr / Kd into Kbar, Qbar, Ktil^T
         if (!fast) {
             OpT kt[4][RS];
             if (ew) {
@@ -555,9 +546,9 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                     f32x4 vk, vq;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        vk[j] = tof(pk[j]) * before[j];        // k e^{G}
-                        vq[j] = tof(pq[j]) * before[j];        // q e^{G}
-                        kt[j][i] = fromf<OpT>(tof(pd[j]) * after[j]);   // k e^{G_last - G}
+                        vk[j] = tof(pk[j]) * before[j];                   // k e^{G}
+                        vq[j] = tof(pq[j]) * before[j];                   // q e^{G}
+                        kt[j][i] = fromf<OpT>(tof(pd[j]) * after[j]);     // k e^{G_last - G}
                     }
                     store4(pk, vk);   // Kbar over Kr, Qbar over Qr (same slots)
                     store4(pq, vq);
@@ -568,113 +559,98 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 #pragma unroll
                 for (int j = 0; j < 4; ++j) store_row_swz<OpT, RS>(sKtT, c0 + j, r0, PC, K::SWZ, kt[j]);
             }
-        }
-        __syncthreads();
-        if constexpr (NB >= 2) {
-            // 16 -> 32: T_ij = -D_i' A_ij D_j' for (i, j) = (1, 0) and (3, 2)
-            constexpr int NP1 = (NB == 4) ? 2 : 1;
-            const int pi = 2 * wave + 1, pj = 2 * wave;
-            const int row0 = 4 * (lane >> 4), col = lane & 15;
-            if (wave < NP1) {
-                const f32x4 M = mma_f32_strided<16>(zero4(), sA + 16 * pi * PA + 16 * pj, PA, 1,
-                                                    sA + 16 * pj * PA + 16 * pj, PA, 1, lane);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sA[(16 * pj + row0 + i) * PA + 16 * pi + col] = M[i];
-            }
             __syncthreads();
-            if (wave < NP1) {
-                const f32x4 X = mma_f32_strided<16>(zero4(), sA + 16 * pi * PA + 16 * pi, PA, 1,
-                                                    sA + 16 * pj * PA + 16 * pi, PA, 1, lane);
+        }
+
+        // ---- (5) wave 0: inverses D_b' of the diagonal 16x16 blocks of I + A, in place in
+        //      sA (forward substitution in registers, DPP broadcasts); the other waves
+        //      meanwhile form R = beta (V - Kbar S^T), stored transposed.
+        if (wave == 0) {
+            const int b = min(lane >> 4, NB - 1), j = lane & 15;
+            float *Ab = sA + 16 * b * PA + 16 * b;
+            float acol[16], x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acol[i] = Ab[i * PA + j];
+            inv_unit_lower16(acol, x, j);
+            if ((lane >> 4) < NB) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) Ab[i * PA + j] = x[i];
+            }
+        } else {
+            const int n = lane & 15, g = lane >> 4;
+            for (int t = wave - 1; t < K::NOT; t += NW - 1) {
+                const int rb = t / NBV, cb2 = t % NBV;
+                PanelK kp, sp;
+                kp.load(sKbar + 16 * rb * PK, PK, lane);
+                sp.load(sS + 16 * cb2 * PK, PK, lane);
+                const f32x4 ak = mma(zero4(), kp, sp);   // (Kbar S^T)[16rb + 4g + i][16cb2 + n]
+                f32x4 rv;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    sA[(16 * pi + row0 + i) * PA + 16 * pj + col] = -X[i];
-                    sT[(16 * pi + row0 + i) * PC + 16 * pj + col] = fromf<OpT>(-X[i]);
-                    sA[(16 * pj + row0 + i) * PA + 16 * pi + col] = 0.f;
+                    const int r = 16 * rb + 4 * g + i;
+                    rv[i] = sBeta[r] * (tof(sV[r * PV + 16 * cb2 + n]) - ak[i]);
                 }
+                store4(sRT + (16 * cb2 + n) * PC + 16 * rb + 4 * g, rv);
             }
-            __syncthreads();
         }
-        if constexpr (NB == 4) {
-            // 32 -> 64: T_LL = -T1 (A_LL T0), T0 / T1 the 32x32 diagonal inverses
-            const int mt = (wave >> 1) & 1, nt = wave & 1;
-            const int row0 = 4 * (lane >> 4), col = lane & 15;
-            if (wave < 4) {
-                const f32x4 M = mma_f32_strided<32>(zero4(), sA + (32 + 16 * mt) * PA, PA, 1,
-                                                    sA + 16 * nt, PA, 1, lane);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sA[(16 * mt + row0 + i) * PA + 32 + 16 * nt + col] = M[i];
-            }
-            __syncthreads();
-            if (wave < 4) {
-                const f32x4 X = mma_f32_strided<32>(zero4(), sA + (32 + 16 * mt) * PA + 32, PA, 1,
-                                                    sA + 32 + 16 * nt, PA, 1, lane);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sT[(32 + 16 * mt + row0 + i) * PC + 16 * nt + col] = fromf<OpT>(-X[i]);
-            }
-            __syncthreads();
-        }
+        __syncthreads();
 
         // Each wave owns one value column block cb of the C x BV outputs (all its
         // row blocks rb) and the matching state column block, so the operand panels
         // of cb are loaded once per phase.
         const int cb = wave % NBV;
 
-        // ---- (5) R = beta (V - Kbar S^T), stored transposed; O^T = S Qbar^T kept in registers
+        // ---- (6) E = (I + A)^{-1} R by block forward substitution,
+        //      E_b = D_b' (R_b - sum_{J<b} A_bJ E_J).  Value columns are independent, so
+        //      wave w solves column block w on its own (fp32 MFMA, wave-local LDS round
+        //      trips, no workgroup barrier) and writes E^T for the updates below.
+        if (wave < NBV) {
+            float *xs = sX + wave * 16 * K::PX;
+            const int n = lane & 15, g = lane >> 4, kq = lane >> 4;
+            const OpT *et = sET + (16 * cb + n) * PC;          // row v = 16 cb + n of E^T
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                f32x4 y = zero4();                               // sum_{J<b} A_bJ E_J
+#pragma unroll
+                for (int J = 0; J < b; ++J)
+#pragma unroll
+                    for (int k0 = 0; k0 < 16; k0 += 4)
+                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * b + n) * PA + 16 * J + k0 + kq],
+                                                                 tof(et[16 * J + k0 + kq]), y, 0, 0, 0);
+                typedef OpT Op4 __attribute__((ext_vector_type(4)));
+                const Op4 rr = *(const Op4 *)(sRT + (16 * cb + n) * PC + 16 * b + 4 * g);
+                f32x4 xv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xv[i] = tof(rr[i]) - y[i];   // X[16b + 4g + i][n]
+                *(f32x4 *)(xs + n * K::PX + 4 * g) = xv;                  // X^T, row n
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                f32x4 e = zero4();
+#pragma unroll
+                for (int k0 = 0; k0 < 16; k0 += 4)
+                    e = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * b + n) * PA + 16 * b + k0 + kq],
+                                                             xs[n * K::PX + k0 + kq], e, 0, 0, 0);
+                store4(sET + (16 * cb + n) * PC + 16 * b + 4 * g, e);    // E^T[16cb + n][16b + 4g + i]
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            }
+        }
+        __syncthreads();
+
+        // ---- (7) O^T = S Qbar^T + E^T P^T;  S^T <- Diag(e^{G_last}) S^T + Ktil^T E
         {
-            Panel<OpT, DK> sp;
+            PanelC ep;
+            ep.load(sET + 16 * cb * PC, PC, lane);
+            PanelK sp;
             sp.load(sS + 16 * cb * PK, PK, lane);
 #pragma unroll
             for (int s = 0; s < K::OT_PER_W; ++s) {
                 const int ot = wave + NW * s;
                 if (ot < K::NOT) {
-                    const int rb = ot / NBV, n = lane & 15, g = lane >> 4;
-                    Panel<OpT, DK> kp, qp;
-                    kp.load(sKbar + 16 * rb * PK, PK, lane);
-                    qp.load(sQbar + 16 * rb * PK, PK, lane);
-                    const f32x4 ak = mma(zero4(), kp, sp);   // (Kbar S^T)[16rb + 4g + i][16cb + n]
-                    Oacc[s] = mma(zero4(), sp, qp);          // O^T[16cb + 4g + i][16rb + n]
-                    f32x4 rv;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 16 * rb + 4 * g + i;
-                        rv[i] = sBeta[r] * (tof(sV[r * PV + 16 * cb + n]) - ak[i]);
-                    }
-                    store4(sRT + (16 * cb + n) * PC + 16 * rb + 4 * g, rv);
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- (6) E = T R (stored transposed)
-        {
-            Panel<OpT, C> rp;
-            rp.load(sRT + 16 * cb * PC, PC, lane);
-#pragma unroll
-            for (int s = 0; s < K::OT_PER_W; ++s) {
-                const int ot = wave + NW * s;
-                if (ot < K::NOT) {
-                    const int rb = ot / NBV, n = lane & 15;
-                    Panel<OpT, C> tp;
-                    tp.load(sT + 16 * rb * PC, PC, lane, 16 * (rb + 1));
-                    const f32x4 e = mma(zero4(), tp, rp, 16 * (rb + 1));
-                    store4(sET + (16 * cb + n) * PC + 16 * rb + 4 * (lane >> 4), e);
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- (7) O^T += E^T P^T;  S^T <- Diag(e^{G_last}) S^T + Ktil^T E
-        {
-            Panel<OpT, C> ep;
-            ep.load(sET + 16 * cb * PC, PC, lane);
-#pragma unroll
-            for (int s = 0; s < K::OT_PER_W; ++s) {
-                const int ot = wave + NW * s;
-                if (ot < K::NOT) {
                     const int rb = ot / NBV;
-                    Panel<OpT, C> pp;
+                    PanelK qp;
+                    qp.load(sQbar + 16 * rb * PK, PK, lane);
+                    PanelC pp;
                     pp.load(sP + 16 * rb * PC, PC, lane, 16 * (rb + 1));
+                    Oacc[s] = mma(zero4(), sp, qp);               // O^T[16cb + 4g + i][16rb + n]
                     Oacc[s] = mma(Oacc[s], ep, pp, 16 * (rb + 1));
                 }
             }
@@ -683,7 +659,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 const int st = wave + NW * s;
                 if (st < K::NST) {
                     const int ct = st / NBV;
-                    Panel<OpT, C> kp;
+                    PanelC kp;
                     kp.load_swz(sKtT, 16 * ct, PC, K::SWZ, lane);
                     const f32x4 acc = mma(zero4(), kp, ep);
 #pragma unroll
@@ -697,7 +673,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             const int ot = wave + NW * s;
             if (ot < K::NOT) {
                 const int rb = ot / NBV;
-                store4(sO + (16 * rb + (lane & 15)) * BV + 16 * cb + 4 * (lane >> 4), Oacc[s]);
+                store4(sO + (16 * rb + (lane & 15)) * PO + 16 * cb + 4 * (lane >> 4), Oacc[s]);
             }
         }
 #pragma unroll

@@ -60,41 +60,16 @@ template <typename OpT, int KL> struct KStep {
     static constexpr int value = sizeof(OpT) == 4 ? 4 : (KL % 32 == 0 ? 32 : 16);
 };
 
-// acc[m][n] += sum_{k < KL} A[m][k] * Bt[n][k] over one 16x16 tile, with A and
-// Bt both row-major in LDS (k contiguous).  `a` / `bt` point at the tile's
-// first row; pa / pb are row pitches in elements.  Contraction steps starting
-// at k0 >= kmax are skipped (used for triangular operands).
-template <typename OpT, int KL>
-__device__ __forceinline__ f32x4 mma_tile(f32x4 acc, const OpT *a, int pa, const OpT *bt, int pb,
-                                          int lane, int kmax = KL) {
-    constexpr int KS = KStep<OpT, KL>::value;
-    constexpr int NS = KL / KS;
-    typedef Mma<OpT, KS> M;
-    typedef typename M::frag frag;
-    const int r = lane & 15, ko = (lane >> 4) * M::KPL;
-    const OpT *pa_ = a + r * pa + ko;
-    const OpT *pb_ = bt + r * pb + ko;
-    // all operand fragments first, so the LDS latencies overlap, then the chain
-    frag fa[NS], fb[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        if (s * KS < kmax) {
-            fa[s] = *(const frag *)(pa_ + s * KS);
-            fb[s] = *(const frag *)(pb_ + s * KS);
-        }
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-        if (s * KS < kmax) acc = M::run(fa[s], fb[s], acc);
-    return acc;
-}
-
 // The MFMA operand fragments of one 16-row panel (16 x KL), loaded once from
 // LDS and reused for several tiles.  Lane l holds row (l & 15) and, for each
 // contraction step s, KPL consecutive k starting at s*KS + KPL*(l >> 4).
-template <typename OpT, int KL>
+// KS_ selects the MFMA shape; products that accumulate into the same tile
+// must use the same shape (back-to-back dependent MFMAs of different shapes
+// need wait states the compiler does not insert).
+template <typename OpT, int KL, int KS_ = KStep<OpT, KL>::value>
 struct Panel {
-    static constexpr int KS = KStep<OpT, KL>::value;
+    static constexpr int KS = KS_;
+    static_assert(KL % KS == 0, "contraction length is a multiple of the MFMA step");
     static constexpr int NS = KL / KS;
     typedef Mma<OpT, KS> M;
     typename M::frag f[NS];
@@ -127,10 +102,11 @@ struct Panel {
 
 // acc += A B^T over one 16x16 tile from two preloaded panels (A rows, B rows);
 // contraction steps starting at k >= kmax are skipped.
-template <typename OpT, int KL>
-__device__ __forceinline__ f32x4 mma(f32x4 acc, const Panel<OpT, KL> &a, const Panel<OpT, KL> &b,
-                                     int kmax = KL) {
-    typedef Panel<OpT, KL> P;
+template <typename OpT, int KLA, int KLB, int KS>
+__device__ __forceinline__ f32x4 mma(f32x4 acc, const Panel<OpT, KLA, KS> &a, const Panel<OpT, KLB, KS> &b,
+                                     int kmax = KLA) {
+    static_assert(KLA == KLB, "operand panels of one product share the contraction length");
+    typedef Panel<OpT, KLA, KS> P;
 #pragma unroll
     for (int s = 0; s < P::NS; ++s)
         if (s * P::KS < kmax) acc = P::M::run(a.f[s], b.f[s], acc);
