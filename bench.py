@@ -48,10 +48,15 @@ KERNEL_SOURCES = ["kimi_delta_attention_fwd_amd/csrc/kda_chunk.h",
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with // comments and blank lines removed, so
+    that counters taken from a kernel stay valid across comment edits only."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

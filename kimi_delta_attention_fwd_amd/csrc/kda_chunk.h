@@ -8,9 +8,8 @@
 //
 //   A_rj = beta_r sum_c k_rc k_jc e^{G_rc - G_jc}   (j <  r)   KK^T system
 //   P_rj =        sum_c q_rc k_jc e^{G_rc - G_jc}   (j <= r)   causal QK^T
-//   T    = (I + A)^{-1}
 //   R    = Diag(beta) (V - Kbar S^T),  Kbar = K e^{G}         provisional errors
-//   E    = T R                                                corrected errors
+//   E    = (I + A)^{-1} R                                     corrected errors
 //   O    = Qbar S^T + P E,             Qbar = Q e^{G}
 //   S^T <- Diag(e^{G_last}) S^T + Ktil^T E,  Ktil = K e^{G_last - G}
 //
@@ -37,10 +36,11 @@
 //    each 16-token block (the precondition in the public header).
 // Every exponent is a sum of same-sign partial sums (no cancellation).
 //
-// T = (I + A)^{-1} is built in fp32: the four 16x16 diagonal blocks by
-// forward substitution in registers (one lane per column, the A entries
-// broadcast inside each 16-lane row with DPP), then the off-diagonal blocks by
-// block doubling (16 -> 32 -> 64) with fp32 MFMA.
+// (I + A) E = R is solved in fp32 by block forward substitution over the
+// 16-row blocks: the inverses of the 16x16 diagonal blocks come from forward
+// substitution in registers (one lane per column, the A entries broadcast
+// inside each 16-lane row with DPP); the off-diagonal updates and the
+// diagonal-block products run on fp32 MFMA, one wave per 16 value columns.
 //
 // Matrix products run on MFMA 16x16 tiles: bf16 operands with fp32
 // accumulation in the bf16 entry points, fp32 operands in the fp32 ones.
@@ -62,7 +62,7 @@ struct ChunkCfg {
     static constexpr int PADE = 16 / (int)sizeof(OpT);
     static constexpr int PK = DK + PADE;             // pitch of [*, DK] operands
     static constexpr int PC = C + PADE;              // pitch of [*, C] operands
-    static constexpr int PA = C + 4;                 // pitch of the fp32 A / T work matrix (16-byte rows)
+    static constexpr int PA = C + 4;                 // pitch of the fp32 A matrix (16-byte rows)
     static constexpr int SWZ = C * (int)sizeof(OpT) / 16 - 1;   // chunk XOR mask of the swizzled Ktil^T
     static constexpr int VE = 16 / (int)sizeof(In);  // elements per 16-byte vector of v / out
     static constexpr int PV = BV + VE;               // pitch of the staged V tile
@@ -125,7 +125,7 @@ struct ChunkCfg {
     static_assert(DK % 16 == 0 && BV % 16 == 0, "tile sizes");
     static_assert(16 % RS == 0, "a thread's rows stay inside one 16-row block");
     static_assert(size_t(C) * BV * sizeof(In) <= SZ_VT, "O staging fits the R^T slot");
-    static_assert(NW >= 4, "the block-doubling steps use four waves");
+    static_assert(NW >= 2, "A and P are formed by separate halves of the waves");
     static_assert(NW % NBV == 0, "each wave keeps one value column block");
 };
 
