@@ -118,9 +118,10 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
 
     const uint64_t ntok = varlen ? (uint64_t)T_total : (uint64_t)nseq * (uint64_t)T;
     const uint64_t nheads = (uint64_t)nseq * (uint64_t)H;
-    // the kernels address rows of one chunk with 32-bit offsets (64 H d elements)
+    // the kernels address the token rows of one chunk with 32-bit byte offsets
+    // (64 rows of H * d elements of up to 4 bytes)
     if (ntok * (uint64_t)H * 128u > (uint64_t)1 << 60 || nheads * 8u > (uint64_t)INT32_MAX ||
-        (uint64_t)H * 128u * 64u > (uint64_t)INT32_MAX)
+        (uint64_t)H * 128u * 64u * 4u > (uint64_t)INT32_MAX)
         return fail(KDA_ERR_BAD_SHAPE, "problem too large");
     const uint64_t es = f32 ? 4 : 2;
     const uint64_t nk = ntok * H * dk, nv = ntok * H * dv, nb = ntok * H, ns = nheads * dv * dk;

@@ -1,16 +1,15 @@
 // Fused chunkwise KDA prefill kernel for gfx950.
 //
-// One workgroup owns one (sequence, head, value block of BV state rows) and
-// walks that sequence's chunks of C tokens in order, keeping its BV x DK slice
-// of the fp32 state in registers the whole time.  Per chunk (cumulative decay
-// G_r = sum_{s<=r} log_alpha_s, per key channel, restarted at the chunk start;
-// S = incoming state):
+// One workgroup owns one (sequence, head, block of BV value rows) and walks the
+// sequence's chunks of C tokens in order.  Per chunk, with G_r the cumulative
+// log-decay of token r inside the chunk (per key channel) and S the state that
+// enters the chunk:
 //
 //   A_rj = beta_r sum_c k_rc k_jc e^{G_rc - G_jc}   (j <  r)   KK^T system
 //   P_rj =        sum_c q_rc k_jc e^{G_rc - G_jc}   (j <= r)   causal QK^T
-//   R    = Diag(beta) (V - Kbar S^T),  Kbar = K e^{G}         provisional errors
-//   E    = (I + A)^{-1} R                                     corrected errors
-//   O    = Qbar S^T + P E,             Qbar = Q e^{G}
+//   R    = Diag(beta) (V - Kbar S^T),   Kbar = K e^{G}         provisional errors
+//   (I + A) E = R                                              corrected errors
+//   O    = Qbar S^T + P E,              Qbar = Q e^{G}
 //   S^T <- Diag(e^{G_last}) S^T + Ktil^T E,  Ktil = K e^{G_last - G}
 //
 // This is the chunk mode of the "KDA derivation summary" page (sect. 6: the
@@ -18,32 +17,47 @@
 // corrects each token's provisional error), on the chunk skeleton of the
 // "Linear/sparse attention tutorial" page (sect. 6.2: intra-chunk causal part,
 // inter-chunk state hand-off, cumulative decay folded into the state and the
-// intra-chunk mask).  The equations above follow from the recurrence by
-// unrolling it over one chunk.
+// intra-chunk mask).  The equations follow from the recurrence by unrolling it
+// over one chunk.
 //
-// Decay factoring.  e^{G_r - G_j} is never formed pairwise; A and P are MFMA
-// products of pre-scaled operands.  Each chunk takes one of two exact paths,
-// chosen per chunk (uniformly for the workgroup):
-//  * fast path, when no key channel decays by more than 80 nats over the
-//    chunk: rows k e^{G}, q e^{G}, columns k e^{-G}.  All factors lie in
-//    [e^-80, e^80], far inside the fp32 / bf16 range.
-//  * sub-block path otherwise: rows are split into 16-row blocks b with start
-//    reference rho_b = G_{16b-1} and end reference sigma_b = G_{16b+15};
-//    rows k e^{G - rho_b} (<= |k|), diagonal-block columns k e^{rho_b - G}
-//    (bounded by the block's own decay), and for row block I > b the columns
-//    k e^{rho_I - G} (<= |k|).  Only the diagonal blocks carry factors above
-//    one: this path needs every channel to decay by less than 80 nats inside
-//    each 16-token block (the precondition in the public header).
-// Every exponent is a sum of same-sign partial sums (no cancellation).
+// Work split (wave specialisation).  The state-independent work of a chunk
+// (decay-scaled operands, A, the inverses of the diagonal blocks of I + A)
+// runs on four "operand" waves one chunk ahead of the state-dependent chain
+// (R, the solve, O, the state update), which runs on BV/16 "state" waves, one
+// per 16 value rows; the P tiles of the next chunk fill the state waves'
+// second segment (the operand waves make them when there is one state wave).  Value rows of the state evolve independently, so each
+// state wave runs its whole chain alone: its 16 x DK slice of the fp32 state
+// stays in MFMA accumulator registers across the whole sequence, and every
+// accumulator tile feeds the next product directly as an operand (a tile held
+// as lane l <-> D[4(l>>4)+i][l&15] is both the B operand over its rows and the
+// A operand of its transpose).  The two groups meet at two workgroup barriers
+// per chunk; everything the state waves read is double-buffered in LDS.
 //
-// (I + A) E = R is solved in fp32 by block forward substitution over the
-// 16-row blocks: the inverses of the 16x16 diagonal blocks come from forward
-// substitution in registers (one lane per column, the A entries broadcast
-// inside each 16-lane row with DPP); the off-diagonal updates and the
-// diagonal-block products run on fp32 MFMA, one wave per 16 value columns.
+// Decay factoring.  e^{G_r - G_j} is never formed pairwise.  Rows are split
+// into 16-token blocks and every key channel c gets a reference rho_I[c] per
+// block I: 0 (the chunk start) when the channel decays by at most 80 nats over
+// the whole chunk, else G just before block I.  The operand waves store, per
+// token r of block I,
+//   Kr = k e^{G_r - rho_I},  Qr = q e^{G_r - rho_I}   (both <= |k|, |q|)
+//   Kd = k e^{rho_I - G_r}                             (<= |k| e^{80})
+// and per channel e^{rho_I} and w_IJ = e^{rho_I - rho_J} (J < I, <= 1).  Then
+//   A/P tile (I, J) = [Kr|Qr]_I (Kd_J w_IJ)^T,  Kbar S^T = Kr (S Diag(e^{rho_I}))^T,
+// and Ktil = k e^{G_last - G_r} <= |k|.  When every channel of a chunk takes
+// the chunk-start reference, e^{rho_I} = w_IJ = 1 and both consumers skip the
+// scaling.  Every factor stays in range as long as no key channel decays by
+// more than 80 nats inside one 16-token block (the precondition in the public
+// header).  The factors come from alpha = e^{log_alpha} by running prefix and
+// suffix products inside each lane's tokens, times one exponential per
+// channel of the partial sums across lanes (all exponents <= 0).
 //
-// Matrix products run on MFMA 16x16 tiles: bf16 operands with fp32
-// accumulation in the bf16 entry points, fp32 operands in the fp32 ones.
+// (I + A) E = R is solved by block forward substitution over the 16-row
+// blocks, E_b = D_b (R_b - sum_{J<b} A_bJ E_J) with D_b the inverse of the
+// b-th diagonal block of I + A.  In the bf16 kernels the fp32 A, D_b and the
+// fp32 right-hand side enter the bf16 MFMA as hi + lo bf16 pairs.
+//
+// MFMA: bf16 operands with fp32 accumulation (16x16x32, or 16x16x16 for
+// 16-long contractions) in the bf16 entry points, fp32 16x16x4 in the fp32
+// ones.  Each accumulator chain uses one MFMA shape.
 #pragma once
 
 #include "kda_device.h"
@@ -51,98 +65,126 @@
 
 namespace kda {
 
-template <typename In, int DK, int BV, int C, int NW = 4>
-struct ChunkCfg {
-    typedef In OpT;                                  // MFMA operand type
-    static constexpr int NWAVE = NW;
-    static constexpr int NT = 64 * NW;               // threads
-    static constexpr int NB = C / 16;                // 16-row blocks per chunk
-    static constexpr int NBV = BV / 16;
-    static constexpr int NDK = DK / 16;
-    static constexpr int PADE = 16 / (int)sizeof(OpT);
-    static constexpr int PK = DK + PADE;             // pitch of [*, DK] operands
-    static constexpr int PC = C + PADE;              // pitch of [*, C] operands
-    static constexpr int PA = C + 4;                 // pitch of the fp32 A matrix (16-byte rows)
-    static constexpr int SWZ = C * (int)sizeof(OpT) / 16 - 1;   // chunk XOR mask of the swizzled Ktil^T
-    static constexpr int VE = 16 / (int)sizeof(In);  // elements per 16-byte vector of v / out
-    static constexpr int PV = BV + VE;               // pitch of the staged V tile
-    // pitch of the staged output tile (padded when it still fits the R^T slot)
-    static constexpr int PO = (C * (BV + VE) <= BV * (C + PADE)) ? BV + VE : BV;
-    static constexpr int NPAIR = NB * (NB + 1) / 2;  // (I, J <= I) column-operand tiles
-    // element-wise phase: each thread owns RS rows x 4 channels
-    static constexpr int NCG = DK / 4;
-    static constexpr int RS = (C * NCG > NT) ? (C * NCG / NT) : 1;
-    static constexpr int NSEG = C / RS;
-    static constexpr int NACT = NCG * NSEG;
-    static constexpr int SEG_PER_BLK = 16 / RS;
-    // fast path: every segment's decay below 80 / NSEG nats bounds the chunk's by 80
-    static constexpr float SEG_LIMIT = 80.f / NSEG;
-    static constexpr int NVCH = C * BV / VE;         // 16-byte vectors in a V / O tile
-    static constexpr int VCH_PER_T = (NVCH + NT - 1) / NT;
-    static constexpr int NOT = NB * NBV;             // output tiles (C x BV)
-    static constexpr int OT_PER_W = (NOT + NW - 1) / NW;
-    static constexpr int NST = NDK * NBV;            // state tiles (DK x BV, transposed state)
-    static constexpr int ST_PER_W = (NST + NW - 1) / NW;
+template <typename T> struct V4T { typedef T type __attribute__((ext_vector_type(4))); };
 
-    static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
-    static constexpr size_t SZ_KR = al(size_t(C) * PK * sizeof(OpT));
-    static constexpr size_t SZ_KCOL = al(size_t(NPAIR) * 16 * PK * sizeof(OpT));
-    static constexpr size_t SZ_GA = 2 * SZ_KR + SZ_KCOL;            // sub-block path: Kr, Qr, Kcol
-    static constexpr size_t SZ_KTT = al(size_t(DK) * PC * sizeof(OpT));
-    static constexpr size_t SZ_GB = 3 * SZ_KR + SZ_KTT;             // Kbar, Qbar, Khat, Ktil^T
-    static constexpr size_t SZ_G = SZ_GA > SZ_GB ? SZ_GA : SZ_GB;
-    static constexpr size_t SZ_S = al(size_t(BV) * PK * sizeof(OpT));
-    static constexpr size_t SZ_CC = al(size_t(C) * PC * sizeof(OpT));
-    static constexpr int PX = 20;                    // pitch of a wave's 16x16 fp32 substitution scratch
-    static constexpr size_t SZ_X = al(size_t(NW) * 16 * PX * sizeof(float));
-    static constexpr size_t SZ_V = al(size_t(C) * PV * sizeof(In));
-    static constexpr size_t SZ_SEG = al(size_t(NSEG) * DK * sizeof(float));
-    static constexpr size_t SZ_BETA = al(size_t(C) * sizeof(float));
-    static constexpr size_t SZ_GL = al(size_t(DK) * sizeof(float));
-    static constexpr size_t SZ_FLAG = 16;
-    static constexpr size_t SZ_A = al(size_t(C) * PA * sizeof(float));
-    static constexpr size_t SZ_VT = al(size_t(BV) * PC * sizeof(OpT));
-    // segment sums live in the E^T slot when they fit (they are dead by the time E^T is written)
-    static constexpr bool SEG_IN_ET = SZ_SEG <= SZ_VT;
-
-    static constexpr size_t O_KR = 0, O_QR = SZ_KR, O_KCOL = 2 * SZ_KR;
-    static constexpr size_t O_KBAR = 0, O_QBAR = SZ_KR, O_KHAT = 2 * SZ_KR, O_KTT = 3 * SZ_KR;
-    static constexpr size_t O_S = SZ_G;
-    static constexpr size_t O_X = O_S + SZ_S;
-    static constexpr size_t O_P = O_X + SZ_X;
-    static constexpr size_t O_V = O_P + SZ_CC;
-    static constexpr size_t O_SEGX = O_V + SZ_V;                         // segment sums, when not in E^T
-    static constexpr size_t O_BETA = O_SEGX + (SEG_IN_ET ? 0 : SZ_SEG);
-    static constexpr size_t O_GL = O_BETA + SZ_BETA;
-    static constexpr size_t O_FLAG = O_GL + SZ_GL;
-    static constexpr size_t O_A = O_FLAG + SZ_FLAG;
-    static constexpr size_t O_RT = O_A + SZ_A, O_ET = O_RT + SZ_VT, O_O = O_RT;
-    static constexpr size_t O_SEG = SEG_IN_ET ? O_ET : O_SEGX;
-    static constexpr size_t LDS = O_ET + SZ_VT;
-    static constexpr bool fits = LDS <= 160 * 1024;
-
-    static_assert(C % 16 == 0 && C <= 64, "chunk length");
-    static_assert(DK % 16 == 0 && BV % 16 == 0, "tile sizes");
-    static_assert(16 % RS == 0, "a thread's rows stay inside one 16-row block");
-    static_assert(size_t(C) * BV * sizeof(In) <= SZ_VT, "O staging fits the R^T slot");
-    static_assert(NW >= 2, "A and P are formed by separate halves of the waves");
-    static_assert(NW % NBV == 0, "each wave keeps one value column block");
-};
-
-template <typename T>
-__device__ __forceinline__ void store4(T *p, f32x4 v);
-template <>
-__device__ __forceinline__ void store4<float>(float *p, f32x4 v) { *(f32x4 *)p = v; }
-template <>
-__device__ __forceinline__ void store4<bf16>(bf16 *p, f32x4 v) {
-    bf16x4 b = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-    *(bf16x4 *)p = b;
+// ---------------------------------------------------------------------------
+// acc += A B over N 16-wide contraction tiles.  For tile t the lane supplies
+// a[t][e] = A[lane & 15][16t + 4(lane>>4) + e] and
+// b[t][e] = B[16t + 4(lane>>4) + e][lane & 15], e = 0..3; the result is in
+// accumulator layout.  KS selects the MFMA: 32 pairs tiles (2s, 2s+1) into one
+// 16x16x32 bf16 product (both operands permuted the same way along k), 16 uses
+// 16x16x16 bf16, 4 uses four 16x16x4 fp32 products per tile.
+// ---------------------------------------------------------------------------
+template <int KS, typename OpT, int N>
+__device__ __forceinline__ f32x4 mma_tiles(f32x4 acc, const typename V4T<OpT>::type (&a)[N],
+                                           const typename V4T<OpT>::type (&b)[N])
+{
+    if constexpr (KS == 32) {
+        static_assert(N % 2 == 0 && sizeof(OpT) == 2, "paired bf16 tiles");
+#pragma unroll
+        for (int s = 0; s < N / 2; ++s) {
+            const bf16x8 a8 = __builtin_shufflevector(a[2 * s], a[2 * s + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 b8 = __builtin_shufflevector(b[2 * s], b[2 * s + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc, 0, 0, 0);
+        }
+    } else if constexpr (KS == 16) {
+        static_assert(sizeof(OpT) == 2, "bf16 tiles");
+#pragma unroll
+        for (int t = 0; t < N; ++t)
+            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a[t]),
+                                                            __builtin_bit_cast(i16x4, b[t]), acc, 0, 0, 0);
+    } else {
+        static_assert(KS == 4 && sizeof(OpT) == 4, "fp32 tiles");
+#pragma unroll
+        for (int t = 0; t < N; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t][i], b[t][i], acc, 0, 0, 0);
+    }
+    return acc;
 }
 
-__device__ __forceinline__ constexpr int pair_index(int I, int J) { return I * (I + 1) / 2 + J; }
+template <typename OpT>
+__device__ __forceinline__ typename V4T<OpT>::type to_op(f32x4 x)
+{
+    typename V4T<OpT>::type r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = fromf<OpT>(x[i]);
+    return r;
+}
 
-// Writes v[0..RS) to row `row`, columns col0 .. col0+RS-1, of an array in the
-// chunk-swizzled layout of Panel::swz_index, in 16-byte (or smaller) pieces.
+template <typename OpT>
+__device__ __forceinline__ f32x4 to_f32(typename V4T<OpT>::type x)
+{
+    f32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = tof(x[i]);
+    return r;
+}
+
+// acc += A B for an fp32 A tile fragment and an operand-type B fragment.  In
+// the bf16 kernels A enters as hi + lo bf16 parts (about 16 significant bits).
+template <typename OpT>
+__device__ __forceinline__ f32x4 mma_fp32a(f32x4 acc, f32x4 a, typename V4T<OpT>::type b)
+{
+    typedef typename V4T<OpT>::type V4;
+    if constexpr (sizeof(OpT) == 4) {
+        const V4 aa[1] = {a}, bb[1] = {b};
+        return mma_tiles<4, OpT, 1>(acc, aa, bb);
+    } else {
+        const V4 hi = to_op<OpT>(a);
+        const V4 lo = to_op<OpT>(a - to_f32<OpT>(hi));
+        const V4 a2[2] = {hi, lo}, b2[2] = {b, b};
+        return mma_tiles<16, OpT, 2>(acc, a2, b2);
+    }
+}
+
+// A X for fp32 A and fp32 X fragments; bf16 kernels use hi/lo parts of both
+// (the lo x lo term is dropped).
+template <typename OpT>
+__device__ __forceinline__ f32x4 mma_fp32ab(f32x4 a, f32x4 x)
+{
+    typedef typename V4T<OpT>::type V4;
+    if constexpr (sizeof(OpT) == 4) {
+        const V4 aa[1] = {a}, xx[1] = {x};
+        return mma_tiles<4, OpT, 1>(zero4(), aa, xx);
+    } else {
+        const V4 ah = to_op<OpT>(a), al = to_op<OpT>(a - to_f32<OpT>(ah));
+        const V4 xh = to_op<OpT>(x), xl = to_op<OpT>(x - to_f32<OpT>(xh));
+        const V4 a3[3] = {ah, ah, al}, x3[3] = {xh, xl, xh};
+        return mma_tiles<16, OpT, 3>(zero4(), a3, x3);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T *p, f32x4 v) { *(typename V4T<T>::type *)p = to_op<T>(v); }
+
+// Raw buffer access (gfx9 descriptor word 3 = 0x00020000).  The descriptor is
+// built from a wave-uniform base and a byte bound; reads at or past the bound
+// return zeros and writes there are dropped, which is how tokens past the end
+// of a sequence become identity tokens and how their outputs are skipped.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, unsigned bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <typename T>
+__device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    if constexpr (sizeof(T) == 16) return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    else if constexpr (sizeof(T) == 8) return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    else return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+template <typename T>
+__device__ __forceinline__ void buf_store(T v, __amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    if constexpr (sizeof(T) == 16) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 0);
+    else __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, soff, 0);
+}
+
+// Writes v[0..RS) to row `row`, columns col0 .. col0+RS-1, of an array stored
+// with Panel::swz_index (16-byte chunks XOR-swizzled by row), in 16-byte or
+// smaller pieces.
 template <typename OpT, int RS>
 __device__ __forceinline__ void store_row_swz(OpT *base, int row, int col0, int pitch, int mask, const OpT (&v)[RS]) {
     constexpr int V = 16 / (int)sizeof(OpT);
@@ -157,69 +199,102 @@ __device__ __forceinline__ void store_row_swz(OpT *base, int row, int col0, int 
     }
 }
 
-// value of `v` in lane K of this lane's 16-lane row (DPP row_newbcast)
-template <int K>
-__device__ __forceinline__ float row_bcast(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + K, 0xF, 0xF, false));
-}
+// e^x via the hardware base-2 exponential; arguments here stay below 89, and
+// results under the fp32 normal range may flush to zero, which only drops
+// contributions that are that small.
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
-// Column j (= lane & 15) of the inverse of the unit lower-triangular 16x16
-// block I + L, where lane j holds column j of L in acol[0..15] (acol[i] =
-// L[i][j]).  Forward substitution x <- x - L[:, k] x_k, the L entries read
-// from lane k of the row.  Every lane of the wave must take part.
-__device__ __forceinline__ void inv_unit_lower16(const float (&acol)[16], float (&x)[16], int j)
+// Tiles of the lower block triangle (I >= J) of a chunk: the NB diagonal tiles
+// first, then the off-diagonal ones row by row.
+__host__ __device__ constexpr int tile_index(int NB, int I, int J)
 {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
-#define KDA_STEP(KK)                                                                                   \
-    {                                                                                                  \
-        _Pragma("unroll") for (int i = KK + 1; i < 16; ++i) x[i] -= row_bcast<KK>(acol[i]) * x[KK]; \
-    }
-    KDA_STEP(0) KDA_STEP(1) KDA_STEP(2) KDA_STEP(3) KDA_STEP(4) KDA_STEP(5) KDA_STEP(6) KDA_STEP(7)
-    KDA_STEP(8) KDA_STEP(9) KDA_STEP(10) KDA_STEP(11) KDA_STEP(12) KDA_STEP(13) KDA_STEP(14)
-#undef KDA_STEP
+    return I == J ? I : NB + I * (I - 1) / 2 + J;
 }
 
-template <typename In, int DK, int BV, int C, int NW>
-__global__ void __launch_bounds__(64 * NW, 1)
+template <typename In, int DK, int BV, int C>
+struct ChunkCfg {
+    typedef In OpT;                                  // MFMA operand type
+    static constexpr bool F32 = sizeof(In) == 4;
+    static constexpr int NB = C / 16;                // 16-token blocks per chunk
+    static constexpr int NBV = BV / 16;              // 16-row value blocks = state waves
+    static constexpr int NDK = DK / 16;
+    static constexpr int NXW = 4;                    // operand waves
+    static constexpr int NW = NBV + NXW;
+    static constexpr int NT = 64 * NW;
+    static constexpr int KD = F32 ? 4 : (DK % 32 == 0 ? 32 : 16);   // MFMA step of d_k contractions
+    static constexpr int KC = F32 ? 4 : (C % 32 == 0 ? 32 : 16);    // MFMA step of token contractions
+    static constexpr int PADE = 16 / (int)sizeof(In);
+    static constexpr int PK = DK + 4;                // rows of [token, d_k] operands
+    static constexpr int PC = C + PADE;              // rows of Ktil^T (16-byte aligned, chunk-swizzled)
+    static constexpr int SWZ = C * (int)sizeof(In) / 16 - 1;
+    static constexpr int PT = 20;                    // rows of an A (fp32) or P tile
+    static constexpr int NPAIR = NB * (NB + 1) / 2;
+    static constexpr int NOFF = NB * (NB - 1) / 2;
+    // operand-wave element mapping: wave x owns channels [x CPW, (x+1) CPW);
+    // a lane owns RS consecutive tokens of 4 channels
+    static constexpr int CPW = DK / NXW;
+    static constexpr int NCG = CPW / 4;
+    static constexpr int RS = (C * NCG > 64) ? C * NCG / 64 : 1;
+    static constexpr int NSEG = C / RS;
+    static constexpr int NACT = NCG * NSEG;
+    // scales block: e^{rho_I} [NB][DK], e^{G_last} [DK], beta [C], per-wave
+    // "all channels referenced to the chunk start" flags [NXW]
+    static constexpr int SC_GL = NB * DK, SC_BETA = NB * DK + DK, SC_FLAG = SC_BETA + C;
+    static constexpr float FAST_NATS = 80.f;
+
+    static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
+    static constexpr size_t SZ_R = al(size_t(C) * PK * sizeof(In));     // Kr, Qr, Kd
+    static constexpr size_t SZ_KT = al(size_t(DK) * PC * sizeof(In));   // Ktil^T
+    static constexpr size_t SZ_SC = al(size_t(SC_FLAG + NXW) * sizeof(float));
+    static constexpr size_t SZ_W = al(size_t(NOFF > 0 ? NOFF : 1) * DK * sizeof(float));
+    static constexpr size_t SZ_A = al(size_t(NPAIR) * 16 * PT * sizeof(float));
+    static constexpr size_t SZ_P = al(size_t(NPAIR) * 16 * PT * sizeof(In));
+    // double-buffered: written by the operand waves for chunk t+1 while the
+    // state waves read chunk t
+    static constexpr size_t O_KR = 0;
+    static constexpr size_t O_QR = O_KR + 2 * SZ_R;
+    static constexpr size_t O_KT = O_QR + 2 * SZ_R;
+    static constexpr size_t O_SC = O_KT + 2 * SZ_KT;
+    // single: Kd and w are private to the operand waves; A and P are written
+    // after the state waves' last read of the previous chunk's
+    static constexpr size_t O_KD = O_SC + 2 * SZ_SC;
+    static constexpr size_t O_W = O_KD + SZ_R;
+    static constexpr size_t O_A = O_W + SZ_W;
+    static constexpr size_t O_P = O_A + SZ_A;
+    static constexpr size_t LDS = O_P + SZ_P;
+    static constexpr bool fits = LDS <= 160 * 1024;
+
+    static_assert(C % 16 == 0 && C <= 64, "chunk length");
+    static_assert(DK % 16 == 0 && DK <= 128 && BV % 16 == 0 && BV <= 64, "tile sizes");
+    static_assert(16 % RS == 0, "a lane's tokens stay inside one 16-token block");
+    static_assert(NACT <= 64, "one operand wave covers its channels");
+    static_assert((NSEG & (NSEG - 1)) == 0, "segment scan over a power of two");
+};
+
+template <typename In, int DK, int BV, int C>
+__global__ void __launch_bounds__((ChunkCfg<In, DK, BV, C>::NT), 1)
 chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
                  const float *__restrict__ log_alpha, const float *__restrict__ beta,
                  const float *S0, In *__restrict__ out, float *S_final,
                  const int *__restrict__ cu_seqlens, int T, int H, int dv, int xcd_map)
 {
-    typedef ChunkCfg<In, DK, BV, C, NW> K;
-    typedef typename K::OpT OpT;
-    typedef In In4 __attribute__((ext_vector_type(4)));
-    constexpr int NB = K::NB, NBV = K::NBV, RS = K::RS, PK = K::PK, PC = K::PC, PA = K::PA;
-    constexpr int PV = K::PV, VE = K::VE, PO = K::PO;
-    // one bf16 MFMA shape for the whole kernel (16x16x32 unless a contraction is only 16 long)
-    constexpr int KSB = sizeof(OpT) == 4 ? 4 : ((DK % 32 == 0 && C % 32 == 0) ? 32 : 16);
-    typedef Panel<OpT, DK, KSB> PanelK;
-    typedef Panel<OpT, C, KSB> PanelC;
+    typedef ChunkCfg<In, DK, BV, C> K;
+    typedef typename V4T<In>::type V4;
+    constexpr int NB = K::NB, NDK = K::NDK, PK = K::PK, PC = K::PC, PT = K::PT, RS = K::RS;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[K::LDS];
-    OpT *sKr = (OpT *)(smem + K::O_KR);
-    OpT *sQr = (OpT *)(smem + K::O_QR);
-    OpT *sKcol = (OpT *)(smem + K::O_KCOL);
-    OpT *sKbar = (OpT *)(smem + K::O_KBAR);
-    OpT *sQbar = (OpT *)(smem + K::O_QBAR);
-    OpT *sKhat = (OpT *)(smem + K::O_KHAT);
-    OpT *sKtT = (OpT *)(smem + K::O_KTT);
-    OpT *sS = (OpT *)(smem + K::O_S);
-    float *sX = (float *)(smem + K::O_X);
-    OpT *sP = (OpT *)(smem + K::O_P);
-    In *sV = (In *)(smem + K::O_V);
-    float *sSeg = (float *)(smem + K::O_SEG);
-    float *sBeta = (float *)(smem + K::O_BETA);
-    float *sGL = (float *)(smem + K::O_GL);
-    int *sFlag = (int *)(smem + K::O_FLAG);
-    float *sA = (float *)(smem + K::O_A);
-    OpT *sRT = (OpT *)(smem + K::O_RT);
-    OpT *sET = (OpT *)(smem + K::O_ET);
-    In *sO = (In *)(smem + K::O_O);
+    In *const sKd = (In *)(smem + K::O_KD);
+    float *const sW = (float *)(smem + K::O_W);
+    float *const sA = (float *)(smem + K::O_A);
+    In *const sP = (In *)(smem + K::O_P);
+    auto bufKr = [&](long ch) { return (In *)(smem + K::O_KR + (ch & 1) * K::SZ_R); };
+    auto bufQr = [&](long ch) { return (In *)(smem + K::O_QR + (ch & 1) * K::SZ_R); };
+    auto bufKt = [&](long ch) { return (In *)(smem + K::O_KT + (ch & 1) * K::SZ_KT); };
+    auto bufSc = [&](long ch) { return (float *)(smem + K::O_SC + (ch & 1) * K::SZ_SC); };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) index
+    const int n = lane & 15, g = lane >> 4;
     const int nvb = dv / BV;
     int head, vb;
     if (xcd_map) {
@@ -242,472 +317,471 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         tok0 = (long)seq * T;
         len = T;
     }
-
-    // element-wise mapping: thread owns rows r0 .. r0+RS-1, channels c0 .. c0+3
-    const int cg = tid % K::NCG, seg = tid / K::NCG;
-    const bool ew = tid < K::NACT;
-    const int c0 = 4 * cg, r0 = seg * RS, blk = r0 / 16;
-
-    // The upper (J > I) 16x16 tiles of P are zero and never rewritten.
-    for (int idx = tid; idx < C * C; idx += K::NT) {
-        const int r = idx / C, j = idx % C;
-        if (j / 16 > r / 16) sP[r * PC + j] = fromf<OpT>(0.f);
-    }
-    if (tid < 2) sFlag[tid] = 0;
-
-    // Incoming state, held transposed (DK x BV) in accumulator layout: wave owns
-    // tiles st = wave + NW s; lane holds S[16 sb + (lane & 15)][16 ct + 4 (lane >> 4) + i].
-    f32x4 Sreg[K::ST_PER_W];
-#pragma unroll
-    for (int s = 0; s < K::ST_PER_W; ++s) {
-        const int st = wave + NW * s;
-        Sreg[s] = zero4();
-        if (st < K::NST) {
-            const int ct = st / NBV, sb = st % NBV;
-            const int irow = 16 * sb + (lane & 15), c = 16 * ct + 4 * (lane >> 4);
-            if (S0) Sreg[s] = *(const f32x4 *)(S0 + ((long)head * dv + vb * BV + irow) * DK + c);
-            store4(sS + irow * PK + c, Sreg[s]);
-        }
-    }
-
-    // -------- global loads of one chunk into registers (prefetched a chunk ahead).
-    // Rows past the end of the sequence load the last valid row (always in
-    // bounds, no branch around the loads) and are zeroed where they are used.
-    In4 kr[RS], qr[RS];
-    f32x4 gr[RS];
-    float betar = 0.f;
-    f32x4 vr[K::VCH_PER_T];
-    // Per-head base pointers; a token row is H*DK (H*dv) elements further on.
+    const long nch = (len + C - 1) / C;
     const int HDK = H * DK, HDV = H * dv;
-    const long hrow = tok0 * H + h;
-    const In *kb = k + hrow * DK + c0, *qb = q + hrow * DK + c0;
-    const float *gb = log_alpha + hrow * DK + c0;
-    const In *vbp = v + hrow * dv + vb * BV;
-    In *ob = out + hrow * dv + vb * BV;
-    const float *bb = beta + hrow;
-    auto prefetch = [&](long t0) {
-        const int last = (int)((len - t0 < C) ? len - t0 : C) - 1;
-        // V and beta first: the waits the compiler places around these loads then
-        // cover only older memory operations, not the q / k / log_alpha loads below.
-        const long tv = t0 * HDV;
+    const long hrow = tok0 * H + h;                 // token rows are H*d elements apart
+
+    // One lower-triangle tile pair (I, J) of chunk ch: the A tile (beta-scaled,
+    // strictly lower on the diagonal) and / or the P tile (lower incl. the
+    // diagonal).  Tiles are computed transposed, d[i] = X[16I + n][16J + 4g + i],
+    // so each lane stores four consecutive columns of one row.
+    auto tile_job = [&](long ch, int p, bool doA, bool doP, f32x4 *lt = nullptr) {
+        int I = p, J = p;
+        if (p >= NB) {
+            const int o = p - NB;
+            I = 1;
+            while ((I + 1) * I / 2 <= o) ++I;
+            J = o - I * (I - 1) / 2;
+        }
+        const float *scc = bufSc(ch);
+        const float *fl = scc + K::SC_FLAG;
+        const bool allfast = __builtin_amdgcn_readfirstlane((int)(fl[0] * fl[1] * fl[2] * fl[3])) != 0;
+        V4 cf[NDK];
 #pragma unroll
-        for (int u = 0; u < K::VCH_PER_T; ++u) {
-            const int idx = tid + u * K::NT;
-            if (K::NVCH % K::NT == 0 || idx < K::NVCH) {
-                const int r = min(idx / (BV / VE), last), cc = idx % (BV / VE);
-                vr[u] = *(const f32x4 *)(vbp + tv + r * HDV + cc * VE);
+        for (int t = 0; t < NDK; ++t) cf[t] = *(const V4 *)(sKd + (16 * J + n) * PK + 16 * t + 4 * g);
+        if (I > J && !allfast) {   // Kd_J w_IJ = k e^{rho_I - G} <= |k|
+            const float *wr = sW + (I * (I - 1) / 2 + J) * DK + 4 * g;
+#pragma unroll
+            for (int t = 0; t < NDK; ++t) {
+                const f32x4 w4 = *(const f32x4 *)(wr + 16 * t);
+                cf[t] = to_op<In>(to_f32<In>(cf[t]) * w4);
             }
         }
-        betar = bb[(t0 + min(tid, last)) * H];   // every lane loads (no branch); lanes >= C ignore it
-        const long tk = t0 * HDK;
-        if (ew) {
+        if (doA) {
+            const In *Kr = bufKr(ch);
+            V4 rk[NDK];
+#pragma unroll
+            for (int t = 0; t < NDK; ++t) rk[t] = *(const V4 *)(Kr + (16 * I + n) * PK + 16 * t + 4 * g);
+            const f32x4 da = mma_tiles<K::KD, In, NDK>(zero4(), cf, rk);
+            const float b = scc[K::SC_BETA + 16 * I + n];
+            f32x4 va;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) va[i] = (I > J || 4 * g + i < n) ? da[i] * b : 0.f;
+            *(f32x4 *)(sA + p * 16 * PT + n * PT + 4 * g) = va;
+            if (lt) {
+                // diagonal tile: also L itself in accumulator layout,
+                // lt[0][i] = L[4g + i][n] (and lt[1] = L^T, the tile just stored)
+                const f32x4 dl = mma_tiles<K::KD, In, NDK>(zero4(), rk, cf);
+                const f32x4 b4 = *(const f32x4 *)(scc + K::SC_BETA + 16 * I + 4 * g);
+                f32x4 vl;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vl[i] = (n < 4 * g + i) ? dl[i] * b4[i] : 0.f;
+                lt[0] = vl;
+                lt[1] = va;
+            }
+        }
+        if (doP) {
+            const In *Qr = bufQr(ch);
+            V4 rq[NDK];
+#pragma unroll
+            for (int t = 0; t < NDK; ++t) rq[t] = *(const V4 *)(Qr + (16 * I + n) * PK + 16 * t + 4 * g);
+            const f32x4 dp = mma_tiles<K::KD, In, NDK>(zero4(), cf, rq);
+            f32x4 vp;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vp[i] = (I > J || 4 * g + i <= n) ? dp[i] : 0.f;
+            store4(sP + p * 16 * PT + n * PT + 4 * g, vp);
+        }
+    };
+
+    if (wave >= K::NBV) {
+        // =============== operand waves: chunk t+1 while the state waves run chunk t
+        const int xw = wave - K::NBV;
+        const int cg = lane % K::NCG, seg = lane / K::NCG;
+        const bool act = lane < K::NACT;
+        const int c0 = xw * K::CPW + 4 * cg;        // this lane's channels c0 .. c0+3
+        const int r0 = seg * RS;                    // and tokens r0 .. r0+RS-1 (inactive lanes: >= C)
+        const int blk_src = ((r0 / 16) * (16 / RS)) * K::NCG + cg;   // lane holding rho of my block
+        typedef typename V4T<In>::type In4;
+
+        // Global loads, a chunk ahead, through buffer descriptors bounded to the
+        // chunk's valid tokens (tokens past the end read as zeros: identity
+        // tokens).  log_alpha of the next chunk is requested as soon as this
+        // chunk's log_alpha has been turned into decay factors (early in stage
+        // A); k, q and beta at the end of stage A.  Token i of this lane sits at
+        // the lane's fixed offset plus i token rows (the scalar offset).
+        In4 kr[RS], qr[RS];
+        f32x4 gr[RS];
+        float betar = 0.f;
+        const int rowb_in = HDK * (int)sizeof(In), rowb_f = HDK * 4;
+        const int voff_in = r0 * rowb_in + c0 * (int)sizeof(In), voff_f = r0 * rowb_f + c0 * 4;
+        auto chunk_valid = [&](long t0) { return (unsigned)((len - t0 < C) ? len - t0 : C); };
+        auto prefetch_g = [&](long t0) {
+            const __amdgpu_buffer_rsrc_t rg = buf_rsrc(log_alpha + (hrow + t0 * H) * DK, chunk_valid(t0) * rowb_f);
+#pragma unroll
+            for (int i = 0; i < RS; ++i) gr[i] = buf_load<f32x4>(rg, voff_f, i * rowb_f);
+        };
+        auto prefetch_kq = [&](long t0) {
+            const unsigned nv = chunk_valid(t0);
+            if (xw == 0) betar = buf_load<float>(buf_rsrc(beta + hrow + t0 * H, nv * H * 4), lane * H * 4, 0);
+            const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + (hrow + t0 * H) * DK, nv * rowb_in);
+            const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + (hrow + t0 * H) * DK, nv * rowb_in);
 #pragma unroll
             for (int i = 0; i < RS; ++i) {
-                const int ro = min(r0 + i, last) * HDK;
-                kr[i] = *(const In4 *)(kb + tk + ro);
-                qr[i] = *(const In4 *)(qb + tk + ro);
-                gr[i] = *(const f32x4 *)(gb + tk + ro);
+                kr[i] = buf_load<In4>(rk, voff_in, i * rowb_in);
+                qr[i] = buf_load<In4>(rq, voff_in, i * rowb_in);
             }
-        }
-    };
-    // Output rows of a chunk staged in sO go to HBM one chunk later, after the
-    // next prefetch has been issued, so the stores drain while the loads wait.
-    auto store_out = [&](long t0, int nv) {
-        const long tv = t0 * HDV;
-#pragma unroll
-        for (int u = 0; u < K::VCH_PER_T; ++u) {
-            const int idx = tid + u * K::NT;
-            if (idx < K::NVCH) {
-                const int r = idx / (BV / VE), cc = idx % (BV / VE);
-                if (r < nv) *(f32x4 *)(ob + tv + r * HDV + cc * VE) = *(const f32x4 *)(sO + r * PO + cc * VE);
-            }
-        }
-    };
+        };
 
-    const long nch = (len + C - 1) / C;
-    if (nch > 0) prefetch(0);
-    __syncthreads();
-
-    f32x4 Oacc[K::OT_PER_W];
-    for (long ch = 0; ch < nch; ++ch) {
-        const long t0 = ch * C;
-        const int nval = (int)((len - t0 < C) ? len - t0 : C);
-
-        // ---- (1) per-thread inclusive scan of log_alpha over its rows; stage beta and V;
-        //      flag the chunk for the sub-block path if any segment decays too fast
-        float L[RS][4];
-        if (ew) {
-#pragma unroll
-            for (int i = 0; i < RS; ++i)
-                if (r0 + i >= nval) {   // identity tokens past the end: k = q = 0, log_alpha = 0
-                    gr[i] = zero4();
-                    kr[i] = In4{};
-                    qr[i] = In4{};
-                }
-            bool steep = false;
+        // ---- stage A: cumulative decay, references, scaled operands
+        auto stage_a = [&](long ch) {
+            const long t0 = ch * C;
+            const int nval = (int)((len - t0 < C) ? len - t0 : C);
+            float tot[4], inc[4], exc[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float acc = 0.f;
 #pragma unroll
-                for (int i = 0; i < RS; ++i) {
-                    acc += gr[i][j];
-                    L[i][j] = acc;
+                for (int i = 0; i < RS; ++i) acc += gr[i][j];
+                tot[j] = acc;
+                inc[j] = acc;
+            }
+            // inclusive scan of the segment sums over the lanes of one channel group
+#pragma unroll
+            for (int d = 1; d < K::NSEG; d <<= 1)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float y = __shfl_up(inc[j], d * K::NCG, 64);
+                    if (seg >= d) inc[j] += y;
                 }
-                sSeg[seg * DK + c0 + j] = acc;
-                steep |= !(fabsf(acc) <= K::SEG_LIMIT);
-            }
-            if (steep) sFlag[ch & 1] = 1;
-        }
-        if (tid < C) sBeta[tid] = (tid < nval) ? betar : 0.f;
+            float rhoI[NB][4], ref[4], glast[4];
+            bool lane_fast = true;
 #pragma unroll
-        for (int u = 0; u < K::VCH_PER_T; ++u) {
-            const int idx = tid + u * K::NT;
-            if (idx < K::NVCH) {
-                const int r = idx / (BV / VE), cc = idx % (BV / VE);
-                *(f32x4 *)(sV + r * PV + cc * VE) = (r < nval) ? vr[u] : zero4();
-            }
-        }
-        __syncthreads();
-        const bool fast = __builtin_amdgcn_readfirstlane(sFlag[ch & 1]) == 0;
-
-        // ---- (2) decay factors and the pre-scaled operands of A and P
-        if (ew) {
-            if (fast) {
-                float pre[4] = {0.f, 0.f, 0.f, 0.f}, tot[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < 4; ++j) {
+                exc[j] = inc[j] - tot[j];                                       // G before my first token
+                glast[j] = __shfl(inc[j], (K::NSEG - 1) * K::NCG + cg, 64);      // G_last
+                const bool fastc = glast[j] >= -K::FAST_NATS;
+                lane_fast = lane_fast && fastc;
+                const float rb = __shfl(exc[j], blk_src, 64);                   // G before my block
+                ref[j] = fastc ? 0.f : rb;
 #pragma unroll
-                for (int s = 0; s < K::NSEG; ++s)
+                for (int I = 0; I < NB; ++I) {
+                    const float r = __shfl(exc[j], (I * (16 / RS)) * K::NCG + cg, 64);
+                    rhoI[I][j] = fastc ? 0.f : r;
+                }
+            }
+            float al[RS][4];
+#pragma unroll
+            for (int i = 0; i < RS; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) al[i][j] = fexp(gr[i][j]);   // alpha of each token
+            // gr is free: request the next chunk's log_alpha now (the empty asm
+            // keeps the loads from being hoisted above the uses of gr)
+            __asm__ volatile("" ::: "memory");
+            if (ch + 1 < nch) prefetch_g(t0 + C);
+            In *Kr = bufKr(ch), *Qr = bufQr(ch), *Kt = bufKt(ch);
+            float *sc = bufSc(ch);
+            // forward over my tokens: e^{G - ref} by prefix products -> Kr, Qr
+            // (and Kd = k / e^{G - ref} where some channel keeps a block reference)
+            {
+                float pp[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pp[j] = fexp(exc[j] - ref[j]);
+#pragma unroll
+                for (int i = 0; i < RS; ++i) {
+                    f32x4 vkr, vqr, vkd;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const float t = sSeg[s * DK + c0 + j];
-                        tot[j] += t;
-                        if (s < seg) pre[j] += t;
-                    }
-                float eGL[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) eGL[j] = __expf(tot[j]);
-                if (seg == 0) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) sGL[c0 + j] = eGL[j];
-                }
-                OpT kt[4][RS];
-#pragma unroll
-                for (int i = 0; i < RS; ++i) {
-                    const int r = r0 + i;
-                    f32x4 vKb, vQb, vKh;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float g = pre[j] + L[i][j];          // G_r (chunk-relative)
-                        const float e = __expf(g), ie = __expf(-g);
+                        pp[j] *= al[i][j];
                         const float kf = tof(kr[i][j]);
-                        vKb[j] = kf * e;                           // k e^{G}
-                        vQb[j] = tof(qr[i][j]) * e;                // q e^{G}
-                        vKh[j] = kf * ie;                          // k e^{-G}
-                        kt[j][i] = fromf<OpT>(vKh[j] * eGL[j]);    // k e^{G_last - G}
+                        vkr[j] = kf * pp[j];                       // k e^{G - ref}
+                        vqr[j] = tof(qr[i][j]) * pp[j];            // q e^{G - ref}
                     }
-                    store4(sKbar + r * PK + c0, vKb);
-                    store4(sQbar + r * PK + c0, vQb);
-                    store4(sKhat + r * PK + c0, vKh);
-                }
+                    if (act) {
+                        const int r = r0 + i;
+                        store4(Kr + r * PK + c0, vkr);
+                        store4(Qr + r * PK + c0, vqr);
+                        if (!lane_fast) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) store_row_swz<OpT, RS>(sKtT, c0 + j, r0, PC, K::SWZ, kt[j]);
-            } else {
-                float BT[NB][4];                // per-block total log-decay
-                float pre[4], post[4];          // in-block sums before / after this segment
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                    for (int I = 0; I < NB; ++I) BT[I][j] = 0.f;
-                    pre[j] = 0.f;
-                    post[j] = 0.f;
-                }
-#pragma unroll
-                for (int s = 0; s < K::NSEG; ++s) {
-                    const int I = s / K::SEG_PER_BLK;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float t = sSeg[s * DK + c0 + j];
-                        BT[I][j] += t;
-                        if (I == blk && s < seg) pre[j] += t;
-                        if (I == blk && s > seg) post[j] += t;
-                    }
-                }
-                float invTb[4], dI[NB][4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float total = 0.f;
-#pragma unroll
-                    for (int I = 0; I < NB; ++I) total += BT[I][j];
-                    if (seg == 0) sGL[c0 + j] = __expf(total);
-                    invTb[j] = __expf(-BT[blk][j]);     // e^{rho_b - sigma_b}
-                    float between = 0.f;               // block totals strictly between blk and I
-#pragma unroll
-                    for (int I = 0; I < NB; ++I) {
-                        dI[I][j] = 0.f;
-                        if (I > blk) {
-                            dI[I][j] = __expf(between);     // e^{rho_I - sigma_b}
-                            between += BT[I][j];
+                            for (int j = 0; j < 4; ++j) vkd[j] = tof(kr[i][j]) * __builtin_amdgcn_rcpf(pp[j]);   // k e^{ref - G}
+                            store4(sKd + r * PK + c0, vkd);
                         }
                     }
                 }
-#pragma unroll
-                for (int i = 0; i < RS; ++i) {
-                    const int r = r0 + i;
-                    f32x4 vKr, vQr, vKd, vKc[NB];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float suf = L[RS - 1][j] - L[i][j];      // sum over rows i+1 .. RS-1
-                        const float x = __expf(pre[j] + L[i][j]);     // e^{G_r - rho_b}
-                        const float y = __expf(post[j] + suf);        // e^{sigma_b - G_r}
-                        const float kf = tof(kr[i][j]);
-                        vKr[j] = kf * x;
-                        vQr[j] = tof(qr[i][j]) * x;
-                        vKd[j] = kf * y * invTb[j];                   // k e^{rho_b - G_r}
-#pragma unroll
-                        for (int I = 0; I < NB; ++I) vKc[I][j] = kf * y * dI[I][j];   // k e^{rho_I - G_r}
-                    }
-                    store4(sKr + r * PK + c0, vKr);
-                    store4(sQr + r * PK + c0, vQr);
-                    store4(sKcol + (pair_index(blk, blk) * 16 + (r - 16 * blk)) * PK + c0, vKd);
-#pragma unroll
-                    for (int I = 0; I < NB; ++I)
-                        if (I > blk) store4(sKcol + (pair_index(I, blk) * 16 + (r - 16 * blk)) * PK + c0, vKc[I]);
-                }
             }
-        }
-        if (tid == 0) sFlag[(ch + 1) & 1] = 0;   // slot of the next chunk (last read a chunk ago)
-        if (ch + 1 < nch) prefetch(t0 + C);
-        if (ch > 0) store_out(t0 - C, C);   // the previous chunk was a full one
-        __syncthreads();
-
-        // ---- (3) A (fp32, beta-scaled, strictly lower) and P (inclusive lower) on MFMA.
-        //      Tiles are computed transposed (column block J of A / P against row block I),
-        //      so each lane ends up with 4 consecutive columns of one row: vector stores,
-        //      one beta per lane.  Half the waves make A, half P; each takes whole column
-        //      blocks (0 and 3, or 1 and 2, when there are four).
-        {
-            constexpr int HW = NW / 2;
-            const bool isA = wave < HW;
-            const int hw = isA ? wave : wave - HW;
-            const int n = lane & 15, g = lane >> 4;
-#pragma unroll
-            for (int J = 0; J < NB; ++J) {
-                const int owner = (HW >= NB) ? J : (NB == 4) ? ((J < 2 ? J : 3 - J) % HW) : (J % HW);
-                if (owner != hw) continue;
-                PanelK cp;
-                if (fast) cp.load(sKhat + 16 * J * PK, PK, lane);
-#pragma unroll
-                for (int I = J; I < NB; ++I) {
-                    if (!fast) cp.load(sKcol + pair_index(I, J) * 16 * PK, PK, lane);
-                    PanelK rp;
-                    rp.load(fast ? ((isA ? sKbar : sQbar) + 16 * I * PK) : ((isA ? sKr : sQr) + 16 * I * PK), PK, lane);
-                    const f32x4 acc = mma(zero4(), cp, rp);   // acc[i] = X[16I + n][16J + 4g + i]
-                    const int r = 16 * I + n, j0 = 16 * J + 4 * g;
-                    f32x4 val;
-                    if (isA) {
-                        const float b = sBeta[r];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) val[i] = (J < I || 4 * g + i < n) ? acc[i] * b : 0.f;
-                        *(f32x4 *)(sA + r * PA + j0) = val;
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) val[i] = (J < I || 4 * g + i <= n) ? acc[i] : 0.f;
-                        store4(sP + r * PC + j0, val);
-                    }
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- (4) sub-block path only: turn Kr / Qr / Kd into Kbar, Qbar, Ktil^T
-        if (!fast) {
-            OpT kt[4][RS];
-            if (ew) {
-                float before[4] = {0.f, 0.f, 0.f, 0.f}, after[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < K::NSEG; ++s) {
-                    const int I = s / K::SEG_PER_BLK;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float t = sSeg[s * DK + c0 + j];
-                        if (I < blk) before[j] += t;
-                        else after[j] += t;
-                    }
-                }
+            // backward: e^{G_last - G} by suffix products -> Ktil, and Kd = Ktil e^{-G_last}
+            // where every channel of the lane takes the chunk-start reference
+            {
+                float sf[4], gli[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    before[j] = __expf(before[j]);   // e^{rho_b}
-                    after[j] = __expf(after[j]);     // e^{G_last - rho_b}
+                    sf[j] = fexp(glast[j] - inc[j]);
+                    gli[j] = fexp(-glast[j]);
                 }
+                In kt[4][RS];
 #pragma unroll
-                for (int i = 0; i < RS; ++i) {
-                    const int r = r0 + i;
-                    OpT *pk = sKr + r * PK + c0, *pq = sQr + r * PK + c0;
-                    const OpT *pd = sKcol + (pair_index(blk, blk) * 16 + (r - 16 * blk)) * PK + c0;
-                    f32x4 vk, vq;
+                for (int i = RS - 1; i >= 0; --i) {
+                    f32x4 vkd;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        vk[j] = tof(pk[j]) * before[j];                   // k e^{G}
-                        vq[j] = tof(pq[j]) * before[j];                   // q e^{G}
-                        kt[j][i] = fromf<OpT>(tof(pd[j]) * after[j]);     // k e^{G_last - G}
+                        const float ktf = tof(kr[i][j]) * sf[j];   // k e^{G_last - G}
+                        kt[j][i] = fromf<In>(ktf);
+                        vkd[j] = ktf * gli[j];                     // k e^{-G}
+                        sf[j] *= al[i][j];
                     }
-                    store4(pk, vk);   // Kbar over Kr, Qbar over Qr (same slots)
-                    store4(pq, vq);
+                    if (act && lane_fast) store4(sKd + (r0 + i) * PK + c0, vkd);
+                }
+                if (act) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) store_row_swz<In, RS>(Kt, c0 + j, r0, PC, K::SWZ, kt[j]);
                 }
             }
-            __syncthreads();   // Kd reads done before Ktil^T overwrites the Kcol region
-            if (ew) {
+            // per-channel scales, written by the lanes of the first segment
+            const bool wave_fast = __all(lane_fast);
+            if (seg == 0) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) store_row_swz<OpT, RS>(sKtT, c0 + j, r0, PC, K::SWZ, kt[j]);
+                for (int j = 0; j < 4; ++j) {
+                    sc[K::SC_GL + c0 + j] = fexp(glast[j]);
+                    if (wave_fast) {   // every reference is the chunk start: all factors are 1
+#pragma unroll
+                        for (int I = 0; I < NB; ++I) sc[I * DK + c0 + j] = 1.f;
+                    } else {
+#pragma unroll
+                        for (int I = 0; I < NB; ++I) {
+                            sc[I * DK + c0 + j] = fexp(rhoI[I][j]);
+#pragma unroll
+                            for (int J = 0; J < I; ++J)
+                                sW[(I * (I - 1) / 2 + J) * DK + c0 + j] = fexp(rhoI[I][j] - rhoI[J][j]);
+                        }
+                    }
+                }
+            }
+            if (lane == 0) sc[K::SC_FLAG + xw] = wave_fast ? 1.f : 0.f;
+            if (xw == 0 && lane < C) sc[K::SC_BETA + lane] = (lane < nval) ? betar : 0.f;
+        };
+
+        // ---- stage B: A tiles (and P tiles when there is a single state wave),
+        //      diagonal-block inverses
+        auto stage_b = [&](long ch) {
+            for (int p = xw; p < K::NPAIR; p += K::NXW) {
+                if (p < NB && !K::F32) {
+                    // D_p = (I + L)^{-1} for the strictly lower diagonal tile L, as
+                    // (I - L)(I + L^2)(I + L^4)(I + L^8) (L^16 = 0).  With two
+                    // tiles in accumulator layout, one fp32 MFMA product gives
+                    // acc(X^T Y); D_p^T is built that way from acc(L), acc(L^T)
+                    // and stored so that lane (n, g) writes row n, columns 4g..4g+3.
+                    // (The powers of L can grow like binomial coefficients before
+                    // they cancel, about 1e-4 relative at worst: fine for the bf16
+                    // kernels, the fp32 ones use the substitution below.)
+                    f32x4 lt[2];
+                    tile_job(ch, p, true, K::NBV == 1, lt);
+                    auto mm = [](f32x4 x, f32x4 y) {   // acc(X^T Y)
+                        const f32x4 a[1] = {x}, b[1] = {y};
+                        return mma_tiles<4, float, 1>(zero4(), a, b);
+                    };
+                    const f32x4 L1 = lt[0], U1 = lt[1];
+                    const f32x4 U2 = mm(L1, U1), L2 = mm(U1, L1);
+                    const f32x4 U3 = mm(L1, U2), L4 = mm(U2, L2), U4 = mm(L2, U2);
+                    const f32x4 L8 = mm(U4, L4);
+                    f32x4 id;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) id[i] = (4 * g + i == n) ? 1.f : 0.f;
+                    const f32x4 M1t = id - U1 + U2 - U3;              // ((I - L)(I + L^2))^T
+                    const f32x4 M2t = M1t + mm(L4, M1t);              // ... (I + L^4)
+                    const f32x4 Dt = M2t + mm(L8, M2t);               // ... (I + L^8)
+                    *(f32x4 *)(sA + p * 16 * PT + n * PT + 4 * g) = Dt;
+                } else if (p < NB) {
+                    // fp32 kernels: column n of D_p by forward substitution over the
+                    // rows of the stored tile (lanes of the other 16-lane rows repeat
+                    // the work and store nothing)
+                    tile_job(ch, p, true, K::NBV == 1);
+                    float *At = sA + p * 16 * PT;
+                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                    float x[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float *Lr = At + i * PT;
+                        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                        for (int kk = 0; kk + 1 < i; kk += 2) {
+                            s0 += Lr[kk] * x[kk];
+                            s1 += Lr[kk + 1] * x[kk + 1];
+                        }
+                        if (i & 1) s0 += Lr[i - 1] * x[i - 1];
+                        x[i] = ((i == n) ? 1.f : 0.f) - (s0 + s1);
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                    if (lane < 16) {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) At[i * PT + n] = x[i];
+                    }
+                } else {
+                    tile_job(ch, p, true, K::NBV == 1);
+                }
+            }
+        };
+
+        // Same barrier sequence as the state waves: two per chunk plus two.
+        if (nch > 0) {
+            prefetch_g(0);
+            prefetch_kq(0);
+            stage_a(0);
+            if (nch > 1) prefetch_kq(C);
+        }
+        __syncthreads();
+        if (nch > 0) stage_b(0);
+        __syncthreads();
+        for (long ch = 0; ch < nch; ++ch) {
+            if (ch + 1 < nch) {
+                stage_a(ch + 1);
+                if (ch + 2 < nch) prefetch_kq((ch + 2) * C);
+            }
+            __syncthreads();
+            if (ch + 1 < nch) stage_b(ch + 1);
+            __syncthreads();
+        }
+    } else {
+        // =============== state waves: value rows 16 cb .. 16 cb + 15 of the block
+        const int cb = wave;
+        const long vrow = (long)head * dv + vb * BV + 16 * cb;   // first state row of this wave
+        // bf16: lane (n, g) loads row 16 (2 u + g/2) + n, columns 8 (g&1) .. +7;
+        // fp32: row 16 u + n, columns 4g .. 4g+3 (u = load index)
+        const int rowb_v = HDV * (int)sizeof(In);
+        const int voff_v = (K::F32 ? n : (16 * (g >> 1) + n)) * rowb_v + (K::F32 ? 4 * g : 8 * (g & 1)) * (int)sizeof(In);
+        const int voff_o = n * rowb_v + 4 * g * (int)sizeof(In);   // output row 16 I + n, columns 4g .. 4g+3
+        const long vcol = hrow * dv + vb * BV + 16 * cb;
+
+        // State, transposed, in accumulator layout: Sacc[ct][i] = S[16 cb + n][16 ct + 4g + i].
+        f32x4 Sacc[NDK];
+#pragma unroll
+        for (int ct = 0; ct < NDK; ++ct)
+            Sacc[ct] = S0 ? *(const f32x4 *)(S0 + (vrow + n) * DK + 16 * ct + 4 * g) : zero4();
+
+        // V of the chunk, prefetched a chunk ahead; an MFMA against an identity
+        // fragment moves it into accumulator layout.
+        constexpr int NVL = K::F32 ? NB : (NB + 1) / 2;
+        typedef In VL __attribute__((ext_vector_type(K::F32 ? 4 : 8)));
+        VL vr[NVL];
+        auto prefetch_v = [&](long t0) {
+            const unsigned nv = (unsigned)((len - t0 < C) ? len - t0 : C);
+            const __amdgpu_buffer_rsrc_t rv = buf_rsrc(v + vcol + t0 * HDV, nv * rowb_v);
+#pragma unroll
+            for (int u = 0; u < NVL; ++u) vr[u] = buf_load<VL>(rv, voff_v, (K::F32 ? 16 : 32) * u * rowb_v);
+        };
+        // identity fragments: k-slot s of the lane's operand -> column n
+        VL ident[K::F32 ? 1 : 2];
+#pragma unroll
+        for (int e = 0; e < (K::F32 ? 4 : 8); ++e) {
+            if constexpr (K::F32) {
+                ident[0][e] = (4 * g + e == n) ? 1.f : 0.f;
+            } else {
+                ident[0][e] = fromf<In>((8 * g + e == n) ? 1.f : 0.f);
+                ident[1][e] = fromf<In>((8 * g + e - 16 == n) ? 1.f : 0.f);
+            }
+        }
+        if (nch > 0) prefetch_v(0);
+        __syncthreads();
+        if (K::NBV >= 2 && nch > 0) {
+            for (int p = cb; p < K::NPAIR; p += K::NBV) tile_job(0, p, false, true);
+        }
+        __syncthreads();
+
+        V4 Eb[NB];   // corrected errors of the chunk, operand type: E[16b + 4g + i][n]
+        for (long ch = 0; ch < nch; ++ch) {
+            const long t0 = ch * C;
+            const int nval = (int)((len - t0 < C) ? len - t0 : C);
+            const In *Kr = bufKr(ch), *Qr = bufQr(ch);
+            const float *sc = bufSc(ch);
+            const float *fl = sc + K::SC_FLAG;
+            const bool allfast = __builtin_amdgcn_readfirstlane((int)(fl[0] * fl[1] * fl[2] * fl[3])) != 0;
+            // ---- R = beta (V - Kbar S^T) and (Qbar S^T)^T, per 16-token block I
+            f32x4 R[NB], O1[NB];
+            V4 ss[NDK];
+            auto rows = [&](int I) {
+                V4 ak[NDK], bq[NDK];
+#pragma unroll
+                for (int ct = 0; ct < NDK; ++ct) {
+                    ak[ct] = *(const V4 *)(Kr + (16 * I + n) * PK + 16 * ct + 4 * g);
+                    bq[ct] = *(const V4 *)(Qr + (16 * I + n) * PK + 16 * ct + 4 * g);
+                }
+                R[I] = mma_tiles<K::KD, In, NDK>(zero4(), ak, ss);    // [16I + 4g + i][n]
+                O1[I] = mma_tiles<K::KD, In, NDK>(zero4(), ss, bq);   // [v = 4g + i][16I + n]
+            };
+            if (allfast) {
+#pragma unroll
+                for (int ct = 0; ct < NDK; ++ct) ss[ct] = to_op<In>(Sacc[ct]);
+#pragma unroll
+                for (int I = 0; I < NB; ++I) rows(I);
+            } else {
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+#pragma unroll
+                    for (int ct = 0; ct < NDK; ++ct) {
+                        const f32x4 er = *(const f32x4 *)(sc + I * DK + 16 * ct + 4 * g);
+                        ss[ct] = to_op<In>(Sacc[ct] * er);        // S Diag(e^{rho_I}), transposed
+                    }
+                    rows(I);
+                }
+            }
+#pragma unroll
+            for (int I = 0; I < NB; ++I) {
+                const f32x4 b4 = *(const f32x4 *)(sc + K::SC_BETA + 16 * I + 4 * g);
+                f32x4 vt;                                           // V[16I + 4g + i][n]
+                if constexpr (K::F32) {
+                    const V4 va[1] = {vr[I]}, vi[1] = {ident[0]};
+                    vt = mma_tiles<4, In, 1>(zero4(), va, vi);
+                } else {
+                    vt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[I / 2], ident[I & 1], zero4(), 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) R[I][i] = b4[i] * (vt[i] - R[I][i]);
+            }
+            if (ch + 1 < nch) prefetch_v(t0 + C);
+
+            // ---- (I + A) E = R, block forward substitution
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                f32x4 y = zero4();
+#pragma unroll
+                for (int J = 0; J < b; ++J) {
+                    const f32x4 a = *(const f32x4 *)(sA + tile_index(NB, b, J) * 16 * PT + n * PT + 4 * g);
+                    y = mma_fp32a<In>(y, a, Eb[J]);
+                }
+                const f32x4 d = *(const f32x4 *)(sA + b * 16 * PT + n * PT + 4 * g);
+                const f32x4 e = mma_fp32ab<In>(d, R[b] - y);
+                Eb[b] = to_op<In>(e);
+            }
+
+            // ---- O^T = (Qbar S^T)^T + E^T P^T, written as O rows (rows past the end dropped)
+            const __amdgpu_buffer_rsrc_t ro = buf_rsrc(out + vcol + t0 * HDV, (unsigned)nval * rowb_v);
+#pragma unroll
+            for (int I = 0; I < NB; ++I) {
+                V4 pb[NB];
+#pragma unroll
+                for (int J = 0; J < NB; ++J)
+                    pb[J] = (J <= I) ? *(const V4 *)(sP + tile_index(NB, I, J) * 16 * PT + n * PT + 4 * g) : V4{};
+                const f32x4 o = O1[I] + mma_tiles<K::KC, In, NB>(zero4(), Eb, pb);   // O[16I + n][16cb + 4g + i]
+                buf_store(to_op<In>(o), ro, voff_o, 16 * I * rowb_v);
+            }
+            __syncthreads();
+
+            // ---- S^T <- Diag(e^{G_last}) S^T + Ktil^T E
+            const In *Kt = bufKt(ch);
+#pragma unroll
+            for (int ct = 0; ct < NDK; ++ct) {
+                const f32x4 gl = *(const f32x4 *)(sc + K::SC_GL + 16 * ct + 4 * g);
+                V4 ka[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    ka[b] = *(const V4 *)(Kt + Panel<In, 16>::swz_index(16 * ct + n, 16 * b + 4 * g, PC, K::SWZ));
+                Sacc[ct] = mma_tiles<K::KC, In, NB>(Sacc[ct] * gl, ka, Eb);
+            }
+            // with two or more state waves, they also form the next chunk's P tiles
+            if (K::NBV >= 2 && ch + 1 < nch) {
+                for (int p = cb; p < K::NPAIR; p += K::NBV) tile_job(ch + 1, p, false, true);
             }
             __syncthreads();
         }
-
-        // ---- (5) wave 0: inverses D_b' of the diagonal 16x16 blocks of I + A, in place in
-        //      sA (forward substitution in registers, DPP broadcasts); the other waves
-        //      meanwhile form R = beta (V - Kbar S^T), stored transposed.
-        if (wave == 0) {
-            const int b = min(lane >> 4, NB - 1), j = lane & 15;
-            float *Ab = sA + 16 * b * PA + 16 * b;
-            float acol[16], x[16];
+        if (S_final) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acol[i] = Ab[i * PA + j];
-            inv_unit_lower16(acol, x, j);
-            if ((lane >> 4) < NB) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) Ab[i * PA + j] = x[i];
-            }
-        } else {
-            const int n = lane & 15, g = lane >> 4;
-            for (int t = wave - 1; t < K::NOT; t += NW - 1) {
-                const int rb = t / NBV, cb2 = t % NBV;
-                PanelK kp, sp;
-                kp.load(sKbar + 16 * rb * PK, PK, lane);
-                sp.load(sS + 16 * cb2 * PK, PK, lane);
-                const f32x4 ak = mma(zero4(), kp, sp);   // (Kbar S^T)[16rb + 4g + i][16cb2 + n]
-                f32x4 rv;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * rb + 4 * g + i;
-                    rv[i] = sBeta[r] * (tof(sV[r * PV + 16 * cb2 + n]) - ak[i]);
-                }
-                store4(sRT + (16 * cb2 + n) * PC + 16 * rb + 4 * g, rv);
-            }
-        }
-        __syncthreads();
-
-        // Each wave owns one value column block cb of the C x BV outputs (all its
-        // row blocks rb) and the matching state column block, so the operand panels
-        // of cb are loaded once per phase.
-        const int cb = wave % NBV;
-
-        // ---- (6) E = (I + A)^{-1} R by block forward substitution,
-        //      E_b = D_b' (R_b - sum_{J<b} A_bJ E_J).  Value columns are independent, so
-        //      wave w solves column block w on its own (fp32 MFMA, wave-local LDS round
-        //      trips, no workgroup barrier) and writes E^T for the updates below.
-        if (wave < NBV) {
-            float *xs = sX + wave * 16 * K::PX;
-            const int n = lane & 15, g = lane >> 4, kq = lane >> 4;
-            const OpT *et = sET + (16 * cb + n) * PC;          // row v = 16 cb + n of E^T
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                f32x4 y = zero4();                               // sum_{J<b} A_bJ E_J
-#pragma unroll
-                for (int J = 0; J < b; ++J)
-#pragma unroll
-                    for (int k0 = 0; k0 < 16; k0 += 4)
-                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * b + n) * PA + 16 * J + k0 + kq],
-                                                                 tof(et[16 * J + k0 + kq]), y, 0, 0, 0);
-                typedef OpT Op4 __attribute__((ext_vector_type(4)));
-                const Op4 rr = *(const Op4 *)(sRT + (16 * cb + n) * PC + 16 * b + 4 * g);
-                f32x4 xv;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) xv[i] = tof(rr[i]) - y[i];   // X[16b + 4g + i][n]
-                *(f32x4 *)(xs + n * K::PX + 4 * g) = xv;                  // X^T, row n
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                f32x4 e = zero4();
-#pragma unroll
-                for (int k0 = 0; k0 < 16; k0 += 4)
-                    e = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * b + n) * PA + 16 * b + k0 + kq],
-                                                             xs[n * K::PX + k0 + kq], e, 0, 0, 0);
-                store4(sET + (16 * cb + n) * PC + 16 * b + 4 * g, e);    // E^T[16cb + n][16b + 4g + i]
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            }
-        }
-        __syncthreads();
-
-        // ---- (7) O^T = S Qbar^T + E^T P^T;  S^T <- Diag(e^{G_last}) S^T + Ktil^T E
-        {
-            PanelC ep;
-            ep.load(sET + 16 * cb * PC, PC, lane);
-            PanelK sp;
-            sp.load(sS + 16 * cb * PK, PK, lane);
-#pragma unroll
-            for (int s = 0; s < K::OT_PER_W; ++s) {
-                const int ot = wave + NW * s;
-                if (ot < K::NOT) {
-                    const int rb = ot / NBV;
-                    PanelK qp;
-                    qp.load(sQbar + 16 * rb * PK, PK, lane);
-                    PanelC pp;
-                    pp.load(sP + 16 * rb * PC, PC, lane, 16 * (rb + 1));
-                    Oacc[s] = mma(zero4(), sp, qp);               // O^T[16cb + 4g + i][16rb + n]
-                    Oacc[s] = mma(Oacc[s], ep, pp, 16 * (rb + 1));
-                }
-            }
-#pragma unroll
-            for (int s = 0; s < K::ST_PER_W; ++s) {
-                const int st = wave + NW * s;
-                if (st < K::NST) {
-                    const int ct = st / NBV;
-                    PanelC kp;
-                    kp.load_swz(sKtT, 16 * ct, PC, K::SWZ, lane);
-                    const f32x4 acc = mma(zero4(), kp, ep);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) Sreg[s][i] = Sreg[s][i] * sGL[16 * ct + 4 * (lane >> 4) + i] + acc[i];
-                }
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int s = 0; s < K::OT_PER_W; ++s) {
-            const int ot = wave + NW * s;
-            if (ot < K::NOT) {
-                const int rb = ot / NBV;
-                store4(sO + (16 * rb + (lane & 15)) * PO + 16 * cb + 4 * (lane >> 4), Oacc[s]);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < K::ST_PER_W; ++s) {
-            const int st = wave + NW * s;
-            if (st < K::NST) {
-                const int ct = st / NBV;
-                store4(sS + (16 * cb + (lane & 15)) * PK + 16 * ct + 4 * (lane >> 4), Sreg[s]);
-            }
-        }
-        __syncthreads();
-    }
-    if (nch > 0) store_out((nch - 1) * C, (int)(len - (nch - 1) * C));
-
-    if (S_final) {
-#pragma unroll
-        for (int s = 0; s < K::ST_PER_W; ++s) {
-            const int st = wave + NW * s;
-            if (st < K::NST) {
-                const int ct = st / NBV, sb = st % NBV;
-                const int irow = 16 * sb + (lane & 15), c = 16 * ct + 4 * (lane >> 4);
-                *(f32x4 *)(S_final + ((long)head * dv + vb * BV + irow) * DK + c) = Sreg[s];
-            }
+            for (int ct = 0; ct < NDK; ++ct) *(f32x4 *)(S_final + (vrow + n) * DK + 16 * ct + 4 * g) = Sacc[ct];
         }
     }
 }
 
-// Waves per workgroup of the chunk kernel.
-constexpr int kChunkWaves = 4;
-
 template <typename In, int DK, int BV, int C>
 hipError_t launch_chunk_t(const ChunkArgs &a)
 {
-    typedef ChunkCfg<In, DK, BV, C, kChunkWaves> K;
+    typedef ChunkCfg<In, DK, BV, C> K;
     if constexpr (!K::fits) {
         return hipErrorInvalidConfiguration;
     } else {
@@ -716,7 +790,7 @@ hipError_t launch_chunk_t(const ChunkArgs &a)
         const int grid = nheads * nvb;
         if (grid == 0) return hipSuccess;
         const int xcd_map = (nheads % 8 == 0) ? 1 : 0;
-        hipLaunchKernelGGL((chunk_fwd_kernel<In, DK, BV, C, kChunkWaves>), dim3(grid), dim3(K::NT), 0, a.stream,
+        hipLaunchKernelGGL((chunk_fwd_kernel<In, DK, BV, C>), dim3(grid), dim3(K::NT), 0, a.stream,
                            (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S0,
                            (In *)a.out, a.S_final, a.cu_seqlens, a.T, a.H, a.dv, xcd_map);
         return hipGetLastError();
@@ -739,7 +813,7 @@ template <typename In, int DK>
 constexpr bool chunk_fits_dk(int BV, int C)
 {
 #define KDA_CASE(BV_, C_) \
-    if (BV == BV_ && C == C_) return ChunkCfg<In, DK, BV_, C_, kChunkWaves>::fits;
+    if (BV == BV_ && C == C_) return ChunkCfg<In, DK, BV_, C_>::fits;
     KDA_CASE(16, 16) KDA_CASE(16, 32) KDA_CASE(16, 64)
     KDA_CASE(32, 16) KDA_CASE(32, 32) KDA_CASE(32, 64)
     KDA_CASE(64, 16) KDA_CASE(64, 32) KDA_CASE(64, 64)

@@ -174,6 +174,22 @@ def test_chunk_decay_at_precondition_edge(dev):
     assert_close("mixed decay", f64(out), f64(sf), o_ref, s_ref, TOL["bf16"])
 
 
+def test_chunk_repeated_key_full_writes(dev):
+    """Every token of a head writes with the same unit key, beta = 1 and no
+    decay: I + A is all ones below the diagonal, the hardest case for the
+    triangular solve (its inverse has entries of +-1 while the powers of A
+    grow like binomial coefficients)."""
+    for dtype, tol in (("bf16", TOL["bf16"]), ("f32", TOL["f32"])):
+        note(f"case repeated key: B1 T200 H2 d64 {dtype}, beta = 1, log_alpha = 0")
+        p = kda_synth.prefill(1, 200, 2, 64, 64, dtype=dtype, s0_sigma=0.1, seed=21, device=dev)
+        p.k.copy_(p.k[:, :1].expand_as(p.k))
+        p.beta.fill_(1.0)
+        p.log_alpha.zero_()
+        out, sf = gpu_chunk(p, 64 if dtype == "bf16" else 32)
+        o_ref, s_ref = oracle_dense(p)
+        assert_close(f"repeated key {dtype}", f64(out), f64(sf), o_ref, s_ref, tol)
+
+
 def test_chunk_mixes_fast_and_sub_block_paths(dev):
     """Strong decay only in some chunks: those take the sub-block path, the
     others the fast path, inside one sequence (and in fp32 mode)."""
