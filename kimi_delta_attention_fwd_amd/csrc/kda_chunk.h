@@ -395,10 +395,11 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 
         // Global loads, a chunk ahead, through buffer descriptors bounded to the
         // chunk's valid tokens (tokens past the end read as zeros: identity
-        // tokens).  log_alpha of the next chunk is requested as soon as this
-        // chunk's log_alpha has been turned into decay factors (early in stage
-        // A); k, q and beta at the end of stage A.  Token i of this lane sits at
-        // the lane's fixed offset plus i token rows (the scalar offset).
+        // tokens).  Each input of the next chunk is requested as soon as this
+        // chunk's copy is no longer needed: log_alpha once it has become decay
+        // factors (early in stage A), q after the forward pass, k and beta at
+        // the end of stage A.  Token i of this lane sits at the lane's fixed
+        // offset plus i token rows (the scalar offset).
         In4 kr[RS], qr[RS];
         f32x4 gr[RS];
         float betar = 0.f;
@@ -410,16 +411,17 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 #pragma unroll
             for (int i = 0; i < RS; ++i) gr[i] = buf_load<f32x4>(rg, voff_f, i * rowb_f);
         };
-        auto prefetch_kq = [&](long t0) {
+        auto prefetch_q = [&](long t0) {
+            const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + (hrow + t0 * H) * DK, chunk_valid(t0) * rowb_in);
+#pragma unroll
+            for (int i = 0; i < RS; ++i) qr[i] = buf_load<In4>(rq, voff_in, i * rowb_in);
+        };
+        auto prefetch_k = [&](long t0) {
             const unsigned nv = chunk_valid(t0);
             if (xw == 0) betar = buf_load<float>(buf_rsrc(beta + hrow + t0 * H, nv * H * 4), lane * H * 4, 0);
             const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + (hrow + t0 * H) * DK, nv * rowb_in);
-            const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + (hrow + t0 * H) * DK, nv * rowb_in);
 #pragma unroll
-            for (int i = 0; i < RS; ++i) {
-                kr[i] = buf_load<In4>(rk, voff_in, i * rowb_in);
-                qr[i] = buf_load<In4>(rq, voff_in, i * rowb_in);
-            }
+            for (int i = 0; i < RS; ++i) kr[i] = buf_load<In4>(rk, voff_in, i * rowb_in);
         };
 
         // ---- stage A: cumulative decay, references, scaled operands
@@ -498,6 +500,9 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                     }
                 }
             }
+            // q is free: request the next chunk's q
+            __asm__ volatile("" ::: "memory");
+            if (ch + 1 < nch) prefetch_q(t0 + C);
             // backward: e^{G_last - G} by suffix products -> Ktil, and Kd = Ktil e^{-G_last}
             // where every channel of the lane takes the chunk-start reference
             {
@@ -613,9 +618,10 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         // Same barrier sequence as the state waves: two per chunk plus two.
         if (nch > 0) {
             prefetch_g(0);
-            prefetch_kq(0);
+            prefetch_q(0);
+            prefetch_k(0);
             stage_a(0);
-            if (nch > 1) prefetch_kq(C);
+            if (nch > 1) prefetch_k(C);
         }
         __syncthreads();
         if (nch > 0) stage_b(0);
@@ -623,7 +629,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         for (long ch = 0; ch < nch; ++ch) {
             if (ch + 1 < nch) {
                 stage_a(ch + 1);
-                if (ch + 2 < nch) prefetch_kq((ch + 2) * C);
+                if (ch + 2 < nch) prefetch_k((ch + 2) * C);
             }
             __syncthreads();
             if (ch + 1 < nch) stage_b(ch + 1);

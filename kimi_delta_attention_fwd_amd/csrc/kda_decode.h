@@ -12,9 +12,10 @@
 //
 // The state dominates the traffic (64 KiB per head at d = 128 against < 1 KiB
 // of token data), so the kernel is a streaming kernel: each row is read once
-// and written once with 16-byte accesses, every lane keeps all of its rows in
-// flight before computing, and the two row reductions use DPP within groups
-// of DK/16 lanes.
+// and written once with 16-byte nontemporal accesses (the state is not reused
+// within a step, so it should not displace cached data), every lane keeps all
+// of its rows in flight before computing, and the two row reductions use DPP
+// within groups of DK/16 lanes.
 #pragma once
 
 #include "kda_device.h"
@@ -60,7 +61,7 @@ decode_step_kernel(const In *__restrict__ q, const In *__restrict__ k, const In 
         if (row < dv) {
             const float *src = S + (head * dv + row) * DK + 4 * sub;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) s[p][u] = *(const f32x4 *)(src + 4 * LPR * u);
+            for (int u = 0; u < 4; ++u) s[p][u] = __builtin_nontemporal_load((const f32x4 *)(src + 4 * LPR * u));
             vi[p] = tof(v[head * dv + row]);
         }
     }
@@ -89,7 +90,7 @@ decode_step_kernel(const In *__restrict__ q, const In *__restrict__ k, const In 
             o = group_sum<LPR>(o);
             float *dst = S + (head * dv + row) * DK + 4 * sub;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) *(f32x4 *)(dst + 4 * LPR * u) = s[p][u];
+            for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(s[p][u], (f32x4 *)(dst + 4 * LPR * u));
             if (sub == 0) out[head * dv + row] = fromf<In>(o);
         }
     }
