@@ -21,11 +21,13 @@
 // over one chunk.
 //
 // Work split (wave specialisation).  The state-independent work of a chunk
-// (decay-scaled operands, A, the inverses of the diagonal blocks of I + A)
-// runs on four "operand" waves one chunk ahead of the state-dependent chain
-// (R, the solve, O, the state update), which runs on BV/16 "state" waves, one
-// per 16 value rows; the P tiles of the next chunk fill the state waves'
-// second segment (the operand waves make them when there is one state wave).  Value rows of the state evolve independently, so each
+// (decay-scaled operands, the diagonal A tiles and the inverses of the
+// diagonal blocks of I + A) runs on four "operand" waves one chunk ahead of
+// the state-dependent chain (R, the solve, O, the state update), which runs
+// on BV/16 "state" waves, one per 16 value rows.  The state waves fill their
+// second segment with the next chunk's P tiles and off-diagonal A tiles (with
+// a single state wave: the off-diagonal P tiles only, the operand waves keep
+// the rest).  Value rows of the state evolve independently, so each
 // state wave runs its whole chain alone: its 16 x DK slice of the fp32 state
 // stays in MFMA accumulator registers across the whole sequence, and every
 // accumulator tile feeds the next product directly as an operand (a tile held
@@ -211,6 +213,17 @@ __host__ __device__ constexpr int tile_index(int NB, int I, int J)
     return I == J ? I : NB + I * (I - 1) / 2 + J;
 }
 
+// True when every operand wave flagged its channels as referenced to the chunk
+// start (flags are 1.0 or 0.0 in LDS); wave-uniform.
+template <int NF>
+__device__ __forceinline__ bool all_flags(const float *fl)
+{
+    float m = 1.f;
+#pragma unroll
+    for (int i = 0; i < NF; ++i) m *= fl[i];
+    return __builtin_amdgcn_readfirstlane((int)m) != 0;
+}
+
 template <typename In, int DK, int BV, int C>
 struct ChunkCfg {
     typedef In OpT;                                  // MFMA operand type
@@ -325,7 +338,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     // strictly lower on the diagonal) and / or the P tile (lower incl. the
     // diagonal).  Tiles are computed transposed, d[i] = X[16I + n][16J + 4g + i],
     // so each lane stores four consecutive columns of one row.
-    auto tile_job = [&](long ch, int p, bool doA, bool doP, f32x4 *lt = nullptr) {
+    auto tile_job = [&](long ch, int p, bool doA, bool doP, f32x4 *lt = nullptr) __attribute__((always_inline)) {
         int I = p, J = p;
         if (p >= NB) {
             const int o = p - NB;
@@ -335,7 +348,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         }
         const float *scc = bufSc(ch);
         const float *fl = scc + K::SC_FLAG;
-        const bool allfast = __builtin_amdgcn_readfirstlane((int)(fl[0] * fl[1] * fl[2] * fl[3])) != 0;
+        const bool allfast = all_flags<K::NXW>(fl);
         V4 cf[NDK];
 #pragma unroll
         for (int t = 0; t < NDK; ++t) cf[t] = *(const V4 *)(sKd + (16 * J + n) * PK + 16 * t + 4 * g);
@@ -406,17 +419,17 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         const int rowb_in = HDK * (int)sizeof(In), rowb_f = HDK * 4;
         const int voff_in = r0 * rowb_in + c0 * (int)sizeof(In), voff_f = r0 * rowb_f + c0 * 4;
         auto chunk_valid = [&](long t0) { return (unsigned)((len - t0 < C) ? len - t0 : C); };
-        auto prefetch_g = [&](long t0) {
+        auto prefetch_g = [&](long t0) __attribute__((always_inline)) {
             const __amdgpu_buffer_rsrc_t rg = buf_rsrc(log_alpha + (hrow + t0 * H) * DK, chunk_valid(t0) * rowb_f);
 #pragma unroll
             for (int i = 0; i < RS; ++i) gr[i] = buf_load<f32x4>(rg, voff_f, i * rowb_f);
         };
-        auto prefetch_q = [&](long t0) {
+        auto prefetch_q = [&](long t0) __attribute__((always_inline)) {
             const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + (hrow + t0 * H) * DK, chunk_valid(t0) * rowb_in);
 #pragma unroll
             for (int i = 0; i < RS; ++i) qr[i] = buf_load<In4>(rq, voff_in, i * rowb_in);
         };
-        auto prefetch_k = [&](long t0) {
+        auto prefetch_k = [&](long t0) __attribute__((always_inline)) {
             const unsigned nv = chunk_valid(t0);
             if (xw == 0) betar = buf_load<float>(buf_rsrc(beta + hrow + t0 * H, nv * H * 4), lane * H * 4, 0);
             const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + (hrow + t0 * H) * DK, nv * rowb_in);
@@ -425,7 +438,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         };
 
         // ---- stage A: cumulative decay, references, scaled operands
-        auto stage_a = [&](long ch) {
+        auto stage_a = [&](long ch) __attribute__((always_inline)) {
             const long t0 = ch * C;
             const int nval = (int)((len - t0 < C) ? len - t0 : C);
             float tot[4], inc[4], exc[4];
@@ -554,10 +567,11 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             if (xw == 0 && lane < C) sc[K::SC_BETA + lane] = (lane < nval) ? betar : 0.f;
         };
 
-        // ---- stage B: A tiles (and P tiles when there is a single state wave),
-        //      diagonal-block inverses
-        auto stage_b = [&](long ch) {
-            for (int p = xw; p < K::NPAIR; p += K::NXW) {
+        // ---- stage B: the diagonal A tiles and their block inverses (with P
+        //      when there is a single state wave, which then also leaves the
+        //      off-diagonal A tiles here)
+        auto stage_b = [&](long ch) __attribute__((always_inline)) {
+            for (int p = xw; p < (K::NBV == 1 ? K::NPAIR : NB); p += K::NXW) {
                 if (p < NB && !K::F32) {
                     // D_p = (I + L)^{-1} for the strictly lower diagonal tile L, as
                     // (I - L)(I + L^2)(I + L^4)(I + L^8) (L^16 = 0).  With two
@@ -610,7 +624,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                         for (int i = 0; i < 16; ++i) At[i * PT + n] = x[i];
                     }
                 } else {
-                    tile_job(ch, p, true, K::NBV == 1);
+                    tile_job(ch, p, true, false);
                 }
             }
         };
@@ -657,7 +671,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         constexpr int NVL = K::F32 ? NB : (NB + 1) / 2;
         typedef In VL __attribute__((ext_vector_type(K::F32 ? 4 : 8)));
         VL vr[NVL];
-        auto prefetch_v = [&](long t0) {
+        auto prefetch_v = [&](long t0) __attribute__((always_inline)) {
             const unsigned nv = (unsigned)((len - t0 < C) ? len - t0 : C);
             const __amdgpu_buffer_rsrc_t rv = buf_rsrc(v + vcol + t0 * HDV, nv * rowb_v);
 #pragma unroll
@@ -674,11 +688,25 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 ident[1][e] = fromf<In>((8 * g + e - 16 == n) ? 1.f : 0.f);
             }
         }
+        // Tiles the state waves form for a chunk, in their second segment: with
+        // two or more state waves the off-diagonal pairs (A and P) and then the
+        // diagonal P tiles, else the off-diagonal P tiles.  Jobs are dealt in
+        // snake order so the heavier pairs spread evenly over the waves.
+        constexpr int NJOB = K::NBV >= 2 ? K::NPAIR : K::NOFF;
+        constexpr int NROUND = (NJOB + K::NBV - 1) / K::NBV;
+        auto y_tiles = [&](long ch) __attribute__((always_inline)) {
+#pragma unroll
+            for (int r = 0; r < NROUND; ++r) {
+                const int s = r * K::NBV + ((r & 1) ? K::NBV - 1 - cb : cb);
+                if (s < NJOB) {
+                    const int p = s < K::NOFF ? NB + s : s - K::NOFF;
+                    tile_job(ch, p, K::NBV >= 2 && p >= NB, true);
+                }
+            }
+        };
         if (nch > 0) prefetch_v(0);
         __syncthreads();
-        if (K::NBV >= 2 && nch > 0) {
-            for (int p = cb; p < K::NPAIR; p += K::NBV) tile_job(0, p, false, true);
-        }
+        if (nch > 0) y_tiles(0);
         __syncthreads();
 
         V4 Eb[NB];   // corrected errors of the chunk, operand type: E[16b + 4g + i][n]
@@ -688,11 +716,11 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             const In *Kr = bufKr(ch), *Qr = bufQr(ch);
             const float *sc = bufSc(ch);
             const float *fl = sc + K::SC_FLAG;
-            const bool allfast = __builtin_amdgcn_readfirstlane((int)(fl[0] * fl[1] * fl[2] * fl[3])) != 0;
+            const bool allfast = all_flags<K::NXW>(fl);
             // ---- R = beta (V - Kbar S^T) and (Qbar S^T)^T, per 16-token block I
             f32x4 R[NB], O1[NB];
             V4 ss[NDK];
-            auto rows = [&](int I) {
+            auto rows = [&](int I) __attribute__((always_inline)) {
                 V4 ak[NDK], bq[NDK];
 #pragma unroll
                 for (int ct = 0; ct < NDK; ++ct) {
@@ -771,10 +799,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                     ka[b] = *(const V4 *)(Kt + Panel<In, 16>::swz_index(16 * ct + n, 16 * b + 4 * g, PC, K::SWZ));
                 Sacc[ct] = mma_tiles<K::KC, In, NB>(Sacc[ct] * gl, ka, Eb);
             }
-            // with two or more state waves, they also form the next chunk's P tiles
-            if (K::NBV >= 2 && ch + 1 < nch) {
-                for (int p = cb; p < K::NPAIR; p += K::NBV) tile_job(ch + 1, p, false, true);
-            }
+            // ---- the next chunk's tiles
+            if (ch + 1 < nch) y_tiles(ch + 1);
             __syncthreads();
         }
         if (S_final) {
