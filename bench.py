@@ -177,14 +177,26 @@ def bench_long(args, torch, kda, kda_synth, stream, steps=3):
     sf = torch.empty((B, H, dv, dk), dtype=torch.float32, device="cuda")
     h = stream.cuda_stream
 
+    # segment-parallel schedule with the library's segment count (workspace
+    # allocated before the timed region), and the single pass for reference
+    nseg = kda.kda_chunk_auto_segments(B, T, H, dk, dv, C, 0)
+    wsb = kda.kda_chunk_segmented_workspace_bytes(B, H, dk, dv, nseg)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+
     def launch():
+        kda.kda_chunk_fwd_segmented(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out, sf, B, T, H, dk, dv, C, nseg,
+                                    ws, wsb, h)
+
+    def launch_single():
         kda.kda_chunk_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out, sf, B, T, H, dk, dv, C, h)
 
     wall, kms = time_launches(launch, stream, steps, 1, torch)
+    _, kms1 = time_launches(launch_single, stream, 2, 1, torch)
     nbytes = prefill_bytes(B * T * H, dk, dv, B * H, s0=True, sfinal=True)
-    del p, out, sf
+    del p, out, sf, ws
     return dict(workload="long prefill: B=1 H=16 T=65536 dk=dv=128 bf16 C=64, S0 in, S_final out",
-                tokens_per_s=B * T * steps / wall, kernel_ms=kms,
+                schedule=f"segment-parallel, {nseg} segments per sequence (map pass, composition, rerun)",
+                tokens_per_s=B * T * steps / wall, kernel_ms=kms, single_pass_kernel_ms=kms1,
                 hbm_gbs=round(nbytes / (kms * 1e-3) / 1e9, 1),
                 hbm_frac=round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
 

@@ -30,7 +30,8 @@
  * v and out are fp32 as well.
  *
  * OWNERSHIP AND EXECUTION.  Every pointer is device memory owned by the
- * caller.  The library allocates nothing, keeps no mutable global state and is
+ * caller (the segmented entry points take their scratch space as a
+ * caller-owned workspace).  The library allocates nothing, keeps no mutable global state and is
  * thread-safe.  Work is enqueued asynchronously on `stream` (a hipStream_t
  * passed as void*; NULL is the default stream).  KDA_OK means "validated and
  * enqueued"; faults inside a kernel surface at the caller's next
@@ -58,6 +59,7 @@
 #ifndef LIBKDA_H
 #define LIBKDA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -127,6 +129,82 @@ kda_status_t kda_chunk_fwd_varlen_f32(const float *q, const float *k, const floa
                                       const float *S0, float *out, float *S_final,
                                       const int32_t *cu_seqlens, int N, int T_total,
                                       int H, int dk, int dv, int C, void *stream);
+
+/*
+ * Segment-parallel chunkwise prefill, for long sequences with few (sequence,
+ * head) pairs.  Same operation, layouts and results (up to rounding) as
+ * kda_chunk_fwd / kda_chunk_fwd_varlen; only the schedule differs.  The chunk
+ * mode of the "KDA derivation summary" page (sect. 6) hands the state from
+ * chunk to chunk, and every quantity a chunk forms from it is affine in the
+ * incoming state; so is a run of chunks: S_end = S_start M + N, with M
+ * (dk x dk) and N (dv x dk) independent of S_start (derived from the chunk
+ * equations, not stated on the pages).  The chunks of every sequence are cut
+ * into nseg consecutive segments of ceil(chunks / nseg) chunks, and three
+ * passes run on `stream`:
+ *   1. every segment but the last, in parallel, runs from S_start = 0 with dk
+ *      extra state rows that start at the identity and see v = 0: the real
+ *      rows end at N, the extra rows at M;
+ *   2. the segments' incoming states are composed in order, in fp32,
+ *      starting from S0;
+ *   3. every segment, in parallel, reruns from its incoming state, writing
+ *      out and (last segment) S_final.
+ * nseg = 1 is the plain single pass (workspace may be NULL).
+ *
+ *   nseg       1 .. 1024; kda_chunk_auto_segments() picks one for a dense batch.
+ *   workspace  device memory owned by the caller, 256-byte aligned, at least
+ *              kda_chunk_segmented_workspace_bytes(...) bytes, disjoint from
+ *              every other argument; its contents on entry do not matter and
+ *              are undefined on exit.  Calls that share a workspace must not
+ *              overlap in time.
+ * Other arguments as in kda_chunk_fwd (dense) / kda_chunk_fwd_varlen.
+ * S_final may be the same pointer as S0 here too.
+ */
+kda_status_t kda_chunk_fwd_segmented(const void *q, const void *k, const void *v,
+                                     const float *log_alpha, const float *beta,
+                                     const float *S0, void *out, float *S_final,
+                                     int B, int T, int H, int dk, int dv, int C,
+                                     int nseg, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/* fp32 q, k, v, out variant of kda_chunk_fwd_segmented. */
+kda_status_t kda_chunk_fwd_segmented_f32(const float *q, const float *k, const float *v,
+                                         const float *log_alpha, const float *beta,
+                                         const float *S0, float *out, float *S_final,
+                                         int B, int T, int H, int dk, int dv, int C,
+                                         int nseg, void *workspace, size_t workspace_bytes,
+                                         void *stream);
+
+/* Packed-sequence variants: every sequence is cut into nseg segments. */
+kda_status_t kda_chunk_fwd_varlen_segmented(const void *q, const void *k, const void *v,
+                                            const float *log_alpha, const float *beta,
+                                            const float *S0, void *out, float *S_final,
+                                            const int32_t *cu_seqlens, int N, int T_total,
+                                            int H, int dk, int dv, int C, int nseg,
+                                            void *workspace, size_t workspace_bytes,
+                                            void *stream);
+kda_status_t kda_chunk_fwd_varlen_segmented_f32(const float *q, const float *k, const float *v,
+                                                const float *log_alpha, const float *beta,
+                                                const float *S0, float *out, float *S_final,
+                                                const int32_t *cu_seqlens, int N, int T_total,
+                                                int H, int dk, int dv, int C, int nseg,
+                                                void *workspace, size_t workspace_bytes,
+                                                void *stream);
+
+/*
+ * Workspace bytes of the segmented entry points for nseq sequences (B or N)
+ * of H heads: 4 * nseq * H * ((nseg - 1) (dv + dk) dk + nseg dv dk), the
+ * first part rounded up to 256 bytes.  0 for nseg = 1 or invalid sizes.
+ */
+size_t kda_chunk_segmented_workspace_bytes(int nseq, int H, int dk, int dv, int nseg);
+
+/*
+ * Segment count for a dense batch (fp32_inputs: 0 for the bf16 entry points,
+ * 1 for the fp32 ones), from a model of the run time: 1 when the plain pass
+ * already fills the GPU, more when few (sequence, head) pairs walk many
+ * chunks.  Queries the current device's compute-unit count (256 assumed if
+ * that fails); never fails, returns at least 1.
+ */
+int kda_chunk_auto_segments(int B, int T, int H, int dk, int dv, int C, int fp32_inputs);
 
 /*
  * One decode step ("KDA derivation summary" page, sect. 6, fused recurrent

@@ -22,6 +22,8 @@ import os
 __all__ = [
     "KdaError", "library_path", "load",
     "kda_chunk_fwd", "kda_chunk_fwd_f32", "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_f32",
+    "kda_chunk_fwd_segmented", "kda_chunk_fwd_segmented_f32", "kda_chunk_fwd_varlen_segmented",
+    "kda_chunk_fwd_varlen_segmented_f32", "kda_chunk_segmented_workspace_bytes", "kda_chunk_auto_segments",
     "kda_recurrent_step", "kda_recurrent_step_f32", "kda_check_cu_seqlens_host",
     "kda_status_string", "kda_last_error", "kda_version",
     "chunk_fwd", "chunk_fwd_varlen", "recurrent_step",
@@ -62,12 +64,22 @@ def load():
     chunk = [P] * 8 + [I] * 6 + [P]
     varlen = [P] * 9 + [I] * 6 + [P]
     step = [P] * 7 + [I] * 4 + [P]
+    Z = ctypes.c_size_t
+    chunk_seg = [P] * 8 + [I] * 7 + [P, Z, P]
+    varlen_seg = [P] * 9 + [I] * 7 + [P, Z, P]
     for name, args in (("kda_chunk_fwd", chunk), ("kda_chunk_fwd_f32", chunk),
                        ("kda_chunk_fwd_varlen", varlen), ("kda_chunk_fwd_varlen_f32", varlen),
+                       ("kda_chunk_fwd_segmented", chunk_seg), ("kda_chunk_fwd_segmented_f32", chunk_seg),
+                       ("kda_chunk_fwd_varlen_segmented", varlen_seg),
+                       ("kda_chunk_fwd_varlen_segmented_f32", varlen_seg),
                        ("kda_recurrent_step", step), ("kda_recurrent_step_f32", step)):
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = I
+    lib.kda_chunk_segmented_workspace_bytes.argtypes = [I] * 5
+    lib.kda_chunk_segmented_workspace_bytes.restype = Z
+    lib.kda_chunk_auto_segments.argtypes = [I] * 7
+    lib.kda_chunk_auto_segments.restype = I
     lib.kda_check_cu_seqlens_host.argtypes = [P, I, I]
     lib.kda_check_cu_seqlens_host.restype = I
     lib.kda_status_string.argtypes = [I]
@@ -130,6 +142,42 @@ def kda_chunk_fwd_varlen_f32(q, k, v, log_alpha, beta, S0, out, S_final, cu_seql
         _ptr(cu_seqlens), N, T_total, H, dk, dv, C, _stream(stream)))
 
 
+def kda_chunk_fwd_segmented(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, dk, dv, C, nseg, workspace,
+                            workspace_bytes, stream=None):
+    _check("kda_chunk_fwd_segmented", load().kda_chunk_fwd_segmented(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_final),
+        B, T, H, dk, dv, C, nseg, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def kda_chunk_fwd_segmented_f32(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, dk, dv, C, nseg,
+                                workspace, workspace_bytes, stream=None):
+    _check("kda_chunk_fwd_segmented_f32", load().kda_chunk_fwd_segmented_f32(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_final),
+        B, T, H, dk, dv, C, nseg, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def kda_chunk_fwd_varlen_segmented(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N, T_total, H, dk,
+                                   dv, C, nseg, workspace, workspace_bytes, stream=None):
+    _check("kda_chunk_fwd_varlen_segmented", load().kda_chunk_fwd_varlen_segmented(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_final),
+        _ptr(cu_seqlens), N, T_total, H, dk, dv, C, nseg, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def kda_chunk_fwd_varlen_segmented_f32(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N, T_total, H,
+                                       dk, dv, C, nseg, workspace, workspace_bytes, stream=None):
+    _check("kda_chunk_fwd_varlen_segmented_f32", load().kda_chunk_fwd_varlen_segmented_f32(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_final),
+        _ptr(cu_seqlens), N, T_total, H, dk, dv, C, nseg, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def kda_chunk_segmented_workspace_bytes(nseq, H, dk, dv, nseg) -> int:
+    return load().kda_chunk_segmented_workspace_bytes(nseq, H, dk, dv, nseg)
+
+
+def kda_chunk_auto_segments(B, T, H, dk, dv, C, fp32_inputs) -> int:
+    return load().kda_chunk_auto_segments(B, T, H, dk, dv, C, 1 if fp32_inputs else 0)
+
+
 def kda_recurrent_step(q, k, v, log_alpha, beta, S, out, N, H, dk, dv, stream=None):
     _check("kda_recurrent_step", load().kda_recurrent_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(out), N, H, dk, dv,
@@ -169,21 +217,41 @@ def _mode(q):
     raise TypeError(f"q, k, v must be bfloat16 or float32, got {q.dtype}")
 
 
-def chunk_fwd(q, k, v, log_alpha, beta, S0=None, C=64, output_final_state=True, stream=None):
-    """Chunk prefill of a dense batch.  Returns ``(out, S_final or None)``."""
+def _workspace(nseq, H, dk, dv, nseg, device):
+    import torch
+    nbytes = kda_chunk_segmented_workspace_bytes(nseq, H, dk, dv, nseg)
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device), nbytes
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, S0=None, C=64, output_final_state=True, stream=None, segments="auto"):
+    """Chunk prefill of a dense batch.  Returns ``(out, S_final or None)``.
+
+    ``segments``: 1 for the single pass, n > 1 for the segment-parallel
+    schedule with n segments per sequence, "auto" for the library's choice.
+    """
     import torch
     f32 = _mode(q)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     sf = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device) if output_final_state else None
-    fn = kda_chunk_fwd_f32 if f32 else kda_chunk_fwd
-    fn(q, k, v, log_alpha, beta, S0, out, sf, B, T, H, dk, dv, C, stream)
+    nseg = kda_chunk_auto_segments(B, T, H, dk, dv, C, f32) if segments == "auto" else int(segments)
+    if nseg == 1:
+        fn = kda_chunk_fwd_f32 if f32 else kda_chunk_fwd
+        fn(q, k, v, log_alpha, beta, S0, out, sf, B, T, H, dk, dv, C, stream)
+    else:
+        ws, nbytes = _workspace(B, H, dk, dv, nseg, q.device)
+        fn = kda_chunk_fwd_segmented_f32 if f32 else kda_chunk_fwd_segmented
+        fn(q, k, v, log_alpha, beta, S0, out, sf, B, T, H, dk, dv, C, nseg, ws, nbytes, stream)
     return out, sf
 
 
-def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, C=64, output_final_state=True, stream=None):
-    """Chunk prefill of N packed sequences ([1, T_total, H, d] tensors, device cu_seqlens [N+1])."""
+def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, C=64, output_final_state=True, stream=None,
+                     segments=1):
+    """Chunk prefill of N packed sequences ([1, T_total, H, d] tensors, device cu_seqlens [N+1]).
+
+    ``segments`` > 1 cuts every sequence into that many segments run in parallel.
+    """
     import torch
     f32 = _mode(q)
     _, T_total, H, dk = q.shape
@@ -191,8 +259,14 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, C=64, output
     N = cu_seqlens.shape[0] - 1
     out = torch.empty((1, T_total, H, dv), dtype=q.dtype, device=q.device)
     sf = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device) if output_final_state else None
-    fn = kda_chunk_fwd_varlen_f32 if f32 else kda_chunk_fwd_varlen
-    fn(q, k, v, log_alpha, beta, S0, out, sf, cu_seqlens, N, T_total, H, dk, dv, C, stream)
+    nseg = int(segments)
+    if nseg == 1:
+        fn = kda_chunk_fwd_varlen_f32 if f32 else kda_chunk_fwd_varlen
+        fn(q, k, v, log_alpha, beta, S0, out, sf, cu_seqlens, N, T_total, H, dk, dv, C, stream)
+    else:
+        ws, nbytes = _workspace(N, H, dk, dv, nseg, q.device)
+        fn = kda_chunk_fwd_varlen_segmented_f32 if f32 else kda_chunk_fwd_varlen_segmented
+        fn(q, k, v, log_alpha, beta, S0, out, sf, cu_seqlens, N, T_total, H, dk, dv, C, nseg, ws, nbytes, stream)
     return out, sf
 
 

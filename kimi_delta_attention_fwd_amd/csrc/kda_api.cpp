@@ -74,20 +74,74 @@ kda_status_t check_aliasing(const Buf &out, const Buf *ins, int nin, const Buf &
     return KDA_OK;
 }
 
-// Value-block width of the chunk kernel: the widest block that still gives
-// every compute unit a workgroup (256 CUs), else the narrowest that fits.
-// KDA_CHUNK_BV overrides the choice for tuning.
-int choose_bv(bool f32, int dk, int dv, int C, long nheads)
+// Value-block width of the chunk kernel: the widest block (at most maxbv) that
+// still gives every compute unit a workgroup (256 CUs), else the narrowest that
+// fits.  `units` counts (sequence, head, segment) triples.  KDA_CHUNK_BV
+// overrides the choice for tuning.
+int choose_bv(bool f32, int dk, int dv, int C, long units, int maxbv = 64)
 {
     if (const char *env = std::getenv("KDA_CHUNK_BV")) {
         const int bv = std::atoi(env);
-        if ((bv == 16 || bv == 32 || bv == 64) && bv <= dv && kda::chunk_fits(f32, dk, bv, C)) return bv;
+        if ((bv == 16 || bv == 32 || bv == 64) && bv <= dv && bv <= maxbv && kda::chunk_fits(f32, dk, bv, C))
+            return bv;
     }
     for (int bv : {64, 32, 16})
-        if (bv <= dv && kda::chunk_fits(f32, dk, bv, C) && nheads * (dv / bv) >= 256) return bv;
+        if (bv <= dv && bv <= maxbv && kda::chunk_fits(f32, dk, bv, C) && units * (dv / bv) >= 256) return bv;
     for (int bv : {16, 32, 64})
-        if (bv <= dv && kda::chunk_fits(f32, dk, bv, C)) return bv;
+        if (bv <= dv && bv <= maxbv && kda::chunk_fits(f32, dk, bv, C)) return bv;
     return 0;
+}
+
+constexpr int kMaxSegments = 1024;
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+// Workspace of the segment-parallel schedule: the segment maps, then the
+// segments' incoming states (fp32).
+uint64_t seg_map_bytes(uint64_t nheads, int dk, int dv, int nseg)
+{
+    return align256(nheads * (uint64_t)(nseg - 1) * (uint64_t)(dv + dk) * (uint64_t)dk * 4u);
+}
+
+uint64_t seg_workspace_bytes(uint64_t nheads, int dk, int dv, int nseg)
+{
+    if (nseg <= 1) return 0;
+    return seg_map_bytes(nheads, dk, dv, nseg) + nheads * (uint64_t)nseg * (uint64_t)dv * (uint64_t)dk * 4u;
+}
+
+// Segment count for a dense batch from a model of the run time in chunk steps:
+// a pass of g workgroups that each walk L chunks takes ceil(g / CUs) L steps
+// (one workgroup per compute unit), the map pass about 0.85 of a step per chunk
+// (no q, no outputs), the composition a fraction of a step per segment, and
+// the two extra launches a few steps.
+int auto_segments(bool f32, int B, int T, int H, int dk, int dv, int C)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || !supported_d(dk) || !supported_d(dv) || !supported_c(C)) return 1;
+    int cus = 256;
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int m = 0;
+        if (hipDeviceGetAttribute(&m, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && m > 0) cus = m;
+    }
+    const long nch = (T + C - 1) / C, nheads = (long)B * H;
+    double best = 0.0;
+    int best_s = 1;
+    for (int s = 1; s <= 64 && s <= nch; ++s) {
+        const int bv = choose_bv(f32, dk, dv, C, nheads * s, s > 1 ? dk : 64);
+        if (bv == 0) continue;
+        const long L = (nch + s - 1) / s;
+        const long g3 = nheads * s * (dv / bv);
+        double cost = (double)((g3 + cus - 1) / cus) * (double)L;
+        if (s > 1) {
+            const long g1 = nheads * (s - 1) * ((dv + dk) / bv);
+            cost += 0.85 * (double)((g1 + cus - 1) / cus) * (double)L + 0.3 * s + 3.0;   // + two more launches
+        }
+        if (s == 1 || cost < best) {
+            best = cost;
+            best_s = s;
+        }
+    }
+    return best_s;
 }
 
 hipError_t dispatch_chunk(bool f32, const kda::ChunkArgs &a)
@@ -107,8 +161,11 @@ hipError_t dispatch_chunk(bool f32, const kda::ChunkArgs &a)
 kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, const void *v,
                           const float *log_alpha, const float *beta, const float *S0, void *out,
                           float *S_final, const int32_t *cu_seqlens, int nseq, int T, int T_total,
-                          int H, int dk, int dv, int C, void *stream)
+                          int H, int dk, int dv, int C, void *stream, int nseg = 1, void *workspace = nullptr,
+                          uint64_t workspace_bytes = 0)
 {
+    if (nseg < 1 || nseg > kMaxSegments)
+        return fail(KDA_ERR_BAD_SHAPE, "segment count must be in [1, %d] (got %d)", kMaxSegments, nseg);
     if (nseq < 0 || T < 0 || T_total < 0)
         return fail(KDA_ERR_BAD_SHAPE, "negative size (sequences %d, T %d, T_total %d)", nseq, T, T_total);
     if (H < 1) return fail(KDA_ERR_BAD_SHAPE, "H must be >= 1 (got %d)", H);
@@ -121,7 +178,8 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
     // the kernels address the token rows of one chunk with 32-bit byte offsets
     // (64 rows of H * d elements of up to 4 bytes)
     if (ntok * (uint64_t)H * 128u > (uint64_t)1 << 60 || nheads * 8u > (uint64_t)INT32_MAX ||
-        (uint64_t)H * 128u * 64u * 4u > (uint64_t)INT32_MAX)
+        (uint64_t)H * 128u * 64u * 4u > (uint64_t)INT32_MAX ||
+        nheads * (uint64_t)nseg * (uint64_t)(dv + dk) / 16u > (uint64_t)INT32_MAX)
         return fail(KDA_ERR_BAD_SHAPE, "problem too large");
     const uint64_t es = f32 ? 4 : 2;
     const uint64_t nk = ntok * H * dk, nv = ntok * H * dv, nb = ntok * H, ns = nheads * dv * dk;
@@ -143,12 +201,26 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
                                      Buf{S_final, S_final ? ns * 4 : 0, "S_final"},
                                      Buf{S0, S0 ? ns * 4 : 0, "S0"});
     if (st != KDA_OK) return st;
+    const uint64_t wsb = seg_workspace_bytes(nheads, dk, dv, nseg);
+    if (nseg > 1) {
+        if (!workspace) return fail(KDA_ERR_NULL_POINTER, "the segmented schedule needs a workspace");
+        if (!aligned(workspace, 256)) return fail(KDA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+        if (workspace_bytes < wsb)
+            return fail(KDA_ERR_BAD_SHAPE, "workspace holds %llu bytes, %llu needed",
+                        (unsigned long long)workspace_bytes, (unsigned long long)wsb);
+        const Buf all[] = {ins[0], ins[1], ins[2], ins[3], ins[4], ins[5], Buf{out, nv * es, "out"},
+                           Buf{S_final, S_final ? ns * 4 : 0, "S_final"}, Buf{S0, S0 ? ns * 4 : 0, "S0"}};
+        for (const Buf &b : all)
+            if (overlap(workspace, wsb, b.p, b.bytes))
+                return fail(KDA_ERR_ALIASING, "workspace overlaps %s", b.name);
+    }
 
-    const int BV = choose_bv(f32, dk, dv, C, (long)nheads);
+    const int BV = choose_bv(f32, dk, dv, C, (long)(nheads * nseg), nseg > 1 ? dk : 64);
     if (BV == 0)
         return fail(KDA_ERR_UNSUPPORTED, "no %s kernel fits LDS for dk=%d, dv=%d, C=%d",
                     f32 ? "fp32" : "bf16", dk, dv, C);
     if (nheads == 0 || (ntok == 0 && !S_final)) return ok();
+    if (ntok == 0) nseg = 1;   // nothing to split: S0 (or zeros) is copied to S_final
 
     kda::ChunkArgs a;
     a.q = q;
@@ -167,6 +239,9 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
     a.dv = dv;
     a.C = C;
     a.BV = BV;
+    a.nsegs = nseg;
+    a.seg_map = nseg > 1 ? (float *)workspace : nullptr;
+    a.seg_start = nseg > 1 ? (float *)((char *)workspace + seg_map_bytes(nheads, dk, dv, nseg)) : nullptr;
     a.stream = (hipStream_t)stream;
     const hipError_t e = dispatch_chunk(f32, a);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "chunk kernel launch failed: %s", hipGetErrorString(e));
@@ -250,6 +325,56 @@ kda_status_t kda_chunk_fwd_varlen_f32(const float *q, const float *k, const floa
 {
     return chunk_common(true, true, q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N, 0, T_total,
                         H, dk, dv, C, stream);
+}
+
+kda_status_t kda_chunk_fwd_segmented(const void *q, const void *k, const void *v, const float *log_alpha,
+                                     const float *beta, const float *S0, void *out, float *S_final, int B,
+                                     int T, int H, int dk, int dv, int C, int nseg, void *workspace,
+                                     size_t workspace_bytes, void *stream)
+{
+    return chunk_common(false, false, q, k, v, log_alpha, beta, S0, out, S_final, nullptr, B, T, 0, H, dk,
+                        dv, C, stream, nseg, workspace, workspace_bytes);
+}
+
+kda_status_t kda_chunk_fwd_segmented_f32(const float *q, const float *k, const float *v,
+                                         const float *log_alpha, const float *beta, const float *S0,
+                                         float *out, float *S_final, int B, int T, int H, int dk, int dv,
+                                         int C, int nseg, void *workspace, size_t workspace_bytes,
+                                         void *stream)
+{
+    return chunk_common(true, false, q, k, v, log_alpha, beta, S0, out, S_final, nullptr, B, T, 0, H, dk,
+                        dv, C, stream, nseg, workspace, workspace_bytes);
+}
+
+kda_status_t kda_chunk_fwd_varlen_segmented(const void *q, const void *k, const void *v,
+                                            const float *log_alpha, const float *beta, const float *S0,
+                                            void *out, float *S_final, const int32_t *cu_seqlens, int N,
+                                            int T_total, int H, int dk, int dv, int C, int nseg,
+                                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    return chunk_common(false, true, q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N, 0, T_total,
+                        H, dk, dv, C, stream, nseg, workspace, workspace_bytes);
+}
+
+kda_status_t kda_chunk_fwd_varlen_segmented_f32(const float *q, const float *k, const float *v,
+                                                const float *log_alpha, const float *beta, const float *S0,
+                                                float *out, float *S_final, const int32_t *cu_seqlens, int N,
+                                                int T_total, int H, int dk, int dv, int C, int nseg,
+                                                void *workspace, size_t workspace_bytes, void *stream)
+{
+    return chunk_common(true, true, q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N, 0, T_total,
+                        H, dk, dv, C, stream, nseg, workspace, workspace_bytes);
+}
+
+size_t kda_chunk_segmented_workspace_bytes(int nseq, int H, int dk, int dv, int nseg)
+{
+    if (nseq <= 0 || H <= 0 || !supported_d(dk) || !supported_d(dv) || nseg < 1 || nseg > kMaxSegments) return 0;
+    return (size_t)seg_workspace_bytes((uint64_t)nseq * (uint64_t)H, dk, dv, nseg);
+}
+
+int kda_chunk_auto_segments(int B, int T, int H, int dk, int dv, int C, int fp32_inputs)
+{
+    return auto_segments(fp32_inputs != 0, B, T, H, dk, dv, C);
 }
 
 kda_status_t kda_recurrent_step(const void *q, const void *k, const void *v, const float *log_alpha,

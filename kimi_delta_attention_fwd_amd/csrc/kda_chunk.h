@@ -284,12 +284,22 @@ struct ChunkCfg {
     static_assert((NSEG & (NSEG - 1)) == 0, "segment scan over a power of two");
 };
 
-template <typename In, int DK, int BV, int C>
+// MAP = false: the prefill itself.  With nsegs > 1 each workgroup runs one of
+// nsegs consecutive segments of its sequence's chunks, from the incoming state
+// seg_start[(head, seg)] (segment 0 included, which holds S0); only the last
+// segment writes S_final.
+// MAP = true: the affine map of each segment but the last.  The state is
+// augmented with DK "virtual" rows that start at the identity and see v = 0;
+// the dv real rows start at zero.  After the segment the real rows hold N and
+// the virtual rows M of S_end = S_start M + N, written to seg_map[(head, seg)];
+// no output is written and q is not read.
+template <typename In, int DK, int BV, int C, bool MAP>
 __global__ void __launch_bounds__((ChunkCfg<In, DK, BV, C>::NT), 1)
 chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
                  const float *__restrict__ log_alpha, const float *__restrict__ beta,
                  const float *S0, In *__restrict__ out, float *S_final,
-                 const int *__restrict__ cu_seqlens, int T, int H, int dv, int xcd_map)
+                 const int *__restrict__ cu_seqlens, int T, int H, int dv, int xcd_map,
+                 int nsegs, const float *seg_start, float *seg_map)
 {
     typedef ChunkCfg<In, DK, BV, C> K;
     typedef typename V4T<In>::type V4;
@@ -308,19 +318,21 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) index
     const int n = lane & 15, g = lane >> 4;
-    const int nvb = dv / BV;
-    int head, vb;
+    const int nsu = MAP ? nsegs - 1 : nsegs;         // segments per sequence in this grid
+    const int nvb = (MAP ? dv + DK : dv) / BV;       // value blocks (of the augmented state)
+    int unit, vb;                                    // unit = (head, segment)
     if (xcd_map) {
         // Workgroups are dealt to the 8 XCDs round-robin; keep all value blocks
-        // of one head on one XCD so their shared q / k / log_alpha reads hit
+        // of one unit on one XCD so their shared q / k / log_alpha reads hit
         // the same L2.
         const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
-        head = (slot / nvb) * 8 + x;
+        unit = (slot / nvb) * 8 + x;
         vb = slot % nvb;
     } else {
-        head = blockIdx.x / nvb;
+        unit = blockIdx.x / nvb;
         vb = blockIdx.x % nvb;
     }
+    const int head = unit / nsu, seg = unit % nsu;
     const int seq = head / H, h = head % H;
     long tok0, len;
     if (cu_seqlens) {
@@ -329,6 +341,13 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     } else {
         tok0 = (long)seq * T;
         len = T;
+    }
+    if (nsegs > 1) {
+        // segment seg: chunks [c0, c1) of the sequence, ceil(nch / nsegs) each
+        const long nch_all = (len + C - 1) / C, L = (nch_all + nsegs - 1) / nsegs;
+        const long c0 = min((long)seg * L, nch_all), c1 = min(c0 + L, nch_all);
+        tok0 += c0 * C;
+        len = max(0L, min(len - c0 * C, (c1 - c0) * C));
     }
     const long nch = (len + C - 1) / C;
     const int HDK = H * DK, HDV = H * dv;
@@ -425,6 +444,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             for (int i = 0; i < RS; ++i) gr[i] = buf_load<f32x4>(rg, voff_f, i * rowb_f);
         };
         auto prefetch_q = [&](long t0) __attribute__((always_inline)) {
+            if constexpr (MAP) return;
             const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + (hrow + t0 * H) * DK, chunk_valid(t0) * rowb_in);
 #pragma unroll
             for (int i = 0; i < RS; ++i) qr[i] = buf_load<In4>(rq, voff_in, i * rowb_in);
@@ -499,12 +519,12 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                         pp[j] *= al[i][j];
                         const float kf = tof(kr[i][j]);
                         vkr[j] = kf * pp[j];                       // k e^{G - ref}
-                        vqr[j] = tof(qr[i][j]) * pp[j];            // q e^{G - ref}
+                        if constexpr (!MAP) vqr[j] = tof(qr[i][j]) * pp[j];   // q e^{G - ref}
                     }
                     if (act) {
                         const int r = r0 + i;
                         store4(Kr + r * PK + c0, vkr);
-                        store4(Qr + r * PK + c0, vqr);
+                        if constexpr (!MAP) store4(Qr + r * PK + c0, vqr);
                         if (!lane_fast) {
 #pragma unroll
                             for (int j = 0; j < 4; ++j) vkd[j] = tof(kr[i][j]) * __builtin_amdgcn_rcpf(pp[j]);   // k e^{ref - G}
@@ -550,8 +570,14 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 for (int j = 0; j < 4; ++j) {
                     sc[K::SC_GL + c0 + j] = fexp(glast[j]);
                     if (wave_fast) {   // every reference is the chunk start: all factors are 1
+                        // (w too: other waves may take block references, and then
+                        // the tiles read w for every channel)
 #pragma unroll
-                        for (int I = 0; I < NB; ++I) sc[I * DK + c0 + j] = 1.f;
+                        for (int I = 0; I < NB; ++I) {
+                            sc[I * DK + c0 + j] = 1.f;
+#pragma unroll
+                            for (int J = 0; J < I; ++J) sW[(I * (I - 1) / 2 + J) * DK + c0 + j] = 1.f;
+                        }
                     } else {
 #pragma unroll
                         for (int I = 0; I < NB; ++I) {
@@ -582,7 +608,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                     // they cancel, about 1e-4 relative at worst: fine for the bf16
                     // kernels, the fp32 ones use the substitution below.)
                     f32x4 lt[2];
-                    tile_job(ch, p, true, K::NBV == 1, lt);
+                    tile_job(ch, p, true, K::NBV == 1 && !MAP, lt);
                     auto mm = [](f32x4 x, f32x4 y) {   // acc(X^T Y)
                         const f32x4 a[1] = {x}, b[1] = {y};
                         return mma_tiles<4, float, 1>(zero4(), a, b);
@@ -602,7 +628,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                     // fp32 kernels: column n of D_p by forward substitution over the
                     // rows of the stored tile (lanes of the other 16-lane rows repeat
                     // the work and store nothing)
-                    tile_job(ch, p, true, K::NBV == 1);
+                    tile_job(ch, p, true, K::NBV == 1 && !MAP);
                     float *At = sA + p * 16 * PT;
                     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
                     float x[16];
@@ -652,7 +678,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     } else {
         // =============== state waves: value rows 16 cb .. 16 cb + 15 of the block
         const int cb = wave;
-        const long vrow = (long)head * dv + vb * BV + 16 * cb;   // first state row of this wave
+        const int row = vb * BV + 16 * cb + n;     // this lane's state row (of the augmented state in MAP mode)
+        const bool vreal = !MAP || vb * BV < dv;   // real value rows (virtual ones see v = 0)
         // bf16: lane (n, g) loads row 16 (2 u + g/2) + n, columns 8 (g&1) .. +7;
         // fp32: row 16 u + n, columns 4g .. 4g+3 (u = load index)
         const int rowb_v = HDV * (int)sizeof(In);
@@ -661,10 +688,30 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         const long vcol = hrow * dv + vb * BV + 16 * cb;
 
         // State, transposed, in accumulator layout: Sacc[ct][i] = S[16 cb + n][16 ct + 4g + i].
+        // Where it comes from and goes to: S0 / S_final for a whole sequence;
+        // the segment's incoming state / S_final (last segment only) for a
+        // segment; zero or the identity / the segment's map in MAP mode.
         f32x4 Sacc[NDK];
+        const float *s0row = nullptr;
+        float *sfrow = nullptr;
+        if constexpr (MAP) {
+            sfrow = seg_map + (((long)head * (nsegs - 1) + seg) * (dv + DK) + row) * DK;
+        } else if (nsegs > 1) {
+            s0row = seg_start + (((long)head * nsegs + seg) * dv + row) * DK;
+            if (seg == nsegs - 1 && S_final) sfrow = S_final + ((long)head * dv + row) * DK;
+        } else {
+            if (S0) s0row = S0 + ((long)head * dv + row) * DK;
+            if (S_final) sfrow = S_final + ((long)head * dv + row) * DK;
+        }
 #pragma unroll
-        for (int ct = 0; ct < NDK; ++ct)
-            Sacc[ct] = S0 ? *(const f32x4 *)(S0 + (vrow + n) * DK + 16 * ct + 4 * g) : zero4();
+        for (int ct = 0; ct < NDK; ++ct) {
+            if constexpr (MAP) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Sacc[ct][i] = (row - dv == 16 * ct + 4 * g + i) ? 1.f : 0.f;
+            } else {
+                Sacc[ct] = s0row ? *(const f32x4 *)(s0row + 16 * ct + 4 * g) : zero4();
+            }
+        }
 
         // V of the chunk, prefetched a chunk ahead; an MFMA against an identity
         // fragment moves it into accumulator layout.
@@ -672,8 +719,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         typedef In VL __attribute__((ext_vector_type(K::F32 ? 4 : 8)));
         VL vr[NVL];
         auto prefetch_v = [&](long t0) __attribute__((always_inline)) {
-            const unsigned nv = (unsigned)((len - t0 < C) ? len - t0 : C);
-            const __amdgpu_buffer_rsrc_t rv = buf_rsrc(v + vcol + t0 * HDV, nv * rowb_v);
+            const unsigned nv = vreal ? (unsigned)((len - t0 < C) ? len - t0 : C) : 0u;
+            const __amdgpu_buffer_rsrc_t rv = buf_rsrc(v + (vreal ? vcol + t0 * HDV : 0), nv * rowb_v);
 #pragma unroll
             for (int u = 0; u < NVL; ++u) vr[u] = buf_load<VL>(rv, voff_v, (K::F32 ? 16 : 32) * u * rowb_v);
         };
@@ -690,9 +737,10 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         }
         // Tiles the state waves form for a chunk, in their second segment: with
         // two or more state waves the off-diagonal pairs (A and P) and then the
-        // diagonal P tiles, else the off-diagonal P tiles.  Jobs are dealt in
-        // snake order so the heavier pairs spread evenly over the waves.
-        constexpr int NJOB = K::NBV >= 2 ? K::NPAIR : K::NOFF;
+        // diagonal P tiles, else the off-diagonal P tiles (MAP mode: no P tiles).
+        // Jobs are dealt in snake order so the heavier pairs spread evenly over
+        // the waves.
+        constexpr int NJOB = MAP ? (K::NBV >= 2 ? K::NOFF : 0) : (K::NBV >= 2 ? K::NPAIR : K::NOFF);
         constexpr int NROUND = (NJOB + K::NBV - 1) / K::NBV;
         auto y_tiles = [&](long ch) __attribute__((always_inline)) {
 #pragma unroll
@@ -700,7 +748,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 const int s = r * K::NBV + ((r & 1) ? K::NBV - 1 - cb : cb);
                 if (s < NJOB) {
                     const int p = s < K::NOFF ? NB + s : s - K::NOFF;
-                    tile_job(ch, p, K::NBV >= 2 && p >= NB, true);
+                    tile_job(ch, p, K::NBV >= 2 && p >= NB, !MAP);
                 }
             }
         };
@@ -725,10 +773,10 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 #pragma unroll
                 for (int ct = 0; ct < NDK; ++ct) {
                     ak[ct] = *(const V4 *)(Kr + (16 * I + n) * PK + 16 * ct + 4 * g);
-                    bq[ct] = *(const V4 *)(Qr + (16 * I + n) * PK + 16 * ct + 4 * g);
+                    if constexpr (!MAP) bq[ct] = *(const V4 *)(Qr + (16 * I + n) * PK + 16 * ct + 4 * g);
                 }
                 R[I] = mma_tiles<K::KD, In, NDK>(zero4(), ak, ss);    // [16I + 4g + i][n]
-                O1[I] = mma_tiles<K::KD, In, NDK>(zero4(), ss, bq);   // [v = 4g + i][16I + n]
+                if constexpr (!MAP) O1[I] = mma_tiles<K::KD, In, NDK>(zero4(), ss, bq);   // [v = 4g + i][16I + n]
             };
             if (allfast) {
 #pragma unroll
@@ -778,7 +826,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             // ---- O^T = (Qbar S^T)^T + E^T P^T, written as O rows (rows past the end dropped)
             const __amdgpu_buffer_rsrc_t ro = buf_rsrc(out + vcol + t0 * HDV, (unsigned)nval * rowb_v);
 #pragma unroll
-            for (int I = 0; I < NB; ++I) {
+            for (int I = 0; I < (MAP ? 0 : NB); ++I) {
                 V4 pb[NB];
 #pragma unroll
                 for (int J = 0; J < NB; ++J)
@@ -803,13 +851,71 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             if (ch + 1 < nch) y_tiles(ch + 1);
             __syncthreads();
         }
-        if (S_final) {
+        if (sfrow) {
 #pragma unroll
-            for (int ct = 0; ct < NDK; ++ct) *(f32x4 *)(S_final + (vrow + n) * DK + 16 * ct + 4 * g) = Sacc[ct];
+            for (int ct = 0; ct < NDK; ++ct) *(f32x4 *)(sfrow + 16 * ct + 4 * g) = Sacc[ct];
         }
     }
 }
 
+// Incoming states of the segments of every (sequence, head): slot 0 holds S0
+// (zero when absent), slot p + 1 = slot p M_p + N_p, row by row, with (M_p,
+// N_p) the map of segment p from the MAP pass.  One workgroup per 16 state rows
+// of a head; thread (r, cg) keeps columns cg DK/16 .. of row r, and the
+// current rows sit in LDS for the products.  fp32 throughout.
+template <int DK>
+__global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const float *seg_map,
+                                                          float *seg_start, int dv, int nsegs)
+{
+    constexpr int CPT = DK / 16;
+    __shared__ float srow[16][DK + 1];
+    const int nrb = dv / 16;
+    const int head = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+    const int r = threadIdx.x >> 4, c0 = (threadIdx.x & 15) * CPT;
+    const int row = rb * 16 + r;
+    float acc[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) acc[j] = S0 ? S0[((long)head * dv + row) * DK + c0 + j] : 0.f;
+    for (int p = 0;; ++p) {
+        float *dst = seg_start + (((long)head * nsegs + p) * dv + row) * DK + c0;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) dst[j] = acc[j];
+        if (p + 1 >= nsegs) break;
+        __syncthreads();   // the previous step's reads of srow are done
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) srow[r][c0 + j] = acc[j];
+        __syncthreads();
+        const float *mp = seg_map + ((long)head * (nsegs - 1) + p) * (dv + DK) * DK;
+        const float *M = mp + (long)dv * DK;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) acc[j] = mp[(long)row * DK + c0 + j];   // N_p
+        for (int i = 0; i < DK; ++i) {
+            const float si = srow[r][i];
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) acc[j] = fmaf(si, M[i * DK + c0 + j], acc[j]);
+        }
+    }
+}
+
+// One pass of the chunk kernel over nsu segments per sequence and nrows state
+// rows per head.
+template <typename In, int DK, int BV, int C, bool MAP>
+hipError_t launch_chunk_pass(const ChunkArgs &a, int nsu, int nrows)
+{
+    typedef ChunkCfg<In, DK, BV, C> K;
+    const long units = (long)a.nseq * a.H * nsu;
+    const long grid = units * (nrows / BV);
+    if (grid == 0) return hipSuccess;
+    const int xcd_map = (units % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((chunk_fwd_kernel<In, DK, BV, C, MAP>), dim3((unsigned)grid), dim3(K::NT), 0, a.stream,
+                       (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S0,
+                       (In *)a.out, a.S_final, a.cu_seqlens, a.T, a.H, a.dv, xcd_map, a.nsegs, a.seg_start,
+                       a.seg_map);
+    return hipGetLastError();
+}
+
+// The whole prefill: one pass, or (nsegs > 1) the map pass over all segments
+// but the last, the composition of the maps, and the pass over all segments.
 template <typename In, int DK, int BV, int C>
 hipError_t launch_chunk_t(const ChunkArgs &a)
 {
@@ -817,15 +923,21 @@ hipError_t launch_chunk_t(const ChunkArgs &a)
     if constexpr (!K::fits) {
         return hipErrorInvalidConfiguration;
     } else {
-        const int nheads = a.nseq * a.H;
-        const int nvb = a.dv / BV;
-        const int grid = nheads * nvb;
-        if (grid == 0) return hipSuccess;
-        const int xcd_map = (nheads % 8 == 0) ? 1 : 0;
-        hipLaunchKernelGGL((chunk_fwd_kernel<In, DK, BV, C>), dim3(grid), dim3(K::NT), 0, a.stream,
-                           (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S0,
-                           (In *)a.out, a.S_final, a.cu_seqlens, a.T, a.H, a.dv, xcd_map);
-        return hipGetLastError();
+        if (a.nsegs <= 1) return launch_chunk_pass<In, DK, BV, C, false>(a, 1, a.dv);
+        if constexpr (DK % BV != 0) {
+            return hipErrorInvalidConfiguration;   // the virtual rows fill whole value blocks
+        } else {
+            hipError_t e = launch_chunk_pass<In, DK, BV, C, true>(a, a.nsegs - 1, a.dv + DK);
+            if (e != hipSuccess) return e;
+            const long ncomp = (long)a.nseq * a.H * (a.dv / 16);
+            if (ncomp > 0) {
+                hipLaunchKernelGGL((seg_compose_kernel<DK>), dim3((unsigned)ncomp), dim3(256), 0, a.stream, a.S0,
+                                   (const float *)a.seg_map, a.seg_start, a.dv, a.nsegs);
+                e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            }
+            return launch_chunk_pass<In, DK, BV, C, false>(a, a.nsegs, a.dv);
+        }
     }
 }
 

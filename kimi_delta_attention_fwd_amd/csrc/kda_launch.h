@@ -13,6 +13,10 @@ struct ChunkArgs {
     float *S_final;
     const int *cu_seqlens;   // device; NULL for the dense [B, T, H, d] layout
     int nseq, T, H, dk, dv, C, BV;
+    // segment-parallel schedule (nsegs > 1): caller-owned workspace,
+    // seg_map [nseq*H][nsegs-1][dv+dk][dk] and seg_start [nseq*H][nsegs][dv][dk] fp32
+    int nsegs;
+    float *seg_map, *seg_start;
     hipStream_t stream;
 };
 

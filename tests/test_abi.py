@@ -164,3 +164,69 @@ def test_chunk_allows_in_place_state_continuation(lib):
     # the call launch-free on a machine without a GPU.
     S0 = A + 500 * MB
     assert chunk(lib, S0=S0, Sf=S0, B=0) == 0
+
+
+# ---------------------------------------------------------------- segment-parallel schedule
+WS = A + 1024 * MB   # fake workspace address, 256-byte aligned, clear of every other buffer
+
+
+def seg(lib, nseg=4, ws=WS, wsb=None, f32=False, B=1, T=4096, H=2, dk=64, dv=64, C=64, **kw):
+    args = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, la=A + 192 * MB, beta=A + 256 * MB, S0=None,
+                out=A + 320 * MB, Sf=A + 384 * MB)
+    args.update(kw)
+    if wsb is None:
+        wsb = lib.kda_chunk_segmented_workspace_bytes(B, H, dk, dv, nseg)
+    fn = lib.kda_chunk_fwd_segmented_f32 if f32 else lib.kda_chunk_fwd_segmented
+    return fn(args["q"], args["k"], args["v"], args["la"], args["beta"], args["S0"], args["out"], args["Sf"],
+              B, T, H, dk, dv, C, nseg, ws, wsb, None)
+
+
+def test_segmented_workspace_bytes_formula(lib):
+    f = lib.kda_chunk_segmented_workspace_bytes
+    assert f(1, 16, 128, 128, 1) == 0
+    nh, dk, dv, s = 16, 128, 128, 8
+    maps = nh * (s - 1) * (dv + dk) * dk * 4
+    maps = (maps + 255) // 256 * 256
+    assert f(1, nh, dk, dv, s) == maps + nh * s * dv * dk * 4
+    # B and H enter only through their product
+    assert f(2, 3, 32, 16, 5) == f(6, 1, 32, 16, 5) == f(3, 2, 32, 16, 5)
+    assert f(1, 1, 48, 64, 2) == 0 and f(1, 1, 64, 64, 0) == 0 and f(1, 1, 64, 64, 2000) == 0
+
+
+def test_auto_segments_model(lib):
+    # the mid workload already fills 256 compute units: one pass
+    assert kda.kda_chunk_auto_segments(4, 8192, 32, 128, 128, 64, False) == 1
+    # the long workload (16 heads, 1024 chunks each) is split
+    s = kda.kda_chunk_auto_segments(1, 65536, 16, 128, 128, 64, False)
+    assert 4 <= s <= 64
+    # never more segments than chunks, never below 1
+    assert kda.kda_chunk_auto_segments(1, 100, 1, 64, 64, 64, False) <= 2
+    assert kda.kda_chunk_auto_segments(0, 0, 1, 64, 64, 64, True) == 1
+    assert kda.kda_chunk_auto_segments(1, 64, 1, 48, 64, 64, False) == 1
+
+
+def test_segmented_validation(lib):
+    assert seg(lib, nseg=0) == 2
+    assert seg(lib, nseg=1025) == 2
+    assert seg(lib, ws=None) == 1
+    assert "workspace" in kda.kda_last_error()
+    assert seg(lib, ws=WS + 16) == 4
+    assert seg(lib, wsb=1024) == 2
+    assert "needed" in kda.kda_last_error()
+    assert seg(lib, ws=A + 320 * MB) == 6                  # workspace on top of out
+    assert "workspace overlaps out" in kda.kda_last_error()
+    assert seg(lib, ws=A) == 6                             # workspace on top of q
+    # one segment needs no workspace; the usual checks still apply
+    assert seg(lib, nseg=1, ws=None, B=0) == 0
+    assert seg(lib, nseg=1, q=A + 2) == 4
+    assert seg(lib, f32=True, dk=128, dv=128, C=64) == 3
+
+
+def test_segmented_varlen_validation(lib):
+    fn = lib.kda_chunk_fwd_varlen_segmented
+    wsb = lib.kda_chunk_segmented_workspace_bytes(3, 4, 64, 64, 3)
+    args = [A, A + 64 * MB, A + 128 * MB, A + 192 * MB, A + 256 * MB, None, A + 320 * MB, A + 384 * MB,
+            A + 448 * MB, 3, 100, 4, 64, 64, 64]
+    assert fn(*args, 3, None, wsb, None) == 1
+    assert fn(*args, 3, WS, wsb - 4, None) == 2
+    assert fn(*args, -1, WS, wsb, None) == 2

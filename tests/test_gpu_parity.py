@@ -47,8 +47,9 @@ def dev():
     return torch.device("cuda:0")
 
 
-def gpu_chunk(p, C, final=True):
-    out, sf = kda.chunk_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S0=p.S0, C=C, output_final_state=final)
+def gpu_chunk(p, C, final=True, segments=1):
+    out, sf = kda.chunk_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S0=p.S0, C=C, output_final_state=final,
+                            segments=segments)
     torch.cuda.synchronize()
     return out, sf
 
@@ -203,6 +204,23 @@ def test_chunk_mixes_fast_and_sub_block_paths(dev):
         assert_close(f"mixed paths {dtype}", f64(out), f64(sf), o_ref, s_ref, tol)
 
 
+@pytest.mark.parametrize("dtype,dk,C", [("bf16", 64, 64), ("f32", 64, 32), ("bf16", 32, 32), ("bf16", 16, 64),
+                                        ("bf16", 128, 64)])
+def test_chunk_some_operand_waves_on_block_references(dev, dtype, dk, C):
+    """Strong decay in the key channels of the first operand wave only (a
+    quarter of them): in those chunks the other operand waves keep chunk-start
+    references (w = 1) while one wave takes block references."""
+    q4 = dk // 4
+    note(f"case partial block references: B1 T600 H2 dk{dk} dv64 {dtype} C{C}, channels 0..{q4 - 1} of head 1 "
+         "at -4.5")
+    p = kda_synth.prefill(1, 600, 2, dk, 64, dtype=dtype, s0_sigma=0.1, seed=41, device=dev)
+    p.log_alpha[:, 70:100] = -3.5
+    p.log_alpha[:, 400:430, 1, :q4] = -4.5
+    out, sf = gpu_chunk(p, C)
+    o_ref, s_ref = oracle_dense(p)
+    assert_close(f"partial block references {dtype}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+
+
 def test_chunk_guard_bands_untouched(dev):
     """Outputs written through interior pointers of larger buffers: the bands
     around out and S_final keep their sentinel values (no out-of-bounds stores)."""
@@ -231,6 +249,89 @@ def test_chunk_is_deterministic(dev):
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
+# ---------------------------------------------------------------- segment-parallel schedule
+SEG_SHAPES = [
+    # B, T, H, dk, dv, C, dtype, segments, with_s0
+    (1, 1000, 2, 64, 64, 64, "bf16", 2, True),
+    (1, 1000, 2, 64, 64, 64, "bf16", 3, False),
+    (2, 700, 2, 128, 128, 64, "bf16", 5, True),    # 11 chunks: segments of 3, 3, 3, 2 and 0 chunks
+    (1, 1000, 1, 64, 64, 64, "bf16", 23, True),    # more segments than chunks: empty segments
+    (1, 333, 2, 32, 64, 32, "f32", 4, True),
+    (1, 300, 3, 128, 16, 64, "bf16", 3, True),     # dv < dk
+    (1, 300, 2, 16, 128, 32, "bf16", 3, True),     # dk < dv: 16-row value blocks
+    (2, 260, 2, 64, 32, 16, "f32", 6, True),
+    (1, 520, 8, 128, 128, 64, "bf16", 4, True),    # 8 heads: XCD-aware workgroup mapping
+]
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,C,dtype,nseg,with_s0", SEG_SHAPES)
+def test_segmented_matches_oracle(dev, B, T, H, dk, dv, C, dtype, nseg, with_s0):
+    """The segment-parallel schedule (map pass, composition, rerun) against the
+    oracle, and against the single pass on the same inputs."""
+    note(f"case segmented B{B} T{T} H{H} dk{dk} dv{dv} C{C} {dtype} segments={nseg} S0={with_s0}")
+    p = kda_synth.prefill(B, T, H, dk, dv, dtype=dtype, s0_sigma=0.1 if with_s0 else None,
+                          seed=2000 + T + dk + dv + nseg, device=dev)
+    out, sf = gpu_chunk(p, C, segments=nseg)
+    o_ref, s_ref = oracle_dense(p)
+    assert_close("segmented", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+    o1, s1 = gpu_chunk(p, C, segments=1)
+    assert_close("segmented vs single pass", f64(out), f64(sf), f64(o1), f64(s1), TOL[dtype])
+
+
+def test_segmented_strong_and_mixed_decay(dev):
+    """Segments that take the sub-block decay path, and a decay strong enough
+    that the segment maps are nearly zero."""
+    for dtype, tol, C in (("bf16", TOL["bf16"], 64), ("f32", TOL["f32"], 32)):
+        note(f"case segmented mixed paths: B1 T600 H2 d64 {dtype}, 4 segments")
+        p = kda_synth.prefill(1, 600, 2, 64, 64, dtype=dtype, s0_sigma=0.1, seed=41, device=dev)
+        p.log_alpha[:, 70:100] = -3.5
+        p.log_alpha[:, 400:430, 1, :32] = -4.5
+        out, sf = gpu_chunk(p, C, segments=4)
+        o_ref, s_ref = oracle_dense(p)
+        assert_close(f"segmented mixed {dtype}", f64(out), f64(sf), o_ref, s_ref, tol)
+
+
+def test_segmented_in_place_and_no_final_state(dev):
+    note("case segmented in place: S_final == S0, and S_final not requested")
+    B, T, H, dk, dv, C, nseg = 1, 800, 2, 128, 128, 64, 3
+    p = kda_synth.prefill(B, T, H, dk, dv, dtype="bf16", s0_sigma=0.1, seed=43, device=dev)
+    o_ref, s_ref = oracle_dense(p)
+    nbytes = kda.kda_chunk_segmented_workspace_bytes(B, H, dk, dv, nseg)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    S = p.S0.clone()
+    out = torch.empty_like(p.v)
+    kda.kda_chunk_fwd_segmented(p.q, p.k, p.v, p.log_alpha, p.beta, S, out, S, B, T, H, dk, dv, C, nseg, ws,
+                                nbytes)
+    torch.cuda.synchronize()
+    assert_close("segmented in-place", f64(out), f64(S), o_ref, s_ref, TOL["bf16"])
+    out2 = torch.empty_like(p.v)
+    kda.kda_chunk_fwd_segmented(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out2, None, B, T, H, dk, dv, C, nseg,
+                                ws, nbytes)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out)
+
+
+def test_segmented_varlen(dev):
+    lengths = [300, 64, 1, 0, 517, 129]
+    for dtype in ("bf16", "f32"):
+        note(f"case segmented varlen lengths {lengths} H2 d64 {dtype} C32, 3 segments per sequence")
+        p = kda_synth.prefill_varlen(lengths, 2, 64, 64, dtype=dtype, s0_sigma=0.1, seed=45, device=dev)
+        out, sf = kda.chunk_fwd_varlen(p.q, p.k, p.v, p.log_alpha, p.beta, p.cu_seqlens, S0=p.S0, C=32,
+                                       segments=3)
+        torch.cuda.synchronize()
+        o_ref, s_ref = oracle.forward_varlen(f64(p.q), f64(p.k), f64(p.v), f64(p.log_alpha), f64(p.beta),
+                                             np.array(p.cu_host), S0=f64(p.S0))
+        assert_close(f"segmented varlen {dtype}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+
+
+def test_segmented_is_deterministic(dev):
+    note("case segmented determinism B1 T900 H2 d128 bf16, 4 segments (two runs, bitwise)")
+    p = kda_synth.prefill(1, 900, 2, 128, 128, dtype="bf16", s0_sigma=0.1, seed=47, device=dev)
+    o1, s1 = gpu_chunk(p, 64, segments=4)
+    o2, s2 = gpu_chunk(p, 64, segments=4)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
 # ---------------------------------------------------------------- packed variable length
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_varlen_small(dev, dtype):
@@ -255,7 +356,7 @@ def test_varlen_equals_dense_per_sequence(dev):
         a, b = p.cu_host[n], p.cu_host[n + 1]
         o_n, s_n = kda.chunk_fwd(p.q[:, a:b].contiguous(), p.k[:, a:b].contiguous(), p.v[:, a:b].contiguous(),
                                  p.log_alpha[:, a:b].contiguous(), p.beta[:, a:b].contiguous(),
-                                 S0=p.S0[n:n + 1].contiguous(), C=64)
+                                 S0=p.S0[n:n + 1].contiguous(), C=64, segments=1)
         torch.cuda.synchronize()
         assert torch.equal(out[:, a:b], o_n) and torch.equal(sf[n:n + 1], s_n)
 
@@ -295,16 +396,20 @@ def test_mid_workload_sampled(dev):
 
 
 def test_long_workload_sampled(dev):
+    """Both schedules of the long workload: the segment-parallel one with the
+    library's segment count (what bench.py times) and the single pass."""
     w = kda_synth.WORKLOADS["long"]
-    note("case long workload: B1 H16 T65536 d128 bf16 C64, S0 in (3 sampled heads)")
     p = kda_synth.workload("long", device=dev)
-    out, sf = gpu_chunk(p, w["C"])
-    assert torch.isfinite(out.float()).all() and torch.isfinite(sf).all()
     pairs = [(0, 0), (0, 9), (0, 15)]
     o_ref, s_ref = sampled(p, pairs)
-    o_gpu = np.stack([f64(out[b, :, h]) for b, h in pairs])[:, :, None]
-    s_gpu = np.stack([f64(sf[b, h]) for b, h in pairs])[:, None]
-    assert_close("long sampled", o_gpu, s_gpu, o_ref, s_ref, TOL["bf16"])
+    for segments in ("auto", 1):
+        note(f"case long workload: B1 H16 T65536 d128 bf16 C64, S0 in (3 sampled heads), segments={segments}")
+        out, sf = gpu_chunk(p, w["C"], segments=segments)
+        assert torch.isfinite(out.float()).all() and torch.isfinite(sf).all()
+        o_gpu = np.stack([f64(out[b, :, h]) for b, h in pairs])[:, :, None]
+        s_gpu = np.stack([f64(sf[b, h]) for b, h in pairs])[:, None]
+        assert_close(f"long sampled ({segments})", o_gpu, s_gpu, o_ref, s_ref, TOL["bf16"])
+        del out, sf
 
 
 # ---------------------------------------------------------------- decode step
@@ -359,7 +464,7 @@ def test_decode_equals_chunk_prefill_on_same_stream(dev):
     outs = [kda.recurrent_step(d.q[t], d.k[t], d.v[t], d.log_alpha[t], d.beta[t], S) for t in range(steps)]
     dec = torch.stack(outs, dim=1)
     tm = lambda t: t.transpose(0, 1).contiguous()
-    pre, sf = kda.chunk_fwd(tm(d.q), tm(d.k), tm(d.v), tm(d.log_alpha), tm(d.beta), S0=d.S0, C=64)
+    pre, sf = kda.chunk_fwd(tm(d.q), tm(d.k), tm(d.v), tm(d.log_alpha), tm(d.beta), S0=d.S0, C=64, segments=1)
     torch.cuda.synchronize()
     e_o = rel(f64(dec), f64(pre))
     e_s = rel(f64(S), f64(sf))
