@@ -5,9 +5,12 @@ A step is one chunk prefill of the mid workload (B=4, H=32, T=8192,
 dk=dv=128, bf16 q/k/v, fp32 gates and state, C=64) through the C ABI
 (kda_chunk_fwd), with every input already resident in HBM.  `value` is
 prefill tokens/s (a token = one position of one sequence, all 32 heads).
+Before the W warm-up steps, about 100 ms of untimed launches let the GPU
+clocks settle (they ramp up over the first ~30 ms of load).
 
 Extra fields measure the other entry points on their own workloads:
   decode        256 sequences x 32 heads, 1024 one-token steps (steps/s)
+  decode_multi  the same sizes, 4 tokens per sequence and launch (tokens/s)
   long_context  B=1, H=16, T=65536 with an initial state (tokens/s)
   varlen        8 packed sequences of U[2048, 16384] tokens x 16 heads (tokens/s)
 
@@ -93,9 +96,24 @@ def load_traffic(kernel: str, workload: str):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
-def time_launches(launch, stream, steps, warmup, torch):
-    """Run `warmup` untimed launches, then exactly `steps` timed ones.
-    Returns (wall seconds over the steps, mean kernel ms from HIP events)."""
+def settle_clocks(launch, torch, seconds=0.1):
+    """Untimed launches for about `seconds` of wall time.  The GPU raises its
+    clocks over the first ~30 ms of sustained load (a launch of the mid
+    prefill takes ~0.9 ms cold and ~0.77 ms once settled), so a few warm-up
+    steps alone would time the ramp rather than the kernel."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            launch()
+        torch.cuda.synchronize()
+
+
+def time_launches(launch, stream, steps, warmup, torch, settle=True):
+    """Settle the clocks, run `warmup` untimed launches, then exactly `steps`
+    timed ones.  Returns (wall seconds over the steps, mean kernel ms from HIP
+    events)."""
+    if settle:
+        settle_clocks(launch, torch)
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
@@ -167,6 +185,30 @@ def bench_decode(args, torch, kda, kda_synth, stream):
         roofline=dict(bound="hbm", achieved=round(nbytes / (kms * 1e-3) / 1e9, 1), peak=HBM_PEAK_GBS,
                       unit="GB/s", frac=round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                       traffic=load_traffic("decode_step", "decode"), algorithmic_bytes=nbytes))
+
+
+def bench_decode_multi(args, torch, kda, kda_synth, stream, T=4, launches=50):
+    """T decode tokens per sequence and launch (kda_recurrent_fwd) on the decode
+    workload's sizes: 256 sequences x 32 heads, dk = dv = 128."""
+    w = kda_synth.WORKLOADS["decode"]
+    N, H, dk, dv = w["N"], w["H"], w["dk"], w["dv"]
+    p = kda_synth.prefill(N, T, H, dk, dv, dtype="bf16", g_mu=w["g_mu"], g_sigma=w["g_sigma"], beta=w["beta"],
+                          s0_sigma=0.1, seed=kda_synth.SEEDS["decode"], device="cuda")
+    S = p.S0.clone()
+    out = torch.empty((N, T, H, dv), dtype=torch.bfloat16, device="cuda")
+    h = stream.cuda_stream
+
+    def launch():
+        kda.kda_recurrent_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S, out, N, T, H, dk, dv, h)
+
+    wall, kms = time_launches(launch, stream, launches, 3, torch)
+    nbytes = N * H * 8 * dk * dv + N * T * H * (2 * (2 * dk + dv) + 4 * dk + 4 + 2 * dv)
+    del p, S, out
+    return dict(workload=f"multi-token decode: {N} sequences x H={H}, dk=dv={dk}, {T} tokens per launch",
+                tokens_per_s=N * T * launches / wall, launches_per_s=launches / wall, kernel_ms=kms,
+                roofline=dict(bound="hbm", achieved=round(nbytes / (kms * 1e-3) / 1e9, 1), peak=HBM_PEAK_GBS,
+                              unit="GB/s", frac=round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              algorithmic_bytes=nbytes))
 
 
 def bench_long(args, torch, kda, kda_synth, stream, steps=3):
@@ -250,7 +292,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--extras", default="decode,long,varlen",
+    ap.add_argument("--extras", default="decode,multi,long,varlen",
                     help="comma-separated extra workloads to run after the mid prefill "
                          "(decode, long, varlen; 'none' for the mid prefill only)")
     ap.add_argument("--no-extras", action="store_true", help="same as --extras none")
@@ -315,11 +357,11 @@ def main():
     del p_mid
     torch.cuda.empty_cache()
     extras = set() if args.no_extras or args.extras == "none" else set(args.extras.split(","))
-    unknown = extras - {"decode", "long", "varlen"}
+    unknown = extras - {"decode", "multi", "long", "varlen"}
     if unknown:
         raise SystemExit(f"unknown --extras entries: {sorted(unknown)}")
-    for name, key, fn in (("decode", "decode", bench_decode), ("long", "long_context", bench_long),
-                          ("varlen", "varlen", bench_varlen)):
+    for name, key, fn in (("decode", "decode", bench_decode), ("multi", "decode_multi", bench_decode_multi),
+                          ("long", "long_context", bench_long), ("varlen", "varlen", bench_varlen)):
         if name in extras:
             result[key] = fn(args, torch, kda, kda_synth, stream)
             torch.cuda.empty_cache()

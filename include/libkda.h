@@ -229,6 +229,31 @@ kda_status_t kda_recurrent_step_f32(const float *q, const float *k, const float 
                                     int N, int H, int dk, int dv, void *stream);
 
 /*
+ * T decode tokens per sequence in one launch: the fused recurrent mode of the
+ * "KDA derivation summary" page (sect. 6), whose kernel gives each program a
+ * sequence, a value head and a value block and loops the update over the
+ * tokens.  The state is read once, advanced through the T tokens in order
+ * and written once, so a launch moves 8 dv dk bytes of state per head
+ * however large T is (short prompts, speculative-decoding verification).
+ *
+ *   q, k      bf16 [N,T,H,dk];  v, out bf16 [N,T,H,dv]
+ *   log_alpha fp32 [N,T,H,dk];  beta fp32 [N,T,H]
+ *   S         fp32 [N,H,dv,dk], updated IN PLACE from S_{t-1} to S_{t+T-1}.
+ *
+ * T = 0 is a no-op.  T = 1 gives exactly kda_recurrent_step's result.
+ */
+kda_status_t kda_recurrent_fwd(const void *q, const void *k, const void *v,
+                               const float *log_alpha, const float *beta,
+                               float *S, void *out,
+                               int N, int T, int H, int dk, int dv, void *stream);
+
+/* fp32 q, k, v, out variant of kda_recurrent_fwd. */
+kda_status_t kda_recurrent_fwd_f32(const float *q, const float *k, const float *v,
+                                   const float *log_alpha, const float *beta,
+                                   float *S, float *out,
+                                   int N, int T, int H, int dk, int dv, void *stream);
+
+/*
  * Host-side check of a cu_seqlens array held in HOST memory: N >= 0,
  * cu[0] = 0, non-decreasing, cu[N] = T_total.  Returns KDA_OK or
  * KDA_ERR_BAD_SHAPE / KDA_ERR_NULL_POINTER.

@@ -24,9 +24,10 @@ __all__ = [
     "kda_chunk_fwd", "kda_chunk_fwd_f32", "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_f32",
     "kda_chunk_fwd_segmented", "kda_chunk_fwd_segmented_f32", "kda_chunk_fwd_varlen_segmented",
     "kda_chunk_fwd_varlen_segmented_f32", "kda_chunk_segmented_workspace_bytes", "kda_chunk_auto_segments",
-    "kda_recurrent_step", "kda_recurrent_step_f32", "kda_check_cu_seqlens_host",
+    "kda_recurrent_step", "kda_recurrent_step_f32", "kda_recurrent_fwd", "kda_recurrent_fwd_f32",
+    "kda_check_cu_seqlens_host",
     "kda_status_string", "kda_last_error", "kda_version",
-    "chunk_fwd", "chunk_fwd_varlen", "recurrent_step",
+    "chunk_fwd", "chunk_fwd_varlen", "recurrent_step", "recurrent_fwd",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -64,6 +65,7 @@ def load():
     chunk = [P] * 8 + [I] * 6 + [P]
     varlen = [P] * 9 + [I] * 6 + [P]
     step = [P] * 7 + [I] * 4 + [P]
+    multi = [P] * 7 + [I] * 5 + [P]
     Z = ctypes.c_size_t
     chunk_seg = [P] * 8 + [I] * 7 + [P, Z, P]
     varlen_seg = [P] * 9 + [I] * 7 + [P, Z, P]
@@ -72,7 +74,8 @@ def load():
                        ("kda_chunk_fwd_segmented", chunk_seg), ("kda_chunk_fwd_segmented_f32", chunk_seg),
                        ("kda_chunk_fwd_varlen_segmented", varlen_seg),
                        ("kda_chunk_fwd_varlen_segmented_f32", varlen_seg),
-                       ("kda_recurrent_step", step), ("kda_recurrent_step_f32", step)):
+                       ("kda_recurrent_step", step), ("kda_recurrent_step_f32", step),
+                       ("kda_recurrent_fwd", multi), ("kda_recurrent_fwd_f32", multi)):
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = I
@@ -190,6 +193,18 @@ def kda_recurrent_step_f32(q, k, v, log_alpha, beta, S, out, N, H, dk, dv, strea
         _stream(stream)))
 
 
+def kda_recurrent_fwd(q, k, v, log_alpha, beta, S, out, N, T, H, dk, dv, stream=None):
+    _check("kda_recurrent_fwd", load().kda_recurrent_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(out), N, T, H, dk, dv,
+        _stream(stream)))
+
+
+def kda_recurrent_fwd_f32(q, k, v, log_alpha, beta, S, out, N, T, H, dk, dv, stream=None):
+    _check("kda_recurrent_fwd_f32", load().kda_recurrent_fwd_f32(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(out), N, T, H, dk, dv,
+        _stream(stream)))
+
+
 def kda_check_cu_seqlens_host(cu_seqlens_host, N, T_total) -> int:
     """Check a host (CPU) int32 cu_seqlens; returns the status code."""
     return load().kda_check_cu_seqlens_host(_ptr(cu_seqlens_host), N, T_total)
@@ -280,4 +295,18 @@ def recurrent_step(q, k, v, log_alpha, beta, S, out=None, stream=None):
         out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     fn = kda_recurrent_step_f32 if f32 else kda_recurrent_step
     fn(q, k, v, log_alpha, beta, S, out, N, H, dk, dv, stream)
+    return out
+
+
+def recurrent_fwd(q, k, v, log_alpha, beta, S, out=None, stream=None):
+    """T decode tokens per sequence on [N, T, H, d] tensors in one launch; S
+    [N, H, dv, dk] fp32 is updated in place.  Returns out [N, T, H, dv]."""
+    import torch
+    f32 = _mode(q)
+    N, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((N, T, H, dv), dtype=q.dtype, device=q.device)
+    fn = kda_recurrent_fwd_f32 if f32 else kda_recurrent_fwd
+    fn(q, k, v, log_alpha, beta, S, out, N, T, H, dk, dv, stream)
     return out

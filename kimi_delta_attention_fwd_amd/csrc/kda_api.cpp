@@ -248,16 +248,21 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
     return ok();
 }
 
+// Shared body of the decode entry points: T tokens per sequence (T = 1 for
+// the step entry points, whose [N, H, d] tensors are the [N, 1, H, d] case).
 kda_status_t step_common(bool f32, const void *q, const void *k, const void *v, const float *log_alpha,
-                         const float *beta, float *S, void *out, int N, int H, int dk, int dv, void *stream)
+                         const float *beta, float *S, void *out, int N, int H, int dk, int dv, void *stream,
+                         int T = 1, bool multi = false)
 {
     if (N < 0) return fail(KDA_ERR_BAD_SHAPE, "N must be >= 0 (got %d)", N);
+    if (T < 0) return fail(KDA_ERR_BAD_SHAPE, "T must be >= 0 (got %d)", T);
     if (H < 1) return fail(KDA_ERR_BAD_SHAPE, "H must be >= 1 (got %d)", H);
     if (!supported_d(dk) || !supported_d(dv))
         return fail(KDA_ERR_UNSUPPORTED, "dk and dv must be 16, 32, 64 or 128 (got %d, %d)", dk, dv);
     const uint64_t nheads = (uint64_t)N * (uint64_t)H;
-    if (nheads > (uint64_t)INT32_MAX) return fail(KDA_ERR_BAD_SHAPE, "problem too large");
-    if (nheads == 0) return ok();
+    const uint64_t ntok = nheads * (uint64_t)T;
+    if (nheads > (uint64_t)INT32_MAX || ntok * 128u > (uint64_t)1 << 60) return fail(KDA_ERR_BAD_SHAPE, "problem too large");
+    if (nheads == 0 || T == 0) return ok();
     if (!q || !k || !v || !log_alpha || !beta || !S || !out)
         return fail(KDA_ERR_NULL_POINTER, "q, k, v, log_alpha, beta, S and out are required");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
@@ -265,10 +270,10 @@ kda_status_t step_common(bool f32, const void *q, const void *k, const void *v, 
         return fail(KDA_ERR_MISALIGNED, "q, k, v, out, log_alpha and S must be 16-byte aligned");
     if (!aligned(beta, 4)) return fail(KDA_ERR_MISALIGNED, "beta must be 4-byte aligned");
     const uint64_t es = f32 ? 4 : 2;
-    const Buf ins[] = {{q, nheads * dk * es, "q"}, {k, nheads * dk * es, "k"}, {v, nheads * dv * es, "v"},
-                       {log_alpha, nheads * dk * 4, "log_alpha"}, {beta, nheads * 4, "beta"}};
+    const Buf ins[] = {{q, ntok * dk * es, "q"}, {k, ntok * dk * es, "k"}, {v, ntok * dv * es, "v"},
+                       {log_alpha, ntok * dk * 4, "log_alpha"}, {beta, ntok * 4, "beta"}};
     const Buf sb{S, nheads * dv * dk * 4, "S"};
-    kda_status_t st = check_aliasing(Buf{out, nheads * dv * es, "out"}, ins, 5, sb, sb);
+    kda_status_t st = check_aliasing(Buf{out, ntok * dv * es, "out"}, ins, 5, sb, sb);
     if (st != KDA_OK) return st;
 
     kda::DecodeArgs a;
@@ -284,7 +289,7 @@ kda_status_t step_common(bool f32, const void *q, const void *k, const void *v, 
     a.dk = dk;
     a.dv = dv;
     a.stream = (hipStream_t)stream;
-    const hipError_t e = kda::launch_decode(a, f32);
+    const hipError_t e = (multi && T > 1) ? kda::launch_decode_multi(a, T, f32) : kda::launch_decode(a, f32);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -389,6 +394,20 @@ kda_status_t kda_recurrent_step_f32(const float *q, const float *k, const float 
                                     void *stream)
 {
     return step_common(true, q, k, v, log_alpha, beta, S, out, N, H, dk, dv, stream);
+}
+
+kda_status_t kda_recurrent_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                               const float *beta, float *S, void *out, int N, int T, int H, int dk, int dv,
+                               void *stream)
+{
+    return step_common(false, q, k, v, log_alpha, beta, S, out, N, H, dk, dv, stream, T, true);
+}
+
+kda_status_t kda_recurrent_fwd_f32(const float *q, const float *k, const float *v, const float *log_alpha,
+                                   const float *beta, float *S, float *out, int N, int T, int H, int dk, int dv,
+                                   void *stream)
+{
+    return step_common(true, q, k, v, log_alpha, beta, S, out, N, H, dk, dv, stream, T, true);
 }
 
 kda_status_t kda_check_cu_seqlens_host(const int32_t *cu, int N, int T_total)

@@ -96,6 +96,104 @@ decode_step_kernel(const In *__restrict__ q, const In *__restrict__ k, const In 
     }
 }
 
+// T tokens per (sequence, head) in one launch: the rows are read once, carried
+// in registers through the tokens in order, and written once.  This is the
+// fused recurrent mode itself (the "KDA derivation summary" page, sect. 6: a
+// program per sequence, value head and value block looping the update over
+// the tokens).  Token t of sequence n sits at row (n T + t) H + h of the
+// [N, T, H, d] inputs.  Per token the arithmetic is the decode step's, in the
+// same order, so T = 1 matches kda_recurrent_step bit for bit.
+template <typename In, int DK>
+__global__ void __launch_bounds__(256)
+decode_multi_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
+                    const float *__restrict__ log_alpha, const float *__restrict__ beta,
+                    float *__restrict__ S, In *__restrict__ out, int T, int H, int dv)
+{
+    typedef In In4 __attribute__((ext_vector_type(4)));
+    constexpr int LPR = DK / 16;
+    constexpr int RPP = 256 / LPR;
+    constexpr int MAXP = (128 + RPP - 1) / RPP;
+    const long head = blockIdx.x;
+    const long n = head / H, h = head % H;
+    const int tid = threadIdx.x, sub = tid % LPR, rloc = tid / LPR;
+
+    f32x4 s[MAXP][4];
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+        const int row = p * RPP + rloc;
+        if (row < dv) {
+            const float *src = S + (head * dv + row) * DK + 4 * sub;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s[p][u] = __builtin_nontemporal_load((const f32x4 *)(src + 4 * LPR * u));
+        }
+    }
+    for (int t = 0; t < T; ++t) {
+        const long tok = (n * T + t) * H + h;
+        f32x4 a[4], kk[4], qq[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const long c = tok * DK + 4 * (sub + LPR * u);
+            const f32x4 la = *(const f32x4 *)(log_alpha + c);
+            const In4 kv = *(const In4 *)(k + c);
+            const In4 qv = *(const In4 *)(q + c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                a[u][j] = __expf(la[j]);
+                kk[u][j] = tof(kv[j]);
+                qq[u][j] = tof(qv[j]);
+            }
+        }
+        const float b = beta[tok];
+#pragma unroll
+        for (int p = 0; p < MAXP; ++p) {
+            const int row = p * RPP + rloc;
+            if (row < dv) {
+                const float vi = tof(v[tok * dv + row]);
+                float pred = 0.f;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        s[p][u][j] *= a[u][j];
+                        pred += s[p][u][j] * kk[u][j];
+                    }
+                pred = group_sum<LPR>(pred);
+                const float e = b * (vi - pred);
+                float o = 0.f;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        s[p][u][j] += e * kk[u][j];
+                        o += s[p][u][j] * qq[u][j];
+                    }
+                o = group_sum<LPR>(o);
+                if (sub == 0) out[tok * dv + row] = fromf<In>(o);
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+        const int row = p * RPP + rloc;
+        if (row < dv) {
+            float *dst = S + (head * dv + row) * DK + 4 * sub;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(s[p][u], (f32x4 *)(dst + 4 * LPR * u));
+        }
+    }
+}
+
+template <typename In, int DK>
+hipError_t launch_decode_multi_t(const DecodeArgs &a, int T)
+{
+    const long grid = (long)a.N * a.H;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_multi_kernel<In, DK>), dim3((unsigned)grid), dim3(256), 0, a.stream,
+                       (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S,
+                       (In *)a.out, T, a.H, a.dv);
+    return hipGetLastError();
+}
+
 template <typename In, int DK>
 hipError_t launch_decode_t(const DecodeArgs &a)
 {

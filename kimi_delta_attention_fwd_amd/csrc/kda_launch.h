@@ -45,7 +45,9 @@ hipError_t launch_chunk_f32_128(const ChunkArgs &);
 // launchers; pure host code, no HIP call.
 bool chunk_fits(bool f32, int dk, int BV, int C);
 
-// Decode step launcher.  Defined in kda_decode.hip.
+// Decode launchers: one token, and T tokens per sequence (q, k, v, out,
+// log_alpha, beta laid out [N, T, H, d]).  Defined in kda_decode.hip.
 hipError_t launch_decode(const DecodeArgs &, bool f32);
+hipError_t launch_decode_multi(const DecodeArgs &, int T, bool f32);
 
 }  // namespace kda

@@ -230,3 +230,19 @@ def test_segmented_varlen_validation(lib):
     assert fn(*args, 3, None, wsb, None) == 1
     assert fn(*args, 3, WS, wsb - 4, None) == 2
     assert fn(*args, -1, WS, wsb, None) == 2
+
+
+def test_recurrent_fwd_validation(lib):
+    def multi(q=A, k=A + MB, v=A + 2 * MB, la=A + 3 * MB, beta=A + 4 * MB, S=A + 8 * MB, out=A + 64 * MB,
+              N=4, T=3, H=2, dk=128, dv=128):
+        return lib.kda_recurrent_fwd(q, k, v, la, beta, S, out, N, T, H, dk, dv, None)
+    assert multi(T=-1) == 2
+    assert multi(T=0, q=None, k=None, v=None, la=None, beta=None, S=None, out=None) == 0
+    assert multi(N=0) == 0
+    assert multi(q=None) == 1
+    assert multi(S=A + 8 * MB + 4) == 4
+    assert multi(dk=96) == 3
+    # out must not overlap q, which holds N*T*H*dk elements (3 tokens, so 3x a step's)
+    assert multi(out=A + 4 * 2 * 128 * 2 * 2 - 16) == 6
+    assert lib.kda_recurrent_fwd_f32(A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 8 * MB, A + 64 * MB,
+                                     4, 2, 2, 16, 256, None) == 3

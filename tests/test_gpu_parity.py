@@ -476,6 +476,60 @@ def test_decode_equals_chunk_prefill_on_same_stream(dev):
     assert_close("prefill", f64(pre), f64(sf), o_ref, s_ref, TOL["bf16"])
 
 
+# ---------------------------------------------------------------- multi-token decode
+@pytest.mark.parametrize("N,T,H,dk,dv,dtype", [(3, 2, 2, 64, 32, "bf16"), (2, 5, 3, 128, 128, "bf16"),
+                                               (4, 16, 1, 16, 128, "f32"), (2, 7, 2, 32, 64, "f32"),
+                                               (5, 3, 2, 128, 16, "bf16"), (1, 64, 2, 128, 128, "bf16")])
+def test_recurrent_fwd_matches_oracle(dev, N, T, H, dk, dv, dtype):
+    note(f"case multi-token decode N{N} T{T} H{H} dk{dk} dv{dv} {dtype}")
+    p = kda_synth.prefill(N, T, H, dk, dv, dtype=dtype, s0_sigma=0.1, seed=61 + T + dk + dv, device=dev)
+    S = p.S0.clone()
+    out = kda.recurrent_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_dense(p)
+    assert_close("recurrent_fwd", f64(out), f64(S), o_ref, s_ref, TOL[dtype])
+
+
+def test_recurrent_fwd_equals_single_steps(dev):
+    """T tokens in one launch give bit for bit what T single-step launches give."""
+    for dtype in ("bf16", "f32"):
+        N, T, H, dk, dv = 3, 6, 2, 128, 64
+        note(f"case multi-token vs single steps N{N} T{T} H{H} dk{dk} dv{dv} {dtype} (bitwise)")
+        p = kda_synth.prefill(N, T, H, dk, dv, dtype=dtype, s0_sigma=0.1, seed=67, device=dev)
+        S1 = p.S0.clone()
+        out1 = kda.recurrent_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S1)
+        S2 = p.S0.clone()
+        outs = [kda.recurrent_step(p.q[:, t].contiguous(), p.k[:, t].contiguous(), p.v[:, t].contiguous(),
+                                   p.log_alpha[:, t].contiguous(), p.beta[:, t].contiguous(), S2)
+                for t in range(T)]
+        torch.cuda.synchronize()
+        assert torch.equal(out1, torch.stack(outs, dim=1)) and torch.equal(S1, S2)
+
+
+def test_recurrent_fwd_edge_cases(dev):
+    note("case multi-token decode edges: T = 0 leaves S alone, T = 1, guard bands around out and S")
+    p = kda_synth.prefill(2, 0, 2, 64, 64, dtype="bf16", s0_sigma=0.1, seed=71, device=dev)
+    S = p.S0.clone()
+    kda.recurrent_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S)
+    torch.cuda.synchronize()
+    assert torch.equal(S, p.S0)
+    N, T, H, dk, dv = 2, 9, 3, 64, 64
+    p = kda_synth.prefill(N, T, H, dk, dv, dtype="bf16", s0_sigma=0.1, seed=73, device=dev)
+    pad = 2048
+    n_out, n_s = N * T * H * dv, N * H * dv * dk
+    big_out = torch.full((n_out + 2 * pad,), 7.0, dtype=torch.bfloat16, device=dev)
+    big_s = torch.full((n_s + 2 * pad,), -3.0, dtype=torch.float32, device=dev)
+    out = big_out[pad:pad + n_out].view(N, T, H, dv)
+    S = big_s[pad:pad + n_s].view(N, H, dv, dk)
+    S.copy_(p.S0)
+    kda.kda_recurrent_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S, out, N, T, H, dk, dv)
+    torch.cuda.synchronize()
+    assert torch.all(big_out[:pad] == 7.0) and torch.all(big_out[pad + n_out:] == 7.0)
+    assert torch.all(big_s[:pad] == -3.0) and torch.all(big_s[pad + n_s:] == -3.0)
+    o_ref, s_ref = oracle_dense(p)
+    assert_close("recurrent_fwd guarded", f64(out), f64(S), o_ref, s_ref, TOL["bf16"])
+
+
 def test_decode_is_deterministic(dev):
     note("case decode determinism N8 H4 d128")
     d = kda_synth.decode(8, 4, 128, 128, 3, seed=51, device=dev, step_block=3)
