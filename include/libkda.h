@@ -191,6 +191,64 @@ kda_status_t kda_chunk_fwd_varlen_segmented_f32(const float *q, const float *k, 
                                                 void *stream);
 
 /*
+ * VARIANTS.  The pages place KDA in a family that differs only in how the
+ * state forgets and how it writes ("Kimi K3 notes 1: KDA" page, the boxed
+ * summary of sect. 5: linear attention, DeltaNet, Gated DeltaNet, KDA;
+ * "Linear/sparse attention tutorial" page, sect. 2.4: RetNet's scalar decay
+ * and GLA's per-channel gate on an additive write).  The *_ex entry points
+ * run any member with the same kernels:
+ *   gate   KDA_GATE_CHANNEL  log_alpha [.., H, dk], one decay per key channel
+ *                            (KDA, GLA)
+ *          KDA_GATE_SCALAR   log_alpha [.., H], one decay per token and head
+ *                            for all key channels (Gated DeltaNet, RetNet-like);
+ *                            4-byte alignment suffices
+ *          KDA_GATE_NONE     alpha = 1; log_alpha is not read and may be NULL
+ *                            (DeltaNet, linear attention)
+ *   write  KDA_WRITE_DELTA   e_t = beta_t (v_t - S~_t k_t)   (the delta rule)
+ *          KDA_WRITE_ADD     e_t = beta_t v_t, S_t = S~_t + beta_t v_t k_t^T
+ *                            (linear attention, GLA; beta = 1 gives them exactly)
+ * variant = gate | write; anything else is KDA_ERR_BAD_SHAPE.  The plain entry
+ * points are variant 0 (KDA_GATE_CHANNEL | KDA_WRITE_DELTA).
+ */
+enum {
+    KDA_GATE_CHANNEL = 0,
+    KDA_GATE_SCALAR = 1,
+    KDA_GATE_NONE = 2,
+    KDA_WRITE_DELTA = 0,
+    KDA_WRITE_ADD = 4
+};
+
+/* Chunk prefill with a variant and an optional segment-parallel schedule
+ * (nseg, workspace as in kda_chunk_fwd_segmented; nseg = 1 needs no
+ * workspace).  Dense and packed layouts, bf16 and fp32 inputs. */
+kda_status_t kda_chunk_fwd_ex(const void *q, const void *k, const void *v,
+                              const float *log_alpha, const float *beta,
+                              const float *S0, void *out, float *S_final,
+                              int B, int T, int H, int dk, int dv, int C,
+                              int variant, int nseg, void *workspace, size_t workspace_bytes,
+                              void *stream);
+kda_status_t kda_chunk_fwd_ex_f32(const float *q, const float *k, const float *v,
+                                  const float *log_alpha, const float *beta,
+                                  const float *S0, float *out, float *S_final,
+                                  int B, int T, int H, int dk, int dv, int C,
+                                  int variant, int nseg, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+kda_status_t kda_chunk_fwd_varlen_ex(const void *q, const void *k, const void *v,
+                                     const float *log_alpha, const float *beta,
+                                     const float *S0, void *out, float *S_final,
+                                     const int32_t *cu_seqlens, int N, int T_total,
+                                     int H, int dk, int dv, int C,
+                                     int variant, int nseg, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+kda_status_t kda_chunk_fwd_varlen_ex_f32(const float *q, const float *k, const float *v,
+                                         const float *log_alpha, const float *beta,
+                                         const float *S0, float *out, float *S_final,
+                                         const int32_t *cu_seqlens, int N, int T_total,
+                                         int H, int dk, int dv, int C,
+                                         int variant, int nseg, void *workspace, size_t workspace_bytes,
+                                         void *stream);
+
+/*
  * Workspace bytes of the segmented entry points for nseq sequences (B or N)
  * of H heads: 4 * nseq * H * ((nseg - 1) (dv + dk) dk + nseg dv dk), the
  * first part rounded up to 256 bytes.  0 for nseg = 1 or invalid sizes.
@@ -252,6 +310,16 @@ kda_status_t kda_recurrent_fwd_f32(const float *q, const float *k, const float *
                                    const float *log_alpha, const float *beta,
                                    float *S, float *out,
                                    int N, int T, int H, int dk, int dv, void *stream);
+
+/* kda_recurrent_fwd with a variant (see VARIANTS above). */
+kda_status_t kda_recurrent_fwd_ex(const void *q, const void *k, const void *v,
+                                  const float *log_alpha, const float *beta,
+                                  float *S, void *out,
+                                  int N, int T, int H, int dk, int dv, int variant, void *stream);
+kda_status_t kda_recurrent_fwd_ex_f32(const float *q, const float *k, const float *v,
+                                      const float *log_alpha, const float *beta,
+                                      float *S, float *out,
+                                      int N, int T, int H, int dk, int dv, int variant, void *stream);
 
 /*
  * Host-side check of a cu_seqlens array held in HOST memory: N >= 0,

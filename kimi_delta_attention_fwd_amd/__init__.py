@@ -24,6 +24,8 @@ __all__ = [
     "kda_chunk_fwd", "kda_chunk_fwd_f32", "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_f32",
     "kda_chunk_fwd_segmented", "kda_chunk_fwd_segmented_f32", "kda_chunk_fwd_varlen_segmented",
     "kda_chunk_fwd_varlen_segmented_f32", "kda_chunk_segmented_workspace_bytes", "kda_chunk_auto_segments",
+    "kda_chunk_fwd_ex", "kda_chunk_fwd_ex_f32", "kda_chunk_fwd_varlen_ex", "kda_chunk_fwd_varlen_ex_f32",
+    "kda_recurrent_fwd_ex", "kda_recurrent_fwd_ex_f32", "variant",
     "kda_recurrent_step", "kda_recurrent_step_f32", "kda_recurrent_fwd", "kda_recurrent_fwd_f32",
     "kda_check_cu_seqlens_host",
     "kda_status_string", "kda_last_error", "kda_version",
@@ -66,6 +68,9 @@ def load():
     varlen = [P] * 9 + [I] * 6 + [P]
     step = [P] * 7 + [I] * 4 + [P]
     multi = [P] * 7 + [I] * 5 + [P]
+    multi_ex = [P] * 7 + [I] * 6 + [P]
+    chunk_ex = [P] * 8 + [I] * 8 + [P, ctypes.c_size_t, P]
+    varlen_ex = [P] * 9 + [I] * 8 + [P, ctypes.c_size_t, P]
     Z = ctypes.c_size_t
     chunk_seg = [P] * 8 + [I] * 7 + [P, Z, P]
     varlen_seg = [P] * 9 + [I] * 7 + [P, Z, P]
@@ -75,7 +80,10 @@ def load():
                        ("kda_chunk_fwd_varlen_segmented", varlen_seg),
                        ("kda_chunk_fwd_varlen_segmented_f32", varlen_seg),
                        ("kda_recurrent_step", step), ("kda_recurrent_step_f32", step),
-                       ("kda_recurrent_fwd", multi), ("kda_recurrent_fwd_f32", multi)):
+                       ("kda_recurrent_fwd", multi), ("kda_recurrent_fwd_f32", multi),
+                       ("kda_recurrent_fwd_ex", multi_ex), ("kda_recurrent_fwd_ex_f32", multi_ex),
+                       ("kda_chunk_fwd_ex", chunk_ex), ("kda_chunk_fwd_ex_f32", chunk_ex),
+                       ("kda_chunk_fwd_varlen_ex", varlen_ex), ("kda_chunk_fwd_varlen_ex_f32", varlen_ex)):
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = I
@@ -205,6 +213,58 @@ def kda_recurrent_fwd_f32(q, k, v, log_alpha, beta, S, out, N, T, H, dk, dv, str
         _stream(stream)))
 
 
+GATES = {"channel": 0, "scalar": 1, "none": 2}
+WRITES = {"delta": 0, "add": 4}
+
+
+def variant(gate="channel", write="delta") -> int:
+    """Variant selector of the *_ex entry points: gate "channel" (KDA, GLA),
+    "scalar" (one decay per token and head) or "none"; write "delta" or "add"."""
+    return GATES[gate] | WRITES[write]
+
+
+def kda_chunk_fwd_ex(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, dk, dv, C, variant, nseg=1,
+                     workspace=None, workspace_bytes=0, stream=None):
+    _check("kda_chunk_fwd_ex", load().kda_chunk_fwd_ex(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_final),
+        B, T, H, dk, dv, C, variant, nseg, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def kda_chunk_fwd_ex_f32(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, dk, dv, C, variant, nseg=1,
+                         workspace=None, workspace_bytes=0, stream=None):
+    _check("kda_chunk_fwd_ex_f32", load().kda_chunk_fwd_ex_f32(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_final),
+        B, T, H, dk, dv, C, variant, nseg, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def kda_chunk_fwd_varlen_ex(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N, T_total, H, dk, dv, C,
+                            variant, nseg=1, workspace=None, workspace_bytes=0, stream=None):
+    _check("kda_chunk_fwd_varlen_ex", load().kda_chunk_fwd_varlen_ex(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_final),
+        _ptr(cu_seqlens), N, T_total, H, dk, dv, C, variant, nseg, _ptr(workspace), workspace_bytes,
+        _stream(stream)))
+
+
+def kda_chunk_fwd_varlen_ex_f32(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N, T_total, H, dk, dv,
+                                C, variant, nseg=1, workspace=None, workspace_bytes=0, stream=None):
+    _check("kda_chunk_fwd_varlen_ex_f32", load().kda_chunk_fwd_varlen_ex_f32(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_final),
+        _ptr(cu_seqlens), N, T_total, H, dk, dv, C, variant, nseg, _ptr(workspace), workspace_bytes,
+        _stream(stream)))
+
+
+def kda_recurrent_fwd_ex(q, k, v, log_alpha, beta, S, out, N, T, H, dk, dv, variant, stream=None):
+    _check("kda_recurrent_fwd_ex", load().kda_recurrent_fwd_ex(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(out), N, T, H, dk, dv, variant,
+        _stream(stream)))
+
+
+def kda_recurrent_fwd_ex_f32(q, k, v, log_alpha, beta, S, out, N, T, H, dk, dv, variant, stream=None):
+    _check("kda_recurrent_fwd_ex_f32", load().kda_recurrent_fwd_ex_f32(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(out), N, T, H, dk, dv, variant,
+        _stream(stream)))
+
+
 def kda_check_cu_seqlens_host(cu_seqlens_host, N, T_total) -> int:
     """Check a host (CPU) int32 cu_seqlens; returns the status code."""
     return load().kda_check_cu_seqlens_host(_ptr(cu_seqlens_host), N, T_total)
@@ -238,11 +298,14 @@ def _workspace(nseq, H, dk, dv, nseg, device):
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device), nbytes
 
 
-def chunk_fwd(q, k, v, log_alpha, beta, S0=None, C=64, output_final_state=True, stream=None, segments="auto"):
+def chunk_fwd(q, k, v, log_alpha, beta, S0=None, C=64, output_final_state=True, stream=None, segments="auto",
+              gate="channel", write="delta"):
     """Chunk prefill of a dense batch.  Returns ``(out, S_final or None)``.
 
     ``segments``: 1 for the single pass, n > 1 for the segment-parallel
     schedule with n segments per sequence, "auto" for the library's choice.
+    ``gate`` / ``write`` select a variant (see :func:`variant`); with
+    gate="scalar" log_alpha is [B, T, H], with gate="none" it may be None.
     """
     import torch
     f32 = _mode(q)
@@ -251,7 +314,12 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, C=64, output_final_state=True, 
     out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     sf = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device) if output_final_state else None
     nseg = kda_chunk_auto_segments(B, T, H, dk, dv, C, f32) if segments == "auto" else int(segments)
-    if nseg == 1:
+    var = variant(gate, write)
+    if var != 0:
+        ws, nbytes = _workspace(B, H, dk, dv, nseg, q.device) if nseg > 1 else (None, 0)
+        fn = kda_chunk_fwd_ex_f32 if f32 else kda_chunk_fwd_ex
+        fn(q, k, v, log_alpha, beta, S0, out, sf, B, T, H, dk, dv, C, var, nseg, ws, nbytes, stream)
+    elif nseg == 1:
         fn = kda_chunk_fwd_f32 if f32 else kda_chunk_fwd
         fn(q, k, v, log_alpha, beta, S0, out, sf, B, T, H, dk, dv, C, stream)
     else:
@@ -298,7 +366,7 @@ def recurrent_step(q, k, v, log_alpha, beta, S, out=None, stream=None):
     return out
 
 
-def recurrent_fwd(q, k, v, log_alpha, beta, S, out=None, stream=None):
+def recurrent_fwd(q, k, v, log_alpha, beta, S, out=None, stream=None, gate="channel", write="delta"):
     """T decode tokens per sequence on [N, T, H, d] tensors in one launch; S
     [N, H, dv, dk] fp32 is updated in place.  Returns out [N, T, H, dv]."""
     import torch
@@ -307,6 +375,11 @@ def recurrent_fwd(q, k, v, log_alpha, beta, S, out=None, stream=None):
     dv = v.shape[-1]
     if out is None:
         out = torch.empty((N, T, H, dv), dtype=q.dtype, device=q.device)
-    fn = kda_recurrent_fwd_f32 if f32 else kda_recurrent_fwd
-    fn(q, k, v, log_alpha, beta, S, out, N, T, H, dk, dv, stream)
+    var = variant(gate, write)
+    if var != 0:
+        fn = kda_recurrent_fwd_ex_f32 if f32 else kda_recurrent_fwd_ex
+        fn(q, k, v, log_alpha, beta, S, out, N, T, H, dk, dv, var, stream)
+    else:
+        fn = kda_recurrent_fwd_f32 if f32 else kda_recurrent_fwd
+        fn(q, k, v, log_alpha, beta, S, out, N, T, H, dk, dv, stream)
     return out

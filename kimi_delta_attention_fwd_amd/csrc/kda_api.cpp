@@ -94,6 +94,10 @@ int choose_bv(bool f32, int dk, int dv, int C, long units, int maxbv = 64)
 
 constexpr int kMaxSegments = 1024;
 
+// Variant selector of the *_ex entry points: bits 0-1 the gate (0 per
+// channel, 1 one value per token and head, 2 none), bit 2 the additive write.
+bool valid_variant(int variant) { return (variant & ~7) == 0 && (variant & 3) != 3; }
+
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 // Workspace of the segment-parallel schedule: the segment maps, then the
@@ -162,8 +166,10 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
                           const float *log_alpha, const float *beta, const float *S0, void *out,
                           float *S_final, const int32_t *cu_seqlens, int nseq, int T, int T_total,
                           int H, int dk, int dv, int C, void *stream, int nseg = 1, void *workspace = nullptr,
-                          uint64_t workspace_bytes = 0)
+                          uint64_t workspace_bytes = 0, int variant = 0)
 {
+    if (!valid_variant(variant)) return fail(KDA_ERR_BAD_SHAPE, "invalid variant %d", variant);
+    const int gate = variant & 3;
     if (nseg < 1 || nseg > kMaxSegments)
         return fail(KDA_ERR_BAD_SHAPE, "segment count must be in [1, %d] (got %d)", kMaxSegments, nseg);
     if (nseq < 0 || T < 0 || T_total < 0)
@@ -184,18 +190,21 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
     const uint64_t es = f32 ? 4 : 2;
     const uint64_t nk = ntok * H * dk, nv = ntok * H * dv, nb = ntok * H, ns = nheads * dv * dk;
 
-    if (ntok > 0 && (!q || !k || !v || !log_alpha || !beta || !out))
+    if (ntok > 0 && (!q || !k || !v || (gate != 2 && !log_alpha) || !beta || !out))
         return fail(KDA_ERR_NULL_POINTER, "q, k, v, log_alpha, beta and out are required when there are tokens");
+    if (gate == 2) log_alpha = nullptr;   // not read
     if (varlen && nseq > 0 && !cu_seqlens) return fail(KDA_ERR_NULL_POINTER, "cu_seqlens is required");
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(log_alpha, 16))
-        return fail(KDA_ERR_MISALIGNED, "q, k, v, out and log_alpha must be 16-byte aligned");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(log_alpha, gate == 0 ? 16 : 4))
+        return fail(KDA_ERR_MISALIGNED, "q, k, v, out and log_alpha must be 16-byte aligned (log_alpha 4 with "
+                                         "one gate per token)");
     if (!aligned(S0, 16) || !aligned(S_final, 16))
         return fail(KDA_ERR_MISALIGNED, "S0 and S_final must be 16-byte aligned");
     if (!aligned(beta, 4) || !aligned(cu_seqlens, 4))
         return fail(KDA_ERR_MISALIGNED, "beta and cu_seqlens must be 4-byte aligned");
 
     const Buf ins[] = {{q, nk * es, "q"}, {k, nk * es, "k"}, {v, nv * es, "v"},
-                       {log_alpha, nk * 4, "log_alpha"}, {beta, nb * 4, "beta"},
+                       {log_alpha, gate == 0 ? nk * 4 : nb * 4, "log_alpha"}, {beta, nb * 4, "beta"},
                        {cu_seqlens, varlen ? (uint64_t)(nseq + 1) * 4 : 0, "cu_seqlens"}};
     kda_status_t st = check_aliasing(Buf{out, nv * es, "out"}, ins, 6,
                                      Buf{S_final, S_final ? ns * 4 : 0, "S_final"},
@@ -240,6 +249,8 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
     a.C = C;
     a.BV = BV;
     a.nsegs = nseg;
+    a.gate = gate;
+    a.add = (variant >> 2) & 1;
     a.seg_map = nseg > 1 ? (float *)workspace : nullptr;
     a.seg_start = nseg > 1 ? (float *)((char *)workspace + seg_map_bytes(nheads, dk, dv, nseg)) : nullptr;
     a.stream = (hipStream_t)stream;
@@ -252,8 +263,10 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
 // the step entry points, whose [N, H, d] tensors are the [N, 1, H, d] case).
 kda_status_t step_common(bool f32, const void *q, const void *k, const void *v, const float *log_alpha,
                          const float *beta, float *S, void *out, int N, int H, int dk, int dv, void *stream,
-                         int T = 1, bool multi = false)
+                         int T = 1, bool multi = false, int variant = 0)
 {
+    if (!valid_variant(variant)) return fail(KDA_ERR_BAD_SHAPE, "invalid variant %d", variant);
+    const int gate = variant & 3;
     if (N < 0) return fail(KDA_ERR_BAD_SHAPE, "N must be >= 0 (got %d)", N);
     if (T < 0) return fail(KDA_ERR_BAD_SHAPE, "T must be >= 0 (got %d)", T);
     if (H < 1) return fail(KDA_ERR_BAD_SHAPE, "H must be >= 1 (got %d)", H);
@@ -263,15 +276,17 @@ kda_status_t step_common(bool f32, const void *q, const void *k, const void *v, 
     const uint64_t ntok = nheads * (uint64_t)T;
     if (nheads > (uint64_t)INT32_MAX || ntok * 128u > (uint64_t)1 << 60) return fail(KDA_ERR_BAD_SHAPE, "problem too large");
     if (nheads == 0 || T == 0) return ok();
-    if (!q || !k || !v || !log_alpha || !beta || !S || !out)
+    if (!q || !k || !v || (gate != 2 && !log_alpha) || !beta || !S || !out)
         return fail(KDA_ERR_NULL_POINTER, "q, k, v, log_alpha, beta, S and out are required");
+    if (gate == 2) log_alpha = nullptr;   // not read
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-        !aligned(log_alpha, 16) || !aligned(S, 16))
-        return fail(KDA_ERR_MISALIGNED, "q, k, v, out, log_alpha and S must be 16-byte aligned");
+        !aligned(log_alpha, gate == 0 ? 16 : 4) || !aligned(S, 16))
+        return fail(KDA_ERR_MISALIGNED, "q, k, v, out, log_alpha and S must be 16-byte aligned (log_alpha 4 "
+                                         "with one gate per token)");
     if (!aligned(beta, 4)) return fail(KDA_ERR_MISALIGNED, "beta must be 4-byte aligned");
     const uint64_t es = f32 ? 4 : 2;
     const Buf ins[] = {{q, ntok * dk * es, "q"}, {k, ntok * dk * es, "k"}, {v, ntok * dv * es, "v"},
-                       {log_alpha, ntok * dk * 4, "log_alpha"}, {beta, ntok * 4, "beta"}};
+                       {log_alpha, gate == 0 ? ntok * dk * 4 : ntok * 4, "log_alpha"}, {beta, ntok * 4, "beta"}};
     const Buf sb{S, nheads * dv * dk * 4, "S"};
     kda_status_t st = check_aliasing(Buf{out, ntok * dv * es, "out"}, ins, 5, sb, sb);
     if (st != KDA_OK) return st;
@@ -288,6 +303,8 @@ kda_status_t step_common(bool f32, const void *q, const void *k, const void *v, 
     a.H = H;
     a.dk = dk;
     a.dv = dv;
+    a.gate = gate;
+    a.add = (variant >> 2) & 1;
     a.stream = (hipStream_t)stream;
     const hipError_t e = (multi && T > 1) ? kda::launch_decode_multi(a, T, f32) : kda::launch_decode(a, f32);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode kernel launch failed: %s", hipGetErrorString(e));
@@ -369,6 +386,58 @@ kda_status_t kda_chunk_fwd_varlen_segmented_f32(const float *q, const float *k, 
 {
     return chunk_common(true, true, q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N, 0, T_total,
                         H, dk, dv, C, stream, nseg, workspace, workspace_bytes);
+}
+
+kda_status_t kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const float *log_alpha,
+                              const float *beta, const float *S0, void *out, float *S_final, int B, int T, int H,
+                              int dk, int dv, int C, int variant, int nseg, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    return chunk_common(false, false, q, k, v, log_alpha, beta, S0, out, S_final, nullptr, B, T, 0, H, dk,
+                        dv, C, stream, nseg, workspace, workspace_bytes, variant);
+}
+
+kda_status_t kda_chunk_fwd_ex_f32(const float *q, const float *k, const float *v, const float *log_alpha,
+                                  const float *beta, const float *S0, float *out, float *S_final, int B, int T,
+                                  int H, int dk, int dv, int C, int variant, int nseg, void *workspace,
+                                  size_t workspace_bytes, void *stream)
+{
+    return chunk_common(true, false, q, k, v, log_alpha, beta, S0, out, S_final, nullptr, B, T, 0, H, dk,
+                        dv, C, stream, nseg, workspace, workspace_bytes, variant);
+}
+
+kda_status_t kda_chunk_fwd_varlen_ex(const void *q, const void *k, const void *v, const float *log_alpha,
+                                     const float *beta, const float *S0, void *out, float *S_final,
+                                     const int32_t *cu_seqlens, int N, int T_total, int H, int dk, int dv, int C,
+                                     int variant, int nseg, void *workspace, size_t workspace_bytes,
+                                     void *stream)
+{
+    return chunk_common(false, true, q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N, 0, T_total,
+                        H, dk, dv, C, stream, nseg, workspace, workspace_bytes, variant);
+}
+
+kda_status_t kda_chunk_fwd_varlen_ex_f32(const float *q, const float *k, const float *v,
+                                         const float *log_alpha, const float *beta, const float *S0,
+                                         float *out, float *S_final, const int32_t *cu_seqlens, int N,
+                                         int T_total, int H, int dk, int dv, int C, int variant, int nseg,
+                                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    return chunk_common(true, true, q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N, 0, T_total,
+                        H, dk, dv, C, stream, nseg, workspace, workspace_bytes, variant);
+}
+
+kda_status_t kda_recurrent_fwd_ex(const void *q, const void *k, const void *v, const float *log_alpha,
+                                  const float *beta, float *S, void *out, int N, int T, int H, int dk, int dv,
+                                  int variant, void *stream)
+{
+    return step_common(false, q, k, v, log_alpha, beta, S, out, N, H, dk, dv, stream, T, true, variant);
+}
+
+kda_status_t kda_recurrent_fwd_ex_f32(const float *q, const float *k, const float *v, const float *log_alpha,
+                                      const float *beta, float *S, float *out, int N, int T, int H, int dk,
+                                      int dv, int variant, void *stream)
+{
+    return step_common(true, q, k, v, log_alpha, beta, S, out, N, H, dk, dv, stream, T, true, variant);
 }
 
 size_t kda_chunk_segmented_workspace_bytes(int nseq, int H, int dk, int dv, int nseg)

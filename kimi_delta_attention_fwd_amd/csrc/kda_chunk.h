@@ -284,6 +284,11 @@ struct ChunkCfg {
     static_assert((NSEG & (NSEG - 1)) == 0, "segment scan over a power of two");
 };
 
+// Variants (uniform arguments, read only when VAR): gate 0 = per-channel log_alpha [.., H, DK],
+// 1 = one log_alpha per token and head [.., H] shared by all key channels,
+// 2 = no decay (log_alpha not read); add = 1 replaces the delta write by the
+// additive one (e = beta v: no prediction, A = 0, E = R = beta V).
+//
 // MAP = false: the prefill itself.  With nsegs > 1 each workgroup runs one of
 // nsegs consecutive segments of its sequence's chunks, from the incoming state
 // seg_start[(head, seg)] (segment 0 included, which holds S0); only the last
@@ -293,14 +298,16 @@ struct ChunkCfg {
 // the dv real rows start at zero.  After the segment the real rows hold N and
 // the virtual rows M of S_end = S_start M + N, written to seg_map[(head, seg)];
 // no output is written and q is not read.
-template <typename In, int DK, int BV, int C, bool MAP>
+template <typename In, int DK, int BV, int C, bool MAP, bool VAR>
 __global__ void __launch_bounds__((ChunkCfg<In, DK, BV, C>::NT), 1)
 chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
                  const float *__restrict__ log_alpha, const float *__restrict__ beta,
                  const float *S0, In *__restrict__ out, float *S_final,
                  const int *__restrict__ cu_seqlens, int T, int H, int dv, int xcd_map,
-                 int nsegs, const float *seg_start, float *seg_map)
+                 int nsegs, const float *seg_start, float *seg_map, int gate_arg, int add_arg)
 {
+    // the plain recurrence (VAR = false) has the variant arguments folded away
+    const int gate = VAR ? gate_arg : 0, add = VAR ? add_arg : 0;
     typedef ChunkCfg<In, DK, BV, C> K;
     typedef typename V4T<In>::type V4;
     constexpr int NB = K::NB, NDK = K::NDK, PK = K::PK, PC = K::PC, PT = K::PT, RS = K::RS;
@@ -439,9 +446,19 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         const int voff_in = r0 * rowb_in + c0 * (int)sizeof(In), voff_f = r0 * rowb_f + c0 * 4;
         auto chunk_valid = [&](long t0) { return (unsigned)((len - t0 < C) ? len - t0 : C); };
         auto prefetch_g = [&](long t0) __attribute__((always_inline)) {
-            const __amdgpu_buffer_rsrc_t rg = buf_rsrc(log_alpha + (hrow + t0 * H) * DK, chunk_valid(t0) * rowb_f);
+            if (gate == 1) {   // one value per token, broadcast to the lane's 4 channels
+                const __amdgpu_buffer_rsrc_t rg = buf_rsrc(log_alpha + hrow + t0 * H, chunk_valid(t0) * H * 4);
 #pragma unroll
-            for (int i = 0; i < RS; ++i) gr[i] = buf_load<f32x4>(rg, voff_f, i * rowb_f);
+                for (int i = 0; i < RS; ++i) {
+                    const float x = buf_load<float>(rg, r0 * H * 4, i * H * 4);
+                    gr[i] = f32x4{x, x, x, x};
+                }
+            } else {           // gate 2: an empty descriptor, every load reads 0
+                const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gate == 0 ? log_alpha + (hrow + t0 * H) * DK : beta,
+                                                          gate == 0 ? chunk_valid(t0) * rowb_f : 0u);
+#pragma unroll
+                for (int i = 0; i < RS; ++i) gr[i] = buf_load<f32x4>(rg, voff_f, i * rowb_f);
+            }
         };
         auto prefetch_q = [&](long t0) __attribute__((always_inline)) {
             if constexpr (MAP) return;
@@ -597,6 +614,12 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         //      when there is a single state wave, which then also leaves the
         //      off-diagonal A tiles here)
         auto stage_b = [&](long ch) __attribute__((always_inline)) {
+            if (add) {   // no A: only the diagonal P tiles of a single state wave
+                if constexpr (K::NBV == 1 && !MAP) {
+                    for (int p = xw; p < NB; p += K::NXW) tile_job(ch, p, false, true);
+                }
+                return;
+            }
             for (int p = xw; p < (K::NBV == 1 ? K::NPAIR : NB); p += K::NXW) {
                 if (p < NB && !K::F32) {
                     // D_p = (I + L)^{-1} for the strictly lower diagonal tile L, as
@@ -748,7 +771,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 const int s = r * K::NBV + ((r & 1) ? K::NBV - 1 - cb : cb);
                 if (s < NJOB) {
                     const int p = s < K::NOFF ? NB + s : s - K::NOFF;
-                    tile_job(ch, p, K::NBV >= 2 && p >= NB, !MAP);
+                    tile_job(ch, p, K::NBV >= 2 && p >= NB && !add, !MAP);
                 }
             }
         };
@@ -772,10 +795,10 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 V4 ak[NDK], bq[NDK];
 #pragma unroll
                 for (int ct = 0; ct < NDK; ++ct) {
-                    ak[ct] = *(const V4 *)(Kr + (16 * I + n) * PK + 16 * ct + 4 * g);
+                    if (!add) ak[ct] = *(const V4 *)(Kr + (16 * I + n) * PK + 16 * ct + 4 * g);
                     if constexpr (!MAP) bq[ct] = *(const V4 *)(Qr + (16 * I + n) * PK + 16 * ct + 4 * g);
                 }
-                R[I] = mma_tiles<K::KD, In, NDK>(zero4(), ak, ss);    // [16I + 4g + i][n]
+                R[I] = add ? zero4() : mma_tiles<K::KD, In, NDK>(zero4(), ak, ss);    // [16I + 4g + i][n]
                 if constexpr (!MAP) O1[I] = mma_tiles<K::KD, In, NDK>(zero4(), ss, bq);   // [v = 4g + i][16I + n]
             };
             if (allfast) {
@@ -809,18 +832,23 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             }
             if (ch + 1 < nch) prefetch_v(t0 + C);
 
-            // ---- (I + A) E = R, block forward substitution
+            // ---- (I + A) E = R, block forward substitution (additive write: E = R)
+            if (add) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                f32x4 y = zero4();
+                for (int b = 0; b < NB; ++b) Eb[b] = to_op<In>(R[b]);
+            } else {
 #pragma unroll
-                for (int J = 0; J < b; ++J) {
-                    const f32x4 a = *(const f32x4 *)(sA + tile_index(NB, b, J) * 16 * PT + n * PT + 4 * g);
-                    y = mma_fp32a<In>(y, a, Eb[J]);
+                for (int b = 0; b < NB; ++b) {
+                    f32x4 y = zero4();
+#pragma unroll
+                    for (int J = 0; J < b; ++J) {
+                        const f32x4 a = *(const f32x4 *)(sA + tile_index(NB, b, J) * 16 * PT + n * PT + 4 * g);
+                        y = mma_fp32a<In>(y, a, Eb[J]);
+                    }
+                    const f32x4 d = *(const f32x4 *)(sA + b * 16 * PT + n * PT + 4 * g);
+                    const f32x4 e = mma_fp32ab<In>(d, R[b] - y);
+                    Eb[b] = to_op<In>(e);
                 }
-                const f32x4 d = *(const f32x4 *)(sA + b * 16 * PT + n * PT + 4 * g);
-                const f32x4 e = mma_fp32ab<In>(d, R[b] - y);
-                Eb[b] = to_op<In>(e);
             }
 
             // ---- O^T = (Qbar S^T)^T + E^T P^T, written as O rows (rows past the end dropped)
@@ -899,19 +927,27 @@ __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const
 
 // One pass of the chunk kernel over nsu segments per sequence and nrows state
 // rows per head.
-template <typename In, int DK, int BV, int C, bool MAP>
-hipError_t launch_chunk_pass(const ChunkArgs &a, int nsu, int nrows)
+template <typename In, int DK, int BV, int C, bool MAP, bool VAR>
+hipError_t launch_chunk_pass_v(const ChunkArgs &a, int nsu, int nrows)
 {
     typedef ChunkCfg<In, DK, BV, C> K;
     const long units = (long)a.nseq * a.H * nsu;
     const long grid = units * (nrows / BV);
     if (grid == 0) return hipSuccess;
     const int xcd_map = (units % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((chunk_fwd_kernel<In, DK, BV, C, MAP>), dim3((unsigned)grid), dim3(K::NT), 0, a.stream,
-                       (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S0,
+    hipLaunchKernelGGL((chunk_fwd_kernel<In, DK, BV, C, MAP, VAR>), dim3((unsigned)grid), dim3(K::NT), 0,
+                       a.stream, (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S0,
                        (In *)a.out, a.S_final, a.cu_seqlens, a.T, a.H, a.dv, xcd_map, a.nsegs, a.seg_start,
-                       a.seg_map);
+                       a.seg_map, a.gate, a.add);
     return hipGetLastError();
+}
+
+// The same, with the kernel specialised for the plain recurrence or not.
+template <typename In, int DK, int BV, int C, bool MAP>
+hipError_t launch_chunk_pass(const ChunkArgs &a, int nsu, int nrows)
+{
+    if (a.gate != 0 || a.add != 0) return launch_chunk_pass_v<In, DK, BV, C, MAP, true>(a, nsu, nrows);
+    return launch_chunk_pass_v<In, DK, BV, C, MAP, false>(a, nsu, nrows);
 }
 
 // The whole prefill: one pass, or (nsegs > 1) the map pass over all segments

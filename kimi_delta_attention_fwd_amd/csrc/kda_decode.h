@@ -23,12 +23,28 @@
 
 namespace kda {
 
-template <typename In, int DK>
+// log decays of 4 key channels starting at element c of the token's
+// log_alpha row: per channel (gate 0), one value per token and head at index
+// tok (gate 1), or none (gate 2: alpha = 1).
+__device__ __forceinline__ f32x4 decay_logs(const float *log_alpha, long c, long tok, int gate)
+{
+    if (gate == 0) return *(const f32x4 *)(log_alpha + c);
+    if (gate == 1) {
+        const float x = log_alpha[tok];
+        return f32x4{x, x, x, x};
+    }
+    return zero4();
+}
+
+// Variants (uniform arguments, read only when VAR): gate as in decay_logs;
+// add = 1 is the additive write e = beta v (no prediction).
+template <typename In, int DK, bool VAR>
 __global__ void __launch_bounds__(256)
 decode_step_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
                    const float *__restrict__ log_alpha, const float *__restrict__ beta,
-                   float *__restrict__ S, In *__restrict__ out, int dv)
+                   float *__restrict__ S, In *__restrict__ out, int dv, int gate_arg, int add_arg)
 {
+    const int gate = VAR ? gate_arg : 0, add = VAR ? add_arg : 0;
     typedef In In4 __attribute__((ext_vector_type(4)));
     constexpr int LPR = DK / 16;          // lanes per state row, 16 floats (4 x float4) each
     constexpr int RPP = 256 / LPR;        // rows per pass of the workgroup
@@ -41,7 +57,7 @@ decode_step_kernel(const In *__restrict__ q, const In *__restrict__ k, const In 
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const long c = head * DK + 4 * (sub + LPR * u);
-        const f32x4 la = *(const f32x4 *)(log_alpha + c);
+        const f32x4 la = decay_logs(log_alpha, c, head, gate);
         const In4 kv = *(const In4 *)(k + c);
         const In4 qv = *(const In4 *)(q + c);
 #pragma unroll
@@ -77,7 +93,7 @@ decode_step_kernel(const In *__restrict__ q, const In *__restrict__ k, const In 
                     s[p][u][j] *= a[u][j];
                     pred += s[p][u][j] * kk[u][j];
                 }
-            pred = group_sum<LPR>(pred);
+            pred = add ? 0.f : group_sum<LPR>(pred);
             const float e = b * (vi[p] - pred);
             float o = 0.f;
 #pragma unroll
@@ -103,12 +119,14 @@ decode_step_kernel(const In *__restrict__ q, const In *__restrict__ k, const In 
 // the tokens).  Token t of sequence n sits at row (n T + t) H + h of the
 // [N, T, H, d] inputs.  Per token the arithmetic is the decode step's, in the
 // same order, so T = 1 matches kda_recurrent_step bit for bit.
-template <typename In, int DK>
+template <typename In, int DK, bool VAR>
 __global__ void __launch_bounds__(256)
 decode_multi_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
                     const float *__restrict__ log_alpha, const float *__restrict__ beta,
-                    float *__restrict__ S, In *__restrict__ out, int T, int H, int dv)
+                    float *__restrict__ S, In *__restrict__ out, int T, int H, int dv, int gate_arg,
+                    int add_arg)
 {
+    const int gate = VAR ? gate_arg : 0, add = VAR ? add_arg : 0;
     typedef In In4 __attribute__((ext_vector_type(4)));
     constexpr int LPR = DK / 16;
     constexpr int RPP = 256 / LPR;
@@ -133,7 +151,7 @@ decode_multi_kernel(const In *__restrict__ q, const In *__restrict__ k, const In
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const long c = tok * DK + 4 * (sub + LPR * u);
-            const f32x4 la = *(const f32x4 *)(log_alpha + c);
+            const f32x4 la = decay_logs(log_alpha, c, tok, gate);
             const In4 kv = *(const In4 *)(k + c);
             const In4 qv = *(const In4 *)(q + c);
 #pragma unroll
@@ -157,7 +175,7 @@ decode_multi_kernel(const In *__restrict__ q, const In *__restrict__ k, const In
                         s[p][u][j] *= a[u][j];
                         pred += s[p][u][j] * kk[u][j];
                     }
-                pred = group_sum<LPR>(pred);
+                pred = add ? 0.f : group_sum<LPR>(pred);
                 const float e = b * (vi - pred);
                 float o = 0.f;
 #pragma unroll
@@ -188,9 +206,14 @@ hipError_t launch_decode_multi_t(const DecodeArgs &a, int T)
 {
     const long grid = (long)a.N * a.H;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_multi_kernel<In, DK>), dim3((unsigned)grid), dim3(256), 0, a.stream,
-                       (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S,
-                       (In *)a.out, T, a.H, a.dv);
+    if (a.gate != 0 || a.add != 0)
+        hipLaunchKernelGGL((decode_multi_kernel<In, DK, true>), dim3((unsigned)grid), dim3(256), 0, a.stream,
+                           (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S,
+                           (In *)a.out, T, a.H, a.dv, a.gate, a.add);
+    else
+        hipLaunchKernelGGL((decode_multi_kernel<In, DK, false>), dim3((unsigned)grid), dim3(256), 0, a.stream,
+                           (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S,
+                           (In *)a.out, T, a.H, a.dv, 0, 0);
     return hipGetLastError();
 }
 
@@ -199,9 +222,14 @@ hipError_t launch_decode_t(const DecodeArgs &a)
 {
     const int grid = a.N * a.H;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_step_kernel<In, DK>), dim3(grid), dim3(256), 0, a.stream,
-                       (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S,
-                       (In *)a.out, a.dv);
+    if (a.gate != 0 || a.add != 0)
+        hipLaunchKernelGGL((decode_step_kernel<In, DK, true>), dim3(grid), dim3(256), 0, a.stream,
+                           (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S,
+                           (In *)a.out, a.dv, a.gate, a.add);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<In, DK, false>), dim3(grid), dim3(256), 0, a.stream,
+                           (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S,
+                           (In *)a.out, a.dv, 0, 0);
     return hipGetLastError();
 }
 

@@ -17,6 +17,9 @@ struct ChunkArgs {
     // seg_map [nseq*H][nsegs-1][dv+dk][dk] and seg_start [nseq*H][nsegs][dv][dk] fp32
     int nsegs;
     float *seg_map, *seg_start;
+    // variant: gate 0 per channel, 1 scalar per token and head, 2 none;
+    // add 1 = additive write
+    int gate, add;
     hipStream_t stream;
 };
 
@@ -26,6 +29,7 @@ struct DecodeArgs {
     float *S;
     void *out;
     int N, H, dk, dv;
+    int gate, add;   // as in ChunkArgs
     hipStream_t stream;
 };
 

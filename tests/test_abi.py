@@ -246,3 +246,22 @@ def test_recurrent_fwd_validation(lib):
     assert multi(out=A + 4 * 2 * 128 * 2 * 2 - 16) == 6
     assert lib.kda_recurrent_fwd_f32(A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 8 * MB, A + 64 * MB,
                                      4, 2, 2, 16, 256, None) == 3
+
+
+def test_variant_validation(lib):
+    P = A
+    def ex(variant, la=A + 192 * MB, nseg=1, ws=None, wsb=0):
+        return lib.kda_chunk_fwd_ex(A, A + 64 * MB, A + 128 * MB, la, A + 256 * MB, None, A + 320 * MB,
+                                    A + 384 * MB, 2, 100, 4, 64, 64, 64, variant, nseg, ws, wsb, None)
+    assert ex(3) == 2 and ex(8) == 2 and ex(-1) == 2
+    assert "variant" in kda.kda_last_error()
+    assert ex(0, la=None) == 1                  # the per-channel gate needs log_alpha
+    assert ex(1, la=None) == 1                  # so does the scalar gate
+    assert ex(1, la=A + 192 * MB + 4) != 4      # 4-byte alignment is enough for one gate per token
+    assert ex(0, la=A + 192 * MB + 4) == 4
+    assert ex(2 | 4, la=A + 192 * MB + 2, nseg=0) == 2   # log_alpha not read with no gate; nseg still checked
+    assert kda.variant("scalar", "add") == 5 and kda.variant() == 0 and kda.variant("none") == 2
+    def rex(variant, la=A + 3 * MB):
+        return lib.kda_recurrent_fwd_ex(A, A + MB, A + 2 * MB, la, A + 4 * MB, A + 8 * MB, A + 64 * MB,
+                                        4, 0, 2, 128, 128, variant, None)
+    assert rex(3) == 2 and rex(2, la=None) == 0

@@ -332,6 +332,81 @@ def test_segmented_is_deterministic(dev):
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
+# ---------------------------------------------------------------- variants (gate, write)
+VARIANTS = [("scalar", "delta"), ("none", "delta"), ("channel", "add"), ("scalar", "add"), ("none", "add")]
+
+
+def variant_inputs(p, gate):
+    """The log_alpha argument of a variant and the per-channel log_alpha the
+    oracle sees for it (a scalar gate broadcast to every key channel, or 0)."""
+    if gate == "channel":
+        return p.log_alpha, p.log_alpha
+    if gate == "scalar":
+        la = p.log_alpha[..., 0].contiguous()
+        return la, la.unsqueeze(-1).expand_as(p.log_alpha).contiguous()
+    return None, torch.zeros_like(p.log_alpha)
+
+
+def oracle_variant(p, la_full, write, S0=None):
+    return oracle.forward(f64(p.q), f64(p.k), f64(p.v), f64(la_full), f64(p.beta),
+                          S0=f64(p.S0 if S0 is None else S0), write=write)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("gate,write", VARIANTS)
+def test_chunk_variants(dev, gate, write, dtype):
+    B, T, H, dk, dv = 2, 200, 2, 64, 64
+    C = 64 if dtype == "bf16" else 32
+    note(f"case chunk variant gate={gate} write={write} B{B} T{T} H{H} d{dk} {dtype} C{C}")
+    p = kda_synth.prefill(B, T, H, dk, dv, dtype=dtype, s0_sigma=0.1, seed=81, device=dev)
+    la, la_full = variant_inputs(p, gate)
+    o_ref, s_ref = oracle_variant(p, la_full, write)
+    for segments in (1, 3):
+        out, sf = kda.chunk_fwd(p.q, p.k, p.v, la, p.beta, S0=p.S0, C=C, segments=segments, gate=gate, write=write)
+        torch.cuda.synchronize()
+        assert_close(f"{gate}/{write} segments={segments}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+
+
+def test_chunk_variant_varlen_and_wide_heads(dev):
+    lengths = [130, 0, 77, 200]
+    for gate, write in (("scalar", "delta"), ("channel", "add")):
+        note(f"case varlen variant gate={gate} write={write} lengths {lengths} H2 dk128 dv128 bf16")
+        p = kda_synth.prefill_varlen(lengths, 2, 128, 128, dtype="bf16", s0_sigma=0.1, seed=83, device=dev)
+        la, la_full = variant_inputs(p, gate)
+        T_total, N = sum(lengths), len(lengths)
+        out = torch.empty_like(p.v)
+        sf = torch.empty((N, 2, 128, 128), dtype=torch.float32, device=dev)
+        kda.kda_chunk_fwd_varlen_ex(p.q, p.k, p.v, la, p.beta, p.S0, out, sf, p.cu_seqlens, N, T_total, 2, 128,
+                                    128, 64, kda.variant(gate, write))
+        torch.cuda.synchronize()
+        o_ref, s_ref = oracle.forward_varlen(f64(p.q), f64(p.k), f64(p.v), f64(la_full), f64(p.beta),
+                                             np.array(p.cu_host), S0=f64(p.S0), write=write)
+        assert_close(f"varlen {gate}/{write}", f64(out), f64(sf), o_ref, s_ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("gate,write", VARIANTS)
+def test_decode_variants(dev, gate, write):
+    for dtype in ("bf16", "f32"):
+        N, T, H, dk, dv = 3, 5, 2, 128, 64
+        note(f"case decode variant gate={gate} write={write} N{N} T{T} H{H} dk{dk} dv{dv} {dtype}")
+        p = kda_synth.prefill(N, T, H, dk, dv, dtype=dtype, s0_sigma=0.1, seed=85, device=dev)
+        la, la_full = variant_inputs(p, gate)
+        o_ref, s_ref = oracle_variant(p, la_full, write)
+        S = p.S0.clone()
+        out = kda.recurrent_fwd(p.q, p.k, p.v, la, p.beta, S, gate=gate, write=write)
+        torch.cuda.synchronize()
+        assert_close(f"decode {gate}/{write} T={T}", f64(out), f64(S), o_ref, s_ref, TOL[dtype])
+        # one token per launch through the same entry point (the step kernel)
+        S = p.S0.clone()
+        outs = [kda.recurrent_fwd(p.q[:, t:t + 1].contiguous(), p.k[:, t:t + 1].contiguous(),
+                                  p.v[:, t:t + 1].contiguous(),
+                                  None if la is None else la[:, t:t + 1].contiguous(),
+                                  p.beta[:, t:t + 1].contiguous(), S, gate=gate, write=write) for t in range(T)]
+        torch.cuda.synchronize()
+        assert_close(f"decode {gate}/{write} T=1 x{T}", f64(torch.cat(outs, dim=1)), f64(S), o_ref, s_ref,
+                     TOL[dtype])
+
+
 # ---------------------------------------------------------------- packed variable length
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_varlen_small(dev, dtype):
