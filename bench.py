@@ -11,6 +11,8 @@ clocks settle (they ramp up over the first ~30 ms of load).
 Extra fields measure the other entry points on their own workloads:
   decode        256 sequences x 32 heads, 1024 one-token steps (steps/s)
   decode_multi  the same sizes, 4 tokens per sequence and launch (tokens/s)
+  fused_prep    mid sizes from raw q, k and bf16 gate pre-activations, against
+                separate preparation passes feeding the plain kernel (ms)
   long_context  B=1, H=16, T=65536 with an initial state (tokens/s)
   varlen        8 packed sequences of U[2048, 16384] tokens x 16 heads (tokens/s)
 
@@ -211,6 +213,42 @@ def bench_decode_multi(args, torch, kda, kda_synth, stream, T=4, launches=50):
                               algorithmic_bytes=nbytes))
 
 
+def bench_prep(args, torch, kda, kda_synth, stream, steps=10):
+    """Fused input preparation on the mid sizes: raw q, k and bf16 gate
+    pre-activations into kda_chunk_fwd_ex (KDA_INPUT_RAW), against the plain
+    kernel fed by separate preparation passes (torch ops: L2 normalisation of
+    q and k, -softplus of g in fp32), timed the same way."""
+    w = kda_synth.WORKLOADS["mid"]
+    B, T, H, dk, dv, C = w["B"], w["T"], w["H"], w["dk"], w["dv"], w["C"]
+    p = kda_synth.prefill_raw(B, T, H, dk, dv, dtype="bf16", g_mu=w["g_mu"], g_sigma=w["g_sigma"],
+                              seed=kda_synth.SEEDS["mid"], device="cuda")
+    out = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device="cuda")
+    sf = torch.empty((B, H, dv, dk), dtype=torch.float32, device="cuda")
+    h = stream.cuda_stream
+    raw = kda.variant(raw=True)
+
+    def fused():
+        kda.kda_chunk_fwd_ex(p.q, p.k, p.v, p.log_alpha, p.beta, None, out, sf, B, T, H, dk, dv, C, raw, 1, None,
+                             0, h)
+
+    def separate():
+        qf, kf = p.q.float(), p.k.float()
+        qn = (qf / qf.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        kn = (kf / kf.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        la = -torch.nn.functional.softplus(p.log_alpha.float())
+        kda.kda_chunk_fwd(qn, kn, p.v, la, p.beta, None, out, sf, B, T, H, dk, dv, C, h)
+
+    _, kms_fused = time_launches(fused, stream, steps, 2, torch)
+    _, kms_sep = time_launches(separate, stream, steps, 2, torch)
+    ntok = B * T * H
+    fused_bytes = ntok * (2 * (2 * dk + dv) + 2 * dk + 4 + 2 * dv) + 4 * dk * dv * B * H
+    del p, out, sf
+    return dict(workload="mid sizes (B=4 H=32 T=8192 d=128, C=64) with raw q, k and bf16 gate pre-activations",
+                fused_kernel_ms=kms_fused, separate_prep_plus_kernel_ms=kms_sep,
+                fused_algorithmic_bytes=fused_bytes,
+                fused_hbm_frac=round(fused_bytes / (kms_fused * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+
+
 def bench_long(args, torch, kda, kda_synth, stream, steps=3):
     w = kda_synth.WORKLOADS["long"]
     p = kda_synth.workload("long", device="cuda")
@@ -292,7 +330,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--extras", default="decode,multi,long,varlen",
+    ap.add_argument("--extras", default="decode,multi,long,varlen,prep",
                     help="comma-separated extra workloads to run after the mid prefill "
                          "(decode, long, varlen; 'none' for the mid prefill only)")
     ap.add_argument("--no-extras", action="store_true", help="same as --extras none")
@@ -357,11 +395,12 @@ def main():
     del p_mid
     torch.cuda.empty_cache()
     extras = set() if args.no_extras or args.extras == "none" else set(args.extras.split(","))
-    unknown = extras - {"decode", "multi", "long", "varlen"}
+    unknown = extras - {"decode", "multi", "long", "varlen", "prep"}
     if unknown:
         raise SystemExit(f"unknown --extras entries: {sorted(unknown)}")
     for name, key, fn in (("decode", "decode", bench_decode), ("multi", "decode_multi", bench_decode_multi),
-                          ("long", "long_context", bench_long), ("varlen", "varlen", bench_varlen)):
+                          ("long", "long_context", bench_long), ("varlen", "varlen", bench_varlen),
+                          ("prep", "fused_prep", bench_prep)):
         if name in extras:
             result[key] = fn(args, torch, kda, kda_synth, stream)
             torch.cuda.empty_cache()

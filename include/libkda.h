@@ -207,15 +207,25 @@ kda_status_t kda_chunk_fwd_varlen_segmented_f32(const float *q, const float *k, 
  *   write  KDA_WRITE_DELTA   e_t = beta_t (v_t - S~_t k_t)   (the delta rule)
  *          KDA_WRITE_ADD     e_t = beta_t v_t, S_t = S~_t + beta_t v_t k_t^T
  *                            (linear attention, GLA; beta = 1 gives them exactly)
- * variant = gate | write; anything else is KDA_ERR_BAD_SHAPE.  The plain entry
- * points are variant 0 (KDA_GATE_CHANNEL | KDA_WRITE_DELTA).
+ *   input  KDA_INPUT_RAW     fused input preparation: q and k arrive as they
+ *                            come out of their projections and are L2-normalised
+ *                            per token inside the kernels (a zero row stays
+ *                            zero; "Kimi K3 notes 1: KDA" page, sect. 4), and
+ *                            the gate argument holds pre-activations g in the
+ *                            input type (bf16 in the bf16 entry points, fp32 in
+ *                            the _f32 ones) with log_alpha = -softplus(g).  For
+ *                            bf16 this halves the gate's HBM bytes and removes
+ *                            the separate normalisation and softplus passes.
+ * variant = gate | write | input; anything else is KDA_ERR_BAD_SHAPE.  The
+ * plain entry points are variant 0 (KDA_GATE_CHANNEL | KDA_WRITE_DELTA).
  */
 enum {
     KDA_GATE_CHANNEL = 0,
     KDA_GATE_SCALAR = 1,
     KDA_GATE_NONE = 2,
     KDA_WRITE_DELTA = 0,
-    KDA_WRITE_ADD = 4
+    KDA_WRITE_ADD = 4,
+    KDA_INPUT_RAW = 8
 };
 
 /* Chunk prefill with a variant and an optional segment-parallel schedule

@@ -104,6 +104,28 @@ def prefill(B, T, H, dk, dv, *, dtype="bf16", g_mu=-4.0, g_sigma=1.5, beta="sigm
     return Prefill(q, k, v, log_alpha, be, S0)
 
 
+def prefill_raw(B, T, H, dk, dv, *, dtype="bf16", g_mu=-4.0, g_sigma=1.5, q_sigma=1.0, k_sigma=1.0,
+                beta="sigmoid", s0_sigma=None, seed=0, device="cuda") -> Prefill:
+    """Dense inputs as they come out of the projections, for the fused input
+    preparation: q ~ N(0, q_sigma), k ~ N(0, k_sigma) NOT normalised, and the
+    gate pre-activations g ~ N(g_mu, g_sigma) in the input type in place of
+    log_alpha (the `log_alpha` field holds g)."""
+    g = _gen(seed, device)
+    dt = DTYPES[dtype]
+    q = (torch.randn((B, T, H, dk), generator=g, device=device, dtype=torch.float32) * q_sigma).to(dt)
+    k = (torch.randn((B, T, H, dk), generator=g, device=device, dtype=torch.float32) * k_sigma).to(dt)
+    v = torch.randn((B, T, H, dv), generator=g, device=device, dtype=torch.float32).to(dt)
+    if beta == "sigmoid":
+        be = torch.sigmoid(torch.randn((B, T, H), generator=g, device=device, dtype=torch.float32))
+    else:
+        be = torch.rand((B, T, H), generator=g, device=device, dtype=torch.float32)
+    pre = (torch.randn((B, T, H, dk), generator=g, device=device, dtype=torch.float32) * g_sigma + g_mu).to(dt)
+    S0 = None
+    if s0_sigma is not None:
+        S0 = torch.randn((B, H, dv, dk), generator=g, device=device, dtype=torch.float32) * s0_sigma
+    return Prefill(q, k, v, pre, be, S0)
+
+
 def prefill_varlen(lengths, H, dk, dv, *, dtype="bf16", g_mu=-4.0, g_sigma=1.5, beta="sigmoid", s0_sigma=0.1,
                    seed=0, device="cuda") -> Prefill:
     """Packed [1, T_total, H, d] inputs for the given sequence lengths."""

@@ -217,10 +217,11 @@ GATES = {"channel": 0, "scalar": 1, "none": 2}
 WRITES = {"delta": 0, "add": 4}
 
 
-def variant(gate="channel", write="delta") -> int:
+def variant(gate="channel", write="delta", raw=False) -> int:
     """Variant selector of the *_ex entry points: gate "channel" (KDA, GLA),
-    "scalar" (one decay per token and head) or "none"; write "delta" or "add"."""
-    return GATES[gate] | WRITES[write]
+    "scalar" (one decay per token and head) or "none"; write "delta" or "add";
+    raw=True for un-normalised q, k and gate pre-activations g (fused prep)."""
+    return GATES[gate] | WRITES[write] | (8 if raw else 0)
 
 
 def kda_chunk_fwd_ex(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, dk, dv, C, variant, nseg=1,
@@ -299,13 +300,14 @@ def _workspace(nseq, H, dk, dv, nseg, device):
 
 
 def chunk_fwd(q, k, v, log_alpha, beta, S0=None, C=64, output_final_state=True, stream=None, segments="auto",
-              gate="channel", write="delta"):
+              gate="channel", write="delta", raw=False):
     """Chunk prefill of a dense batch.  Returns ``(out, S_final or None)``.
 
     ``segments``: 1 for the single pass, n > 1 for the segment-parallel
     schedule with n segments per sequence, "auto" for the library's choice.
-    ``gate`` / ``write`` select a variant (see :func:`variant`); with
-    gate="scalar" log_alpha is [B, T, H], with gate="none" it may be None.
+    ``gate`` / ``write`` / ``raw`` select a variant (see :func:`variant`); with
+    gate="scalar" log_alpha is [B, T, H], with gate="none" it may be None;
+    with raw=True it holds the pre-activations g in q's dtype.
     """
     import torch
     f32 = _mode(q)
@@ -314,7 +316,7 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, C=64, output_final_state=True, 
     out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     sf = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device) if output_final_state else None
     nseg = kda_chunk_auto_segments(B, T, H, dk, dv, C, f32) if segments == "auto" else int(segments)
-    var = variant(gate, write)
+    var = variant(gate, write, raw)
     if var != 0:
         ws, nbytes = _workspace(B, H, dk, dv, nseg, q.device) if nseg > 1 else (None, 0)
         fn = kda_chunk_fwd_ex_f32 if f32 else kda_chunk_fwd_ex
@@ -366,7 +368,7 @@ def recurrent_step(q, k, v, log_alpha, beta, S, out=None, stream=None):
     return out
 
 
-def recurrent_fwd(q, k, v, log_alpha, beta, S, out=None, stream=None, gate="channel", write="delta"):
+def recurrent_fwd(q, k, v, log_alpha, beta, S, out=None, stream=None, gate="channel", write="delta", raw=False):
     """T decode tokens per sequence on [N, T, H, d] tensors in one launch; S
     [N, H, dv, dk] fp32 is updated in place.  Returns out [N, T, H, dv]."""
     import torch
@@ -375,7 +377,7 @@ def recurrent_fwd(q, k, v, log_alpha, beta, S, out=None, stream=None, gate="chan
     dv = v.shape[-1]
     if out is None:
         out = torch.empty((N, T, H, dv), dtype=q.dtype, device=q.device)
-    var = variant(gate, write)
+    var = variant(gate, write, raw)
     if var != 0:
         fn = kda_recurrent_fwd_ex_f32 if f32 else kda_recurrent_fwd_ex
         fn(q, k, v, log_alpha, beta, S, out, N, T, H, dk, dv, var, stream)

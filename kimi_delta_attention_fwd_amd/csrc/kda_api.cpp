@@ -95,8 +95,27 @@ int choose_bv(bool f32, int dk, int dv, int C, long units, int maxbv = 64)
 constexpr int kMaxSegments = 1024;
 
 // Variant selector of the *_ex entry points: bits 0-1 the gate (0 per
-// channel, 1 one value per token and head, 2 none), bit 2 the additive write.
-bool valid_variant(int variant) { return (variant & ~7) == 0 && (variant & 3) != 3; }
+// channel, 1 one value per token and head, 2 none), bit 2 the additive write,
+// bit 3 raw inputs (q, k normalised in the kernel, gate pre-activations).
+bool valid_variant(int variant) { return (variant & ~15) == 0 && (variant & 3) != 3; }
+
+// Bytes and alignment of the gate argument: fp32 log_alpha, or with raw
+// inputs g in the input type (es bytes per element).
+uint64_t gate_bytes(int variant, uint64_t ntok_heads, int dk, uint64_t es)
+{
+    const uint64_t e = (variant & 8) ? es : 4;
+    switch (variant & 3) {
+    case 0: return ntok_heads * (uint64_t)dk * e;
+    case 1: return ntok_heads * e;
+    default: return 0;
+    }
+}
+
+uintptr_t gate_align(int variant, uint64_t es)
+{
+    if ((variant & 3) == 0) return 16;
+    return (variant & 8) ? es : 4;
+}
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
@@ -187,24 +206,24 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
         (uint64_t)H * 128u * 64u * 4u > (uint64_t)INT32_MAX ||
         nheads * (uint64_t)nseg * (uint64_t)(dv + dk) / 16u > (uint64_t)INT32_MAX)
         return fail(KDA_ERR_BAD_SHAPE, "problem too large");
-    const uint64_t es = f32 ? 4 : 2;
     const uint64_t nk = ntok * H * dk, nv = ntok * H * dv, nb = ntok * H, ns = nheads * dv * dk;
 
     if (ntok > 0 && (!q || !k || !v || (gate != 2 && !log_alpha) || !beta || !out))
         return fail(KDA_ERR_NULL_POINTER, "q, k, v, log_alpha, beta and out are required when there are tokens");
     if (gate == 2) log_alpha = nullptr;   // not read
     if (varlen && nseq > 0 && !cu_seqlens) return fail(KDA_ERR_NULL_POINTER, "cu_seqlens is required");
+    const uint64_t es = f32 ? 4 : 2;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-        !aligned(log_alpha, gate == 0 ? 16 : 4))
-        return fail(KDA_ERR_MISALIGNED, "q, k, v, out and log_alpha must be 16-byte aligned (log_alpha 4 with "
-                                         "one gate per token)");
+        !aligned(log_alpha, gate_align(variant, es)))
+        return fail(KDA_ERR_MISALIGNED, "q, k, v, out and log_alpha must be 16-byte aligned (log_alpha: its "
+                                         "element size with one gate per token)");
     if (!aligned(S0, 16) || !aligned(S_final, 16))
         return fail(KDA_ERR_MISALIGNED, "S0 and S_final must be 16-byte aligned");
     if (!aligned(beta, 4) || !aligned(cu_seqlens, 4))
         return fail(KDA_ERR_MISALIGNED, "beta and cu_seqlens must be 4-byte aligned");
 
     const Buf ins[] = {{q, nk * es, "q"}, {k, nk * es, "k"}, {v, nv * es, "v"},
-                       {log_alpha, gate == 0 ? nk * 4 : nb * 4, "log_alpha"}, {beta, nb * 4, "beta"},
+                       {log_alpha, gate_bytes(variant, nb, dk, es), "log_alpha"}, {beta, nb * 4, "beta"},
                        {cu_seqlens, varlen ? (uint64_t)(nseq + 1) * 4 : 0, "cu_seqlens"}};
     kda_status_t st = check_aliasing(Buf{out, nv * es, "out"}, ins, 6,
                                      Buf{S_final, S_final ? ns * 4 : 0, "S_final"},
@@ -251,6 +270,7 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
     a.nsegs = nseg;
     a.gate = gate;
     a.add = (variant >> 2) & 1;
+    a.prep = (variant >> 3) & 1;
     a.seg_map = nseg > 1 ? (float *)workspace : nullptr;
     a.seg_start = nseg > 1 ? (float *)((char *)workspace + seg_map_bytes(nheads, dk, dv, nseg)) : nullptr;
     a.stream = (hipStream_t)stream;
@@ -279,14 +299,14 @@ kda_status_t step_common(bool f32, const void *q, const void *k, const void *v, 
     if (!q || !k || !v || (gate != 2 && !log_alpha) || !beta || !S || !out)
         return fail(KDA_ERR_NULL_POINTER, "q, k, v, log_alpha, beta, S and out are required");
     if (gate == 2) log_alpha = nullptr;   // not read
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-        !aligned(log_alpha, gate == 0 ? 16 : 4) || !aligned(S, 16))
-        return fail(KDA_ERR_MISALIGNED, "q, k, v, out, log_alpha and S must be 16-byte aligned (log_alpha 4 "
-                                         "with one gate per token)");
-    if (!aligned(beta, 4)) return fail(KDA_ERR_MISALIGNED, "beta must be 4-byte aligned");
     const uint64_t es = f32 ? 4 : 2;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(log_alpha, gate_align(variant, es)) || !aligned(S, 16))
+        return fail(KDA_ERR_MISALIGNED, "q, k, v, out, log_alpha and S must be 16-byte aligned (log_alpha: its "
+                                         "element size with one gate per token)");
+    if (!aligned(beta, 4)) return fail(KDA_ERR_MISALIGNED, "beta must be 4-byte aligned");
     const Buf ins[] = {{q, ntok * dk * es, "q"}, {k, ntok * dk * es, "k"}, {v, ntok * dv * es, "v"},
-                       {log_alpha, gate == 0 ? ntok * dk * 4 : ntok * 4, "log_alpha"}, {beta, ntok * 4, "beta"}};
+                       {log_alpha, gate_bytes(variant, ntok, dk, es), "log_alpha"}, {beta, ntok * 4, "beta"}};
     const Buf sb{S, nheads * dv * dk * 4, "S"};
     kda_status_t st = check_aliasing(Buf{out, ntok * dv * es, "out"}, ins, 5, sb, sb);
     if (st != KDA_OK) return st;
@@ -305,6 +325,7 @@ kda_status_t step_common(bool f32, const void *q, const void *k, const void *v, 
     a.dv = dv;
     a.gate = gate;
     a.add = (variant >> 2) & 1;
+    a.prep = (variant >> 3) & 1;
     a.stream = (hipStream_t)stream;
     const hipError_t e = (multi && T > 1) ? kda::launch_decode_multi(a, T, f32) : kda::launch_decode(a, f32);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode kernel launch failed: %s", hipGetErrorString(e));

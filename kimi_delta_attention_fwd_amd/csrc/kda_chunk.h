@@ -175,7 +175,8 @@ __device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, int voff, int so
 {
     if constexpr (sizeof(T) == 16) return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
     else if constexpr (sizeof(T) == 8) return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
-    else return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    else if constexpr (sizeof(T) == 4) return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    else return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
 }
 template <typename T>
 __device__ __forceinline__ void buf_store(T v, __amdgpu_buffer_rsrc_t r, int voff, int soff)
@@ -205,6 +206,7 @@ __device__ __forceinline__ void store_row_swz(OpT *base, int row, int col0, int 
 // results under the fp32 normal range may flush to zero, which only drops
 // contributions that are that small.
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
 
 // Tiles of the lower block triangle (I >= J) of a chunk: the NB diagonal tiles
 // first, then the off-diagonal ones row by row.
@@ -253,12 +255,16 @@ struct ChunkCfg {
     // scales block: e^{rho_I} [NB][DK], e^{G_last} [DK], beta [C], per-wave
     // "all channels referenced to the chunk start" flags [NXW]
     static constexpr int SC_GL = NB * DK, SC_BETA = NB * DK + DK, SC_FLAG = SC_BETA + C;
+    // input preparation (raw q, k): per-wave partial squared norms of k and q
+    // [NXW][C], then per token beta / |k|^2, |k| and 1 / |q|
+    static constexpr int SC_PK = SC_FLAG + NXW, SC_PQ = SC_PK + NXW * C, SC_BH = SC_PQ + NXW * C;
+    static constexpr int SC_KN = SC_BH + C, SC_QI = SC_KN + C, SC_END = SC_QI + C;
     static constexpr float FAST_NATS = 80.f;
 
     static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
     static constexpr size_t SZ_R = al(size_t(C) * PK * sizeof(In));     // Kr, Qr, Kd
     static constexpr size_t SZ_KT = al(size_t(DK) * PC * sizeof(In));   // Ktil^T
-    static constexpr size_t SZ_SC = al(size_t(SC_FLAG + NXW) * sizeof(float));
+    static constexpr size_t SZ_SC = al(size_t(SC_END) * sizeof(float));
     static constexpr size_t SZ_W = al(size_t(NOFF > 0 ? NOFF : 1) * DK * sizeof(float));
     static constexpr size_t SZ_A = al(size_t(NPAIR) * 16 * PT * sizeof(float));
     static constexpr size_t SZ_P = al(size_t(NPAIR) * 16 * PT * sizeof(In));
@@ -288,6 +294,12 @@ struct ChunkCfg {
 // 1 = one log_alpha per token and head [.., H] shared by all key channels,
 // 2 = no decay (log_alpha not read); add = 1 replaces the delta write by the
 // additive one (e = beta v: no prediction, A = 0, E = R = beta V).
+// prep = 1: q and k arrive raw and are L2-normalised here, and the gate
+// argument holds g (input type) with log_alpha = -softplus(g).  With unit
+// keys k^ = k / |k| the recurrence is the same as the one on the raw keys
+// with beta^ = beta / |k|^2 and v' = |k| v (the error scales by 1 / |k|, the
+// write e k^T does not change), and o = S q / |q|; so the chunk algorithm runs
+// on the raw operands with those per-token factors.
 //
 // MAP = false: the prefill itself.  With nsegs > 1 each workgroup runs one of
 // nsegs consecutive segments of its sequence's chunks, from the incoming state
@@ -304,10 +316,10 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                  const float *__restrict__ log_alpha, const float *__restrict__ beta,
                  const float *S0, In *__restrict__ out, float *S_final,
                  const int *__restrict__ cu_seqlens, int T, int H, int dv, int xcd_map,
-                 int nsegs, const float *seg_start, float *seg_map, int gate_arg, int add_arg)
+                 int nsegs, const float *seg_start, float *seg_map, int gate_arg, int add_arg, int prep_arg)
 {
     // the plain recurrence (VAR = false) has the variant arguments folded away
-    const int gate = VAR ? gate_arg : 0, add = VAR ? add_arg : 0;
+    const int gate = VAR ? gate_arg : 0, add = VAR ? add_arg : 0, prep = VAR ? prep_arg : 0;
     typedef ChunkCfg<In, DK, BV, C> K;
     typedef typename V4T<In>::type V4;
     constexpr int NB = K::NB, NDK = K::NDK, PK = K::PK, PC = K::PC, PT = K::PT, RS = K::RS;
@@ -364,6 +376,14 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     // strictly lower on the diagonal) and / or the P tile (lower incl. the
     // diagonal).  Tiles are computed transposed, d[i] = X[16I + n][16J + 4g + i],
     // so each lane stores four consecutive columns of one row.
+    // beta / |k|^2 of token r from the operand waves' partial squared norms
+    // (0 for a zero key: identity tokens past the end of a sequence)
+    auto beta_hat = [&](const float *scc, int r) __attribute__((always_inline)) {
+        float sk = 0.f;
+#pragma unroll
+        for (int w = 0; w < K::NXW; ++w) sk += scc[K::SC_PK + w * C + r];
+        return sk > 0.f ? scc[K::SC_BETA + r] / sk : 0.f;
+    };
     auto tile_job = [&](long ch, int p, bool doA, bool doP, f32x4 *lt = nullptr) __attribute__((always_inline)) {
         int I = p, J = p;
         if (p >= NB) {
@@ -392,7 +412,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 #pragma unroll
             for (int t = 0; t < NDK; ++t) rk[t] = *(const V4 *)(Kr + (16 * I + n) * PK + 16 * t + 4 * g);
             const f32x4 da = mma_tiles<K::KD, In, NDK>(zero4(), cf, rk);
-            const float b = scc[K::SC_BETA + 16 * I + n];
+            const float b = prep ? beta_hat(scc, 16 * I + n) : scc[K::SC_BETA + 16 * I + n];
             f32x4 va;
 #pragma unroll
             for (int i = 0; i < 4; ++i) va[i] = (I > J || 4 * g + i < n) ? da[i] * b : 0.f;
@@ -401,7 +421,11 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 // diagonal tile: also L itself in accumulator layout,
                 // lt[0][i] = L[4g + i][n] (and lt[1] = L^T, the tile just stored)
                 const f32x4 dl = mma_tiles<K::KD, In, NDK>(zero4(), rk, cf);
-                const f32x4 b4 = *(const f32x4 *)(scc + K::SC_BETA + 16 * I + 4 * g);
+                f32x4 b4 = *(const f32x4 *)(scc + K::SC_BETA + 16 * I + 4 * g);
+                if (prep) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) b4[i] = beta_hat(scc, 16 * I + 4 * g + i);
+                }
                 f32x4 vl;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) vl[i] = (n < 4 * g + i) ? dl[i] * b4[i] : 0.f;
@@ -439,13 +463,35 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         // factors (early in stage A), q after the forward pass, k and beta at
         // the end of stage A.  Token i of this lane sits at the lane's fixed
         // offset plus i token rows (the scalar offset).
-        In4 kr[RS], qr[RS];
-        f32x4 gr[RS];
+        In4 kr[RS], qr[RS], grp[RS];
+        f32x4 gr[RS];   // log_alpha; with prep first the raw bits of g, converted in stage A
         float betar = 0.f;
         const int rowb_in = HDK * (int)sizeof(In), rowb_f = HDK * 4;
         const int voff_in = r0 * rowb_in + c0 * (int)sizeof(In), voff_f = r0 * rowb_f + c0 * 4;
         auto chunk_valid = [&](long t0) { return (unsigned)((len - t0 < C) ? len - t0 : C); };
         auto prefetch_g = [&](long t0) __attribute__((always_inline)) {
+            if (prep) {        // g in the input type, its bits kept in gr until stage A
+                const In *gp = (const In *)log_alpha;
+                if (gate == 1) {
+                    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gp + hrow + t0 * H, chunk_valid(t0) * H * (int)sizeof(In));
+#pragma unroll
+                    for (int i = 0; i < RS; ++i) {
+                        const In x = buf_load<In>(rg, r0 * H * (int)sizeof(In), i * H * (int)sizeof(In));
+                        gr[i][0] = tof(x);
+                    }
+                } else if (gate == 0) {
+                    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gp + (hrow + t0 * H) * DK, chunk_valid(t0) * rowb_in);
+#pragma unroll
+                    for (int i = 0; i < RS; ++i) {
+                        if constexpr (sizeof(In) == 2) {   // 4 bf16 in the first two dwords
+                            grp[i] = buf_load<In4>(rg, voff_in, i * rowb_in);
+                        } else {
+                            gr[i] = buf_load<f32x4>(rg, voff_in, i * rowb_in);
+                        }
+                    }
+                }
+                return;
+            }
             if (gate == 1) {   // one value per token, broadcast to the lane's 4 channels
                 const __amdgpu_buffer_rsrc_t rg = buf_rsrc(log_alpha + hrow + t0 * H, chunk_valid(t0) * H * 4);
 #pragma unroll
@@ -478,6 +524,20 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         auto stage_a = [&](long ch) __attribute__((always_inline)) {
             const long t0 = ch * C;
             const int nval = (int)((len - t0 < C) ? len - t0 : C);
+            if (prep) {   // log_alpha = -softplus(g); no gate: 0
+#pragma unroll
+                for (int i = 0; i < RS; ++i) {
+                    f32x4 gv = gr[i];
+                    if (gate == 1) {
+                        gv = f32x4{gr[i][0], gr[i][0], gr[i][0], gr[i][0]};
+                    } else if constexpr (sizeof(In) == 2) {   // unpack the 4 bf16 of channels c0 .. c0+3
+                        gv = f32x4{tof(grp[i][0]), tof(grp[i][1]), tof(grp[i][2]), tof(grp[i][3])};
+                    }
+                    // rows past the end are identity tokens: log_alpha = 0 there, not -softplus(0)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) gr[i][j] = (gate == 2 || r0 + i >= nval) ? 0.f : neg_softplus(gv[j]);
+                }
+            }
             float tot[4], inc[4], exc[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -526,17 +586,24 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             // (and Kd = k / e^{G - ref} where some channel keeps a block reference)
             {
                 float pp[4];
+                float sk[RS], sq[RS];   // prep: squared norms over this wave's channels
 #pragma unroll
                 for (int j = 0; j < 4; ++j) pp[j] = fexp(exc[j] - ref[j]);
 #pragma unroll
                 for (int i = 0; i < RS; ++i) {
                     f32x4 vkr, vqr, vkd;
+                    sk[i] = 0.f;
+                    sq[i] = 0.f;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         pp[j] *= al[i][j];
                         const float kf = tof(kr[i][j]);
                         vkr[j] = kf * pp[j];                       // k e^{G - ref}
                         if constexpr (!MAP) vqr[j] = tof(qr[i][j]) * pp[j];   // q e^{G - ref}
+                        if (prep) {
+                            sk[i] += kf * kf;
+                            if constexpr (!MAP) sq[i] += tof(qr[i][j]) * tof(qr[i][j]);
+                        }
                     }
                     if (act) {
                         const int r = r0 + i;
@@ -546,6 +613,20 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 #pragma unroll
                             for (int j = 0; j < 4; ++j) vkd[j] = tof(kr[i][j]) * __builtin_amdgcn_rcpf(pp[j]);   // k e^{ref - G}
                             store4(sKd + r * PK + c0, vkd);
+                        }
+                    }
+                }
+                if (prep) {   // per token over the channel group's lanes, stored by its first lane
+#pragma unroll
+                    for (int i = 0; i < RS; ++i) {
+                        sk[i] = group_sum<K::NCG>(sk[i]);
+                        sq[i] = group_sum<K::NCG>(sq[i]);
+                    }
+                    if (act && cg == 0) {
+#pragma unroll
+                        for (int i = 0; i < RS; ++i) {
+                            sc[K::SC_PK + xw * C + r0 + i] = sk[i];
+                            sc[K::SC_PQ + xw * C + r0 + i] = sq[i];
                         }
                     }
                 }
@@ -614,6 +695,20 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         //      when there is a single state wave, which then also leaves the
         //      off-diagonal A tiles here)
         auto stage_b = [&](long ch) __attribute__((always_inline)) {
+            if (prep && xw == 0 && lane < C) {
+                // per-token factors for the state waves' next chunk: beta / |k|^2,
+                // |k| and 1 / |q| (zero vectors give 0)
+                float *sc = bufSc(ch);
+                float sk = 0.f, sq = 0.f;
+#pragma unroll
+                for (int w = 0; w < K::NXW; ++w) {
+                    sk += sc[K::SC_PK + w * C + lane];
+                    sq += sc[K::SC_PQ + w * C + lane];
+                }
+                sc[K::SC_BH + lane] = sk > 0.f ? sc[K::SC_BETA + lane] / sk : 0.f;
+                sc[K::SC_KN + lane] = __builtin_sqrtf(sk);
+                sc[K::SC_QI + lane] = sq > 0.f ? __builtin_amdgcn_rsqf(sq) : 0.f;
+            }
             if (add) {   // no A: only the diagonal P tiles of a single state wave
                 if constexpr (K::NBV == 1 && !MAP) {
                     for (int p = xw; p < NB; p += K::NXW) tile_job(ch, p, false, true);
@@ -819,7 +914,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             }
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
-                const f32x4 b4 = *(const f32x4 *)(sc + K::SC_BETA + 16 * I + 4 * g);
+                const f32x4 b4 = *(const f32x4 *)(sc + (prep ? K::SC_BH : K::SC_BETA) + 16 * I + 4 * g);
                 f32x4 vt;                                           // V[16I + 4g + i][n]
                 if constexpr (K::F32) {
                     const V4 va[1] = {vr[I]}, vi[1] = {ident[0]};
@@ -827,6 +922,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 } else {
                     vt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[I / 2], ident[I & 1], zero4(), 0, 0, 0);
                 }
+                if (prep) vt = vt * *(const f32x4 *)(sc + K::SC_KN + 16 * I + 4 * g);   // |k| v
 #pragma unroll
                 for (int i = 0; i < 4; ++i) R[I][i] = b4[i] * (vt[i] - R[I][i]);
             }
@@ -859,7 +955,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 #pragma unroll
                 for (int J = 0; J < NB; ++J)
                     pb[J] = (J <= I) ? *(const V4 *)(sP + tile_index(NB, I, J) * 16 * PT + n * PT + 4 * g) : V4{};
-                const f32x4 o = O1[I] + mma_tiles<K::KC, In, NB>(zero4(), Eb, pb);   // O[16I + n][16cb + 4g + i]
+                f32x4 o = O1[I] + mma_tiles<K::KC, In, NB>(zero4(), Eb, pb);   // O[16I + n][16cb + 4g + i]
+                if (prep) o = o * sc[K::SC_QI + 16 * I + n];                   // / |q|
                 buf_store(to_op<In>(o), ro, voff_o, 16 * I * rowb_v);
             }
             __syncthreads();
@@ -938,7 +1035,7 @@ hipError_t launch_chunk_pass_v(const ChunkArgs &a, int nsu, int nrows)
     hipLaunchKernelGGL((chunk_fwd_kernel<In, DK, BV, C, MAP, VAR>), dim3((unsigned)grid), dim3(K::NT), 0,
                        a.stream, (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S0,
                        (In *)a.out, a.S_final, a.cu_seqlens, a.T, a.H, a.dv, xcd_map, a.nsegs, a.seg_start,
-                       a.seg_map, a.gate, a.add);
+                       a.seg_map, a.gate, a.add, a.prep);
     return hipGetLastError();
 }
 
@@ -946,7 +1043,7 @@ hipError_t launch_chunk_pass_v(const ChunkArgs &a, int nsu, int nrows)
 template <typename In, int DK, int BV, int C, bool MAP>
 hipError_t launch_chunk_pass(const ChunkArgs &a, int nsu, int nrows)
 {
-    if (a.gate != 0 || a.add != 0) return launch_chunk_pass_v<In, DK, BV, C, MAP, true>(a, nsu, nrows);
+    if (a.gate != 0 || a.add != 0 || a.prep != 0) return launch_chunk_pass_v<In, DK, BV, C, MAP, true>(a, nsu, nrows);
     return launch_chunk_pass_v<In, DK, BV, C, MAP, false>(a, nsu, nrows);
 }
 

@@ -25,9 +25,25 @@ namespace kda {
 
 // log decays of 4 key channels starting at element c of the token's
 // log_alpha row: per channel (gate 0), one value per token and head at index
-// tok (gate 1), or none (gate 2: alpha = 1).
-__device__ __forceinline__ f32x4 decay_logs(const float *log_alpha, long c, long tok, int gate)
+// tok (gate 1), or none (gate 2: alpha = 1).  With prep the argument holds
+// the pre-activations g in the input type and log(alpha) = -softplus(g).
+template <typename In>
+__device__ __forceinline__ f32x4 decay_logs(const float *log_alpha, long c, long tok, int gate, int prep)
 {
+    typedef In In4 __attribute__((ext_vector_type(4)));
+    if (prep) {
+        const In *gp = (const In *)log_alpha;
+        if (gate == 0) {
+            const In4 gv = *(const In4 *)(gp + c);
+            return f32x4{neg_softplus(tof(gv[0])), neg_softplus(tof(gv[1])), neg_softplus(tof(gv[2])),
+                         neg_softplus(tof(gv[3]))};
+        }
+        if (gate == 1) {
+            const float x = neg_softplus(tof(gp[tok]));
+            return f32x4{x, x, x, x};
+        }
+        return zero4();
+    }
     if (gate == 0) return *(const f32x4 *)(log_alpha + c);
     if (gate == 1) {
         const float x = log_alpha[tok];
@@ -36,15 +52,32 @@ __device__ __forceinline__ f32x4 decay_logs(const float *log_alpha, long c, long
     return zero4();
 }
 
+// prep: scales the lane's 16 channels of a token's k (or q) to unit L2 norm
+// over the row's LPR lanes (a zero vector stays zero).
+template <int LPR>
+__device__ __forceinline__ void normalise16(f32x4 (&x)[4])
+{
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ss += x[u][j] * x[u][j];
+    ss = group_sum<LPR>(ss);
+    const float r = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = x[u] * r;
+}
+
 // Variants (uniform arguments, read only when VAR): gate as in decay_logs;
 // add = 1 is the additive write e = beta v (no prediction).
 template <typename In, int DK, bool VAR>
 __global__ void __launch_bounds__(256)
 decode_step_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
                    const float *__restrict__ log_alpha, const float *__restrict__ beta,
-                   float *__restrict__ S, In *__restrict__ out, int dv, int gate_arg, int add_arg)
+                   float *__restrict__ S, In *__restrict__ out, int dv, int gate_arg, int add_arg,
+                   int prep_arg)
 {
-    const int gate = VAR ? gate_arg : 0, add = VAR ? add_arg : 0;
+    const int gate = VAR ? gate_arg : 0, add = VAR ? add_arg : 0, prep = VAR ? prep_arg : 0;
     typedef In In4 __attribute__((ext_vector_type(4)));
     constexpr int LPR = DK / 16;          // lanes per state row, 16 floats (4 x float4) each
     constexpr int RPP = 256 / LPR;        // rows per pass of the workgroup
@@ -57,7 +90,7 @@ decode_step_kernel(const In *__restrict__ q, const In *__restrict__ k, const In 
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const long c = head * DK + 4 * (sub + LPR * u);
-        const f32x4 la = decay_logs(log_alpha, c, head, gate);
+        const f32x4 la = decay_logs<In>(log_alpha, c, head, gate, prep);
         const In4 kv = *(const In4 *)(k + c);
         const In4 qv = *(const In4 *)(q + c);
 #pragma unroll
@@ -66,6 +99,10 @@ decode_step_kernel(const In *__restrict__ q, const In *__restrict__ k, const In 
             kk[u][j] = tof(kv[j]);
             qq[u][j] = tof(qv[j]);
         }
+    }
+    if (prep) {
+        normalise16<LPR>(kk);
+        normalise16<LPR>(qq);
     }
     const float b = beta[head];
 
@@ -124,9 +161,9 @@ __global__ void __launch_bounds__(256)
 decode_multi_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
                     const float *__restrict__ log_alpha, const float *__restrict__ beta,
                     float *__restrict__ S, In *__restrict__ out, int T, int H, int dv, int gate_arg,
-                    int add_arg)
+                    int add_arg, int prep_arg)
 {
-    const int gate = VAR ? gate_arg : 0, add = VAR ? add_arg : 0;
+    const int gate = VAR ? gate_arg : 0, add = VAR ? add_arg : 0, prep = VAR ? prep_arg : 0;
     typedef In In4 __attribute__((ext_vector_type(4)));
     constexpr int LPR = DK / 16;
     constexpr int RPP = 256 / LPR;
@@ -151,7 +188,7 @@ decode_multi_kernel(const In *__restrict__ q, const In *__restrict__ k, const In
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const long c = tok * DK + 4 * (sub + LPR * u);
-            const f32x4 la = decay_logs(log_alpha, c, tok, gate);
+            const f32x4 la = decay_logs<In>(log_alpha, c, tok, gate, prep);
             const In4 kv = *(const In4 *)(k + c);
             const In4 qv = *(const In4 *)(q + c);
 #pragma unroll
@@ -160,6 +197,10 @@ decode_multi_kernel(const In *__restrict__ q, const In *__restrict__ k, const In
                 kk[u][j] = tof(kv[j]);
                 qq[u][j] = tof(qv[j]);
             }
+        }
+        if (prep) {
+            normalise16<LPR>(kk);
+            normalise16<LPR>(qq);
         }
         const float b = beta[tok];
 #pragma unroll
@@ -206,14 +247,14 @@ hipError_t launch_decode_multi_t(const DecodeArgs &a, int T)
 {
     const long grid = (long)a.N * a.H;
     if (grid == 0) return hipSuccess;
-    if (a.gate != 0 || a.add != 0)
+    if (a.gate != 0 || a.add != 0 || a.prep != 0)
         hipLaunchKernelGGL((decode_multi_kernel<In, DK, true>), dim3((unsigned)grid), dim3(256), 0, a.stream,
                            (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S,
-                           (In *)a.out, T, a.H, a.dv, a.gate, a.add);
+                           (In *)a.out, T, a.H, a.dv, a.gate, a.add, a.prep);
     else
         hipLaunchKernelGGL((decode_multi_kernel<In, DK, false>), dim3((unsigned)grid), dim3(256), 0, a.stream,
                            (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S,
-                           (In *)a.out, T, a.H, a.dv, 0, 0);
+                           (In *)a.out, T, a.H, a.dv, 0, 0, 0);
     return hipGetLastError();
 }
 
@@ -222,14 +263,14 @@ hipError_t launch_decode_t(const DecodeArgs &a)
 {
     const int grid = a.N * a.H;
     if (grid == 0) return hipSuccess;
-    if (a.gate != 0 || a.add != 0)
+    if (a.gate != 0 || a.add != 0 || a.prep != 0)
         hipLaunchKernelGGL((decode_step_kernel<In, DK, true>), dim3(grid), dim3(256), 0, a.stream,
                            (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S,
-                           (In *)a.out, a.dv, a.gate, a.add);
+                           (In *)a.out, a.dv, a.gate, a.add, a.prep);
     else
         hipLaunchKernelGGL((decode_step_kernel<In, DK, false>), dim3(grid), dim3(256), 0, a.stream,
                            (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S,
-                           (In *)a.out, a.dv, 0, 0);
+                           (In *)a.out, a.dv, 0, 0, 0);
     return hipGetLastError();
 }
 

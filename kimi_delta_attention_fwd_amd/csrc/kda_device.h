@@ -145,4 +145,13 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// log(alpha) = -softplus(g) = -(max(g, 0) + log(1 + e^{-|g|})), through the
+// hardware base-2 exponential and logarithm (for e^{-|g|} below ~6e-8 the
+// sum rounds to 1 and log(alpha) to -max(g, 0), an error below 6e-8).
+__device__ __forceinline__ float neg_softplus(float g)
+{
+    const float t = __builtin_amdgcn_exp2f(-fabsf(g) * 1.4426950408889634f);
+    return -(fmaxf(g, 0.f) + __builtin_amdgcn_logf(1.f + t) * 0.6931471805599453f);
+}
+
 }  // namespace kda

@@ -18,8 +18,8 @@ struct ChunkArgs {
     int nsegs;
     float *seg_map, *seg_start;
     // variant: gate 0 per channel, 1 scalar per token and head, 2 none;
-    // add 1 = additive write
-    int gate, add;
+    // add 1 = additive write; prep 1 = raw q, k and gate pre-activations
+    int gate, add, prep;
     hipStream_t stream;
 };
 
@@ -29,7 +29,7 @@ struct DecodeArgs {
     float *S;
     void *out;
     int N, H, dk, dv;
-    int gate, add;   // as in ChunkArgs
+    int gate, add, prep;   // as in ChunkArgs
     hipStream_t stream;
 };
 

@@ -89,6 +89,36 @@ def _mode(write: str) -> int:
     raise ValueError(f"write must be 'delta' or 'add', got {write!r}")
 
 
+def prepare(q_raw, k_raw, g=None, gate: str = "channel"):
+    """Raw inputs to the recurrence's inputs, in float64.
+
+    q and k are divided by their L2 norm over the key channels (the "Kimi K3
+    notes 1: KDA" page, sect. 4: q and k pass a feature map and an L2
+    normalisation before the recurrence); a zero row stays zero.  The gate is
+    log_alpha = -softplus(g) = -log(1 + e^g), the parameterisation this build
+    reads for the pages' alpha in (0, 1] (elementwise, per channel, or one
+    value per token and head broadcast to every channel; "none" gives 0).
+    Returns (q, k, log_alpha [.., H, dk]).
+    """
+    q = _f64(q_raw)
+    k = _f64(k_raw)
+
+    def unit(x):
+        n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+        return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+
+    if gate == "none":
+        la = np.zeros_like(k)
+    else:
+        gg = _f64(g)
+        la = -np.logaddexp(0.0, gg)            # -log(e^0 + e^g)
+        if gate == "scalar":
+            la = np.broadcast_to(la[..., None], k.shape).copy()
+        elif gate != "channel":
+            raise ValueError(f"gate must be 'channel', 'scalar' or 'none', got {gate!r}")
+    return unit(q), unit(k), la
+
+
 def forward(q, k, v, log_alpha, beta, S0=None, write: str = "delta"):
     """Token-by-token recurrence for a dense batch.
 

@@ -253,7 +253,7 @@ def test_variant_validation(lib):
     def ex(variant, la=A + 192 * MB, nseg=1, ws=None, wsb=0):
         return lib.kda_chunk_fwd_ex(A, A + 64 * MB, A + 128 * MB, la, A + 256 * MB, None, A + 320 * MB,
                                     A + 384 * MB, 2, 100, 4, 64, 64, 64, variant, nseg, ws, wsb, None)
-    assert ex(3) == 2 and ex(8) == 2 and ex(-1) == 2
+    assert ex(3) == 2 and ex(16) == 2 and ex(-1) == 2 and ex(8 | 3) == 2
     assert "variant" in kda.kda_last_error()
     assert ex(0, la=None) == 1                  # the per-channel gate needs log_alpha
     assert ex(1, la=None) == 1                  # so does the scalar gate
@@ -265,3 +265,18 @@ def test_variant_validation(lib):
         return lib.kda_recurrent_fwd_ex(A, A + MB, A + 2 * MB, la, A + 4 * MB, A + 8 * MB, A + 64 * MB,
                                         4, 0, 2, 128, 128, variant, None)
     assert rex(3) == 2 and rex(2, la=None) == 0
+
+
+def test_raw_input_variant_validation(lib):
+    def ex(variant, la=A + 192 * MB, B=2, out=A + 320 * MB, nseg=2):
+        # nseg = 2 without a workspace: a call whose other arguments pass stops
+        # at the workspace check (status 1, "workspace"), before any launch
+        return lib.kda_chunk_fwd_ex(A, A + 64 * MB, A + 128 * MB, la, A + 256 * MB, None, out, A + 384 * MB,
+                                    B, 100, 4, 64, 64, 64, variant, nseg, None, 0, None)
+    assert ex(8 | 1, la=A + 192 * MB + 2) == 1 and "workspace" in kda.kda_last_error()   # 2-byte aligned g
+    assert ex(1, la=A + 192 * MB + 2) == 4        # one fp32 log_alpha per token needs 4-byte alignment
+    assert ex(8, la=None) == 1 and "log_alpha" in kda.kda_last_error()
+    # bf16 g [B, T, H, dk] occupies 2 bytes per element: out right after it does not overlap
+    g_bytes = 2 * 100 * 4 * 64 * 2
+    assert ex(8, out=A + 192 * MB + g_bytes) == 1 and "workspace" in kda.kda_last_error()
+    assert ex(8, out=A + 192 * MB + g_bytes - 16) == 6

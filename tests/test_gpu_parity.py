@@ -407,6 +407,85 @@ def test_decode_variants(dev, gate, write):
                      TOL[dtype])
 
 
+# ---------------------------------------------------------------- fused input preparation
+def oracle_raw(p, gate, write="delta", varlen=False):
+    """The oracle on the raw inputs: q, k normalised and log_alpha = -softplus(g)
+    by oracle.prepare (float64), then the recurrence."""
+    g = None if gate == "none" else (p.log_alpha[..., 0] if gate == "scalar" else p.log_alpha)
+    qn, kn, la = oracle.prepare(f64(p.q), f64(p.k), None if g is None else f64(g), gate=gate)
+    if varlen:
+        return oracle.forward_varlen(qn, kn, f64(p.v), la, f64(p.beta), np.array(p.cu_host), S0=f64(p.S0),
+                                     write=write)
+    return oracle.forward(qn, kn, f64(p.v), la, f64(p.beta), S0=f64(p.S0), write=write)
+
+
+def raw_gate_arg(p, gate):
+    if gate == "channel":
+        return p.log_alpha
+    if gate == "scalar":
+        return p.log_alpha[..., 0].contiguous()
+    return None
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("gate,write", [("channel", "delta"), ("scalar", "delta"), ("none", "delta"),
+                                        ("channel", "add")])
+def test_chunk_raw_inputs(dev, gate, write, dtype):
+    """q, k un-normalised (different scales per token) and gate pre-activations:
+    normalisation and softplus inside the kernel, both schedules."""
+    B, T, H, dk, dv = 2, 230, 2, 128 if dtype == "bf16" else 64, 64
+    C = 64 if dtype == "bf16" else 32
+    note(f"case raw inputs gate={gate} write={write} B{B} T{T} H{H} dk{dk} dv{dv} {dtype} C{C}")
+    p = kda_synth.prefill_raw(B, T, H, dk, dv, dtype=dtype, s0_sigma=0.1, q_sigma=2.0, k_sigma=0.5, seed=91,
+                              device=dev)
+    # a spread of key and query norms across tokens
+    scale = torch.exp(torch.linspace(-2.0, 2.0, T, device=dev)).view(1, T, 1, 1)
+    p.k = (p.k.float() * scale).to(p.k.dtype)
+    p.q = (p.q.float() * scale.flip(1)).to(p.q.dtype)
+    o_ref, s_ref = oracle_raw(p, gate, write)
+    for segments in (1, 3):
+        out, sf = kda.chunk_fwd(p.q, p.k, p.v, raw_gate_arg(p, gate), p.beta, S0=p.S0, C=C, segments=segments,
+                                gate=gate, write=write, raw=True)
+        torch.cuda.synchronize()
+        assert_close(f"raw {gate}/{write} segments={segments}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+
+
+def test_chunk_raw_inputs_varlen_and_zero_rows(dev):
+    lengths = [150, 1, 0, 97]
+    note(f"case raw inputs varlen lengths {lengths} H2 d128 bf16, zero q and k rows")
+    p = kda_synth.prefill_raw(1, sum(lengths), 2, 128, 128, dtype="bf16", seed=93, device=dev)
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + n)
+    p.cu_host = cu
+    p.cu_seqlens = torch.tensor(cu, dtype=torch.int32, device=dev)
+    p.S0 = torch.randn((len(lengths), 2, 128, 128), device=dev) * 0.1
+    p.k[0, 5, 1] = 0     # a zero key writes nothing
+    p.q[0, 9, 0] = 0     # a zero query reads nothing
+    out = torch.empty_like(p.v)
+    sf = torch.empty_like(p.S0)
+    kda.kda_chunk_fwd_varlen_ex(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out, sf, p.cu_seqlens, len(lengths),
+                                sum(lengths), 2, 128, 128, 64, kda.variant(raw=True))
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_raw(p, "channel", varlen=True)
+    assert torch.isfinite(out.float()).all()
+    assert_close("raw varlen", f64(out), f64(sf), o_ref, s_ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("gate", ["channel", "scalar", "none"])
+def test_decode_raw_inputs(dev, gate):
+    for dtype in ("bf16", "f32"):
+        N, T, H, dk, dv = 3, 4, 2, 64, 128
+        note(f"case decode raw inputs gate={gate} N{N} T{T} H{H} dk{dk} dv{dv} {dtype}")
+        p = kda_synth.prefill_raw(N, T, H, dk, dv, dtype=dtype, s0_sigma=0.1, q_sigma=3.0, k_sigma=0.3, seed=95,
+                                  device=dev)
+        o_ref, s_ref = oracle_raw(p, gate)
+        S = p.S0.clone()
+        out = kda.recurrent_fwd(p.q, p.k, p.v, raw_gate_arg(p, gate), p.beta, S, gate=gate, raw=True)
+        torch.cuda.synchronize()
+        assert_close(f"decode raw {gate}", f64(out), f64(S), o_ref, s_ref, TOL[dtype])
+
+
 # ---------------------------------------------------------------- packed variable length
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_varlen_small(dev, dtype):

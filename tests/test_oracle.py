@@ -368,3 +368,41 @@ def test_oracle_empty_sequence_and_varlen():
         o_n, S_n = oracle.forward(q[:, sl], k[:, sl], v[:, sl], la[:, sl], beta[:, sl], S0=S0[n:n + 1])
         assert np.array_equal(out[:, sl], o_n)
         assert np.array_equal(S[n:n + 1], S_n)
+
+
+# ---------------------------------------------------------------- input preparation
+def test_prepare_normalises_and_applies_the_gate():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((2, 7, 3, 16)) * 3.0
+    k = rng.standard_normal((2, 7, 3, 16)) * 0.2
+    k[0, 2, 1] = 0.0                                   # a zero key stays zero
+    g = rng.standard_normal((2, 7, 3, 16)) * 4.0
+    qn, kn, la = oracle.prepare(q, k, g)
+    assert np.allclose(np.linalg.norm(qn, axis=-1), 1.0, atol=1e-14)
+    norms = np.linalg.norm(kn, axis=-1)
+    assert np.all(kn[0, 2, 1] == 0.0)
+    assert np.allclose(np.delete(norms.reshape(-1), np.ravel_multi_index((0, 2, 1), norms.shape)), 1.0,
+                       atol=1e-14)
+    # direction kept, scale removed
+    assert np.allclose(qn * np.linalg.norm(q, axis=-1, keepdims=True), q, atol=1e-12)
+    # log alpha = log(sigmoid(-g)) written another way, and its limits
+    assert np.allclose(la, np.log(1.0 / (1.0 + np.exp(g))), atol=1e-12)
+    assert np.all(la < 0.0)
+    _, _, l0 = oracle.prepare(q[:1, :1, :1, :1], q[:1, :1, :1, :1], np.zeros((1, 1, 1, 1)))
+    assert abs(l0[0, 0, 0, 0] + np.log(2.0)) < 1e-15
+    _, _, lbig = oracle.prepare(q[:1, :1, :1, :1], q[:1, :1, :1, :1], np.full((1, 1, 1, 1), 800.0))
+    assert lbig[0, 0, 0, 0] == -800.0                  # no overflow for large pre-activations
+
+
+def test_prepare_scalar_gate_and_scale_invariance():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((1, 5, 2, 8))
+    k = rng.standard_normal((1, 5, 2, 8))
+    gs = rng.standard_normal((1, 5, 2))
+    _, _, la = oracle.prepare(q, k, gs, gate="scalar")
+    assert la.shape == (1, 5, 2, 8) and np.all(la == la[..., :1])
+    _, _, la0 = oracle.prepare(q, k, None, gate="none")
+    assert np.all(la0 == 0.0)
+    a1 = oracle.prepare(q, k, gs, gate="scalar")
+    a2 = oracle.prepare(q * 7.5, k * 0.01, gs, gate="scalar")
+    assert all(np.allclose(x, y, atol=1e-14) for x, y in zip(a1, a2))
