@@ -210,7 +210,7 @@ def bench_decode_multi(args, torch, kda, kda_synth, stream, T=4, launches=50):
                 tokens_per_s=N * T * launches / wall, launches_per_s=launches / wall, kernel_ms=kms,
                 roofline=dict(bound="hbm", achieved=round(nbytes / (kms * 1e-3) / 1e9, 1), peak=HBM_PEAK_GBS,
                               unit="GB/s", frac=round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                              algorithmic_bytes=nbytes))
+                              traffic=load_traffic("decode_multi", "decode_multi"), algorithmic_bytes=nbytes))
 
 
 def bench_prep(args, torch, kda, kda_synth, stream, steps=10):

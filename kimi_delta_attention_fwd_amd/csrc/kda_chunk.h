@@ -986,17 +986,21 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 // Incoming states of the segments of every (sequence, head): slot 0 holds S0
 // (zero when absent), slot p + 1 = slot p M_p + N_p, row by row, with (M_p,
 // N_p) the map of segment p from the MAP pass.  One workgroup per 16 state rows
-// of a head; thread (r, cg) keeps columns cg DK/16 .. of row r, and the
-// current rows sit in LDS for the products.  fp32 throughout.
+// of a head; thread (r, cg) keeps columns cg DK/16 .. of row r.  Each step
+// stages M_p in LDS (coalesced 16-byte loads, in two halves of DK/2 rows for
+// DK = 128 to stay within the LDS budget) next to the current rows.  fp32
+// throughout.
 template <int DK>
 __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const float *seg_map,
                                                           float *seg_start, int dv, int nsegs)
 {
-    constexpr int CPT = DK / 16;
-    __shared__ float srow[16][DK + 1];
+    constexpr int CPT = DK / 16;                  // columns per thread
+    constexpr int MR = DK > 64 ? DK / 2 : DK;     // rows of M staged at a time
+    __shared__ __attribute__((aligned(16))) float srow[16][DK + 4];
+    __shared__ __attribute__((aligned(16))) float sm[MR][DK];
     const int nrb = dv / 16;
     const int head = blockIdx.x / nrb, rb = blockIdx.x % nrb;
-    const int r = threadIdx.x >> 4, c0 = (threadIdx.x & 15) * CPT;
+    const int tid = threadIdx.x, r = tid >> 4, c0 = (tid & 15) * CPT;
     const int row = rb * 16 + r;
     float acc[CPT];
 #pragma unroll
@@ -1009,15 +1013,21 @@ __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const
         __syncthreads();   // the previous step's reads of srow are done
 #pragma unroll
         for (int j = 0; j < CPT; ++j) srow[r][c0 + j] = acc[j];
-        __syncthreads();
         const float *mp = seg_map + ((long)head * (nsegs - 1) + p) * (dv + DK) * DK;
-        const float *M = mp + (long)dv * DK;
 #pragma unroll
         for (int j = 0; j < CPT; ++j) acc[j] = mp[(long)row * DK + c0 + j];   // N_p
-        for (int i = 0; i < DK; ++i) {
-            const float si = srow[r][i];
+        const float *M = mp + (long)dv * DK;
+        for (int h0 = 0; h0 < DK; h0 += MR) {
+            if (h0 > 0) __syncthreads();   // everyone is done with the previous half of M
+            for (int e = tid * 4; e < MR * DK; e += 256 * 4)
+                *(f32x4 *)(&sm[0][0] + e) = *(const f32x4 *)(M + (long)h0 * DK + e);
+            __syncthreads();
+#pragma unroll 8
+            for (int i = 0; i < MR; ++i) {
+                const float si = srow[r][h0 + i];
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) acc[j] = fmaf(si, M[i * DK + c0 + j], acc[j]);
+                for (int j = 0; j < CPT; ++j) acc[j] = fmaf(si, sm[i][c0 + j], acc[j]);
+            }
         }
     }
 }
