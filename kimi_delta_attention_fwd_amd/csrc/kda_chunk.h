@@ -288,6 +288,7 @@ struct ChunkCfg {
     static_assert(16 % RS == 0, "a lane's tokens stay inside one 16-token block");
     static_assert(NACT <= 64, "one operand wave covers its channels");
     static_assert((NSEG & (NSEG - 1)) == 0, "segment scan over a power of two");
+    static_assert(NSEG >= NB && NSEG >= NOFF, "a segment of lanes per scale and w vector");
 };
 
 // Variants (uniform arguments, read only when VAR): gate 0 = per-channel log_alpha [.., H, DK],
@@ -661,28 +662,33 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                     for (int j = 0; j < 4; ++j) store_row_swz<In, RS>(Kt, c0 + j, r0, PC, K::SWZ, kt[j]);
                 }
             }
-            // per-channel scales, written by the lanes of the first segment
+            // per-channel scales, one 4-channel vector store per lane: e^{G_last}
+            // by the first segment's lanes, e^{rho_I} by segment I, w_IJ by
+            // segment I(I-1)/2 + J.  w is stored also when all factors are 1:
+            // other waves may take block references, and then the tiles read w
+            // for every channel.
             const bool wave_fast = __all(lane_fast);
-            if (seg == 0) {
+            if (seg == 0) *(f32x4 *)(sc + K::SC_GL + c0) = f32x4{fexp(glast[0]), fexp(glast[1]), fexp(glast[2]), fexp(glast[3])};
+            if (wave_fast) {   // a uniform branch: no exponentials when every factor is 1
+                const f32x4 one{1.f, 1.f, 1.f, 1.f};
+                if (seg < NB) *(f32x4 *)(sc + seg * DK + c0) = one;
+                if (seg < K::NOFF) *(f32x4 *)(sW + seg * DK + c0) = one;
+            } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    sc[K::SC_GL + c0 + j] = fexp(glast[j]);
-                    if (wave_fast) {   // every reference is the chunk start: all factors are 1
-                        // (w too: other waves may take block references, and then
-                        // the tiles read w for every channel)
+                for (int I = 0; I < NB; ++I) {
+                    if (seg == I) {
+                        f32x4 e;
 #pragma unroll
-                        for (int I = 0; I < NB; ++I) {
-                            sc[I * DK + c0 + j] = 1.f;
+                        for (int j = 0; j < 4; ++j) e[j] = fexp(rhoI[I][j]);
+                        *(f32x4 *)(sc + I * DK + c0) = e;
+                    }
 #pragma unroll
-                            for (int J = 0; J < I; ++J) sW[(I * (I - 1) / 2 + J) * DK + c0 + j] = 1.f;
-                        }
-                    } else {
+                    for (int J = 0; J < I; ++J) {
+                        if (seg == I * (I - 1) / 2 + J) {
+                            f32x4 w;
 #pragma unroll
-                        for (int I = 0; I < NB; ++I) {
-                            sc[I * DK + c0 + j] = fexp(rhoI[I][j]);
-#pragma unroll
-                            for (int J = 0; J < I; ++J)
-                                sW[(I * (I - 1) / 2 + J) * DK + c0 + j] = fexp(rhoI[I][j] - rhoI[J][j]);
+                            for (int j = 0; j < 4; ++j) w[j] = fexp(rhoI[I][j] - rhoI[J][j]);
+                            *(f32x4 *)(sW + (I * (I - 1) / 2 + J) * DK + c0) = w;
                         }
                     }
                 }
@@ -1042,10 +1048,11 @@ hipError_t launch_chunk_pass_v(const ChunkArgs &a, int nsu, int nrows)
     const long grid = units * (nrows / BV);
     if (grid == 0) return hipSuccess;
     const int xcd_map = (units % 8 == 0) ? 1 : 0;
+    // the kernel divides by the segment count: never pass less than 1
     hipLaunchKernelGGL((chunk_fwd_kernel<In, DK, BV, C, MAP, VAR>), dim3((unsigned)grid), dim3(K::NT), 0,
                        a.stream, (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S0,
-                       (In *)a.out, a.S_final, a.cu_seqlens, a.T, a.H, a.dv, xcd_map, a.nsegs, a.seg_start,
-                       a.seg_map, a.gate, a.add, a.prep);
+                       (In *)a.out, a.S_final, a.cu_seqlens, a.T, a.H, a.dv, xcd_map, a.nsegs < 1 ? 1 : a.nsegs,
+                       a.seg_start, a.seg_map, a.gate, a.add, a.prep);
     return hipGetLastError();
 }
 
