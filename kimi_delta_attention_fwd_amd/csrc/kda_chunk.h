@@ -24,10 +24,11 @@
 // (decay-scaled operands, the diagonal A tiles and the inverses of the
 // diagonal blocks of I + A) runs on four "operand" waves one chunk ahead of
 // the state-dependent chain (R, the solve, O, the state update), which runs
-// on BV/16 "state" waves, one per 16 value rows.  The state waves fill their
-// second segment with the next chunk's P tiles and off-diagonal A tiles (with
-// a single state wave: the off-diagonal P tiles only, the operand waves keep
-// the rest).  Value rows of the state evolve independently, so each
+// on BV/16 "state" waves, one per 16 value rows.  The state update needs only
+// the chunk's own E and double-buffered operands, so it closes the state
+// waves' first segment; their second segment forms the next chunk's P tiles
+// and off-diagonal A tiles (with a single state wave: the off-diagonal P tiles
+// only, the operand waves keep the rest).  Value rows of the state evolve independently, so each
 // state wave runs its whole chain alone: its 16 x DK slice of the fp32 state
 // stays in MFMA accumulator registers across the whole sequence, and every
 // accumulator tile feeds the next product directly as an operand (a tile held
@@ -965,9 +966,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 if (prep) o = o * sc[K::SC_QI + 16 * I + n];                   // / |q|
                 buf_store(to_op<In>(o), ro, voff_o, 16 * I * rowb_v);
             }
-            __syncthreads();
-
-            // ---- S^T <- Diag(e^{G_last}) S^T + Ktil^T E
+            // ---- S^T <- Diag(e^{G_last}) S^T + Ktil^T E (Ktil and the scales of this chunk are
+            //      double-buffered, so this needs no barrier)
             const In *Kt = bufKt(ch);
 #pragma unroll
             for (int ct = 0; ct < NDK; ++ct) {
@@ -978,6 +978,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                     ka[b] = *(const V4 *)(Kt + Panel<In, 16>::swz_index(16 * ct + n, 16 * b + 4 * g, PC, K::SWZ));
                 Sacc[ct] = mma_tiles<K::KC, In, NB>(Sacc[ct] * gl, ka, Eb);
             }
+            __syncthreads();
+
             // ---- the next chunk's tiles
             if (ch + 1 < nch) y_tiles(ch + 1);
             __syncthreads();
