@@ -558,19 +558,32 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                     if (seg >= d) inc[j] += y;
                 }
             float rhoI[NB][4], ref[4], glast[4];
-            bool lane_fast = true;
+            bool fastc[4], lane_fast = true;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 exc[j] = inc[j] - tot[j];                                       // G before my first token
                 glast[j] = __shfl(inc[j], (K::NSEG - 1) * K::NCG + cg, 64);      // G_last
-                const bool fastc = glast[j] >= -K::FAST_NATS;
-                lane_fast = lane_fast && fastc;
-                const float rb = __shfl(exc[j], blk_src, 64);                   // G before my block
-                ref[j] = fastc ? 0.f : rb;
+                fastc[j] = glast[j] >= -K::FAST_NATS;
+                lane_fast = lane_fast && fastc[j];
+            }
+            const bool wave_fast = __all(lane_fast);
+            if (wave_fast) {   // every channel of the wave takes the chunk-start reference
 #pragma unroll
-                for (int I = 0; I < NB; ++I) {
-                    const float r = __shfl(exc[j], (I * (16 / RS)) * K::NCG + cg, 64);
-                    rhoI[I][j] = fastc ? 0.f : r;
+                for (int j = 0; j < 4; ++j) {
+                    ref[j] = 0.f;
+#pragma unroll
+                    for (int I = 0; I < NB; ++I) rhoI[I][j] = 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float rb = __shfl(exc[j], blk_src, 64);               // G before my block
+                    ref[j] = fastc[j] ? 0.f : rb;
+#pragma unroll
+                    for (int I = 0; I < NB; ++I) {
+                        const float r = __shfl(exc[j], (I * (16 / RS)) * K::NCG + cg, 64);
+                        rhoI[I][j] = fastc[j] ? 0.f : r;
+                    }
                 }
             }
             float al[RS][4];
@@ -668,7 +681,6 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             // segment I(I-1)/2 + J.  w is stored also when all factors are 1:
             // other waves may take block references, and then the tiles read w
             // for every channel.
-            const bool wave_fast = __all(lane_fast);
             if (seg == 0) *(f32x4 *)(sc + K::SC_GL + c0) = f32x4{fexp(glast[0]), fexp(glast[1]), fexp(glast[2]), fexp(glast[3])};
             if (wave_fast) {   // a uniform branch: no exponentials when every factor is 1
                 const f32x4 one{1.f, 1.f, 1.f, 1.f};
