@@ -179,10 +179,15 @@ __device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, int voff, int so
     else if constexpr (sizeof(T) == 4) return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
     else return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
 }
+// A store of more than 8 bytes reads its data registers after it issues, and
+// a vector ALU write to them must wait one cycle.  The compiler inserts that
+// wait only when the scalar offset is the constant 0, so 16-byte stores fold
+// the offset into the per-lane one (with an SGPR offset a following write has
+// been seen to replace the stored data).
 template <typename T>
 __device__ __forceinline__ void buf_store(T v, __amdgpu_buffer_rsrc_t r, int voff, int soff)
 {
-    if constexpr (sizeof(T) == 16) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 0);
+    if constexpr (sizeof(T) == 16) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff + soff, 0, 0);
     else __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, soff, 0);
 }
 

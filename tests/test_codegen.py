@@ -1,0 +1,77 @@
+"""Checks on the gfx950 machine code of the built library (no GPU needed).
+
+A vector memory store of more than 8 bytes reads its data registers after it
+issues; a vector ALU instruction that writes those registers must come at
+least one cycle later.  The compiler inserts that wait for every such store
+except a buffer store whose scalar offset is a register, and there the
+overwrite has been seen to replace part of the stored data (one column group
+of an output block, only under some timings).  The kernels therefore never
+give a wide buffer store a register scalar offset; these tests disassemble
+the device code objects of libkda.so and check both that rule and the
+property it protects.
+"""
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+PKG = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "kimi_delta_attention_fwd_amd")
+LIB = os.path.join(PKG, "libkda.so")
+OBJDUMP = "/opt/rocm/llvm/bin/llvm-objdump"
+
+WIDE_STORE = re.compile(r"^(buffer|global|flat)_store_dwordx(3|4)\s+(?:v\[\d+:\d+\],\s*)?v\[(\d+):(\d+)\]")
+BUF_STORE = re.compile(r"^buffer_store_dwordx(3|4)\s+v\[\d+:\d+\],\s*\S+,\s*s\[\d+:\d+\],\s*(\S+)")
+VALU_DST = re.compile(r"^v_\S+\s+(?:v(\d+)\b|v\[(\d+):(\d+)\])")
+
+
+@pytest.fixture(scope="module")
+def disassembly():
+    if not os.path.exists(LIB):
+        pytest.skip("libkda.so is not built")
+    if not os.path.exists(OBJDUMP):
+        pytest.skip("llvm-objdump not found")
+    with tempfile.TemporaryDirectory() as d:
+        lib = os.path.join(d, "libkda.so")
+        shutil.copy(LIB, lib)
+        # --offloading writes each bundled code object next to its input
+        subprocess.run([OBJDUMP, "--offloading", lib], cwd=d, check=True, capture_output=True)
+        objs = sorted(f for f in os.listdir(d) if f.endswith("gfx950"))
+        assert objs, "no gfx950 code object in libkda.so"
+        lines = []
+        for f in objs:
+            out = subprocess.run([OBJDUMP, "-d", "--mcpu=gfx950", os.path.join(d, f)],
+                                 check=True, capture_output=True, text=True).stdout
+            lines += [l.split("//")[0].strip() for l in out.splitlines()]
+    return [l for l in lines if l]
+
+
+def test_wide_buffer_stores_take_constant_scalar_offset(disassembly):
+    offenders = []
+    for l in disassembly:
+        m = BUF_STORE.match(l)
+        if m and m.group(2).startswith("s"):
+            offenders.append(l)
+    assert not offenders, f"{len(offenders)} wide buffer stores with a register scalar offset, e.g. {offenders[0]}"
+
+
+def test_wide_store_data_not_overwritten_at_once(disassembly):
+    n_stores = 0
+    bad = []
+    for i, l in enumerate(disassembly):
+        m = WIDE_STORE.match(l)
+        if not m:
+            continue
+        n_stores += 1
+        lo, hi = int(m.group(3)), int(m.group(4))
+        nxt = next((x for x in disassembly[i + 1:i + 4] if not x.endswith(">:") and not x.startswith(".")), "")
+        d = VALU_DST.match(nxt)
+        if d:
+            a = int(d.group(1) or d.group(2))
+            b = int(d.group(1) or d.group(3))
+            if not (b < lo or a > hi):
+                bad.append(f"{l}  ->  {nxt}")
+    assert n_stores > 0
+    assert not bad, f"{len(bad)} wide stores whose data is overwritten by the next instruction, e.g. {bad[0]}"
