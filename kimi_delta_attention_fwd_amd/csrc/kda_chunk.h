@@ -808,11 +808,16 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         __syncthreads();
         if (nch > 0) stage_b(0);
         __syncthreads();
+        // Stage A sets the pace of the first segment, where each operand wave
+        // shares its SIMD with a state wave that has time to spare: the operand
+        // waves issue first there (wave priority, this workgroup only).
         for (long ch = 0; ch < nch; ++ch) {
+            __builtin_amdgcn_s_setprio(3);
             if (ch + 1 < nch) {
                 stage_a(ch + 1);
                 if (ch + 2 < nch) prefetch_k((ch + 2) * C);
             }
+            __builtin_amdgcn_s_setprio(0);
             __syncthreads();
             if (ch + 1 < nch) stage_b(ch + 1);
             __syncthreads();
