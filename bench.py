@@ -23,7 +23,12 @@ measured with HIP events recorded around each launch on the stream the
 kernel runs on.  `traffic` is the HBM bytes per launch from rocprofv3
 FETCH_SIZE / WRITE_SIZE counters (scaled by the same counters on a plain
 copy kernel), taken from profiles/traffic.json when that file was made from
-the current kernel sources, else null.
+the current kernel sources, else null.  `copy_peak_gbs` is the bandwidth
+the library's streaming copy (kda_stream_copy: 16-byte nontemporal loads and
+stores, the decode kernels' access pattern) reaches on 1 GiB on the same GPU
+in the same run (bytes read plus bytes written, median of 10 timed copies),
+and `frac_of_copy` the kernel's achieved bandwidth as a fraction of it; the
+decode rooflines carry the same two fields.
 
 cpu_baseline: the float64 CPU oracle on the same mid workload (all of it,
 repeated until about ten seconds of CPU work are timed), OpenMP over the
@@ -304,6 +309,28 @@ def bench_varlen(args, torch, kda, kda_synth, stream, steps=3):
                 hbm_frac=round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
 
 
+def measure_copy_peak(torch, kda, stream, nbytes=1 << 30, reps=10):
+    """Achievable HBM bandwidth: the library's streaming copy of `nbytes`,
+    counting the bytes read and written, median of `reps` copies timed with
+    HIP events on `stream` after a few untimed ones."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        kda.kda_stream_copy(src, dst, nbytes, stream)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        kda.kda_stream_copy(src, dst, nbytes, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    del src, dst
+    ms.sort()
+    return 2 * nbytes / (ms[len(ms) // 2] * 1e-3) / 1e9
+
+
 def cpu_baseline(p, kda_synth, target_s=10.0, max_passes=8):
     """Float64 oracle on the whole mid workload (every sequence, head and token),
     repeated until about `target_s` seconds of CPU work have been timed."""
@@ -404,6 +431,10 @@ def main():
         if name in extras:
             result[key] = fn(args, torch, kda, kda_synth, stream)
             torch.cuda.empty_cache()
+    copy_gbs = measure_copy_peak(torch, kda, stream)
+    for roof in [result["roofline"]] + [result[k]["roofline"] for k in ("decode", "decode_multi") if k in result]:
+        roof["copy_peak_gbs"] = round(copy_gbs, 1)
+        roof["frac_of_copy"] = round(roof["achieved"] / copy_gbs, 4)
     print(json.dumps(result), flush=True)
 
 

@@ -332,6 +332,18 @@ kda_status_t kda_recurrent_fwd_ex_f32(const float *q, const float *k, const floa
                                       int N, int T, int H, int dk, int dv, int variant, void *stream);
 
 /*
+ * Bandwidth reference, not part of the attention computation: copies `bytes`
+ * from src to dst (device memory, 16-byte aligned, bytes a multiple of 16,
+ * non-overlapping) with 16-byte nontemporal loads and stores, the access
+ * pattern the decode kernels stream the state with.  Timing it gives the
+ * achievable HBM bandwidth that the streaming kernels are compared against.
+ * bytes = 0 is a no-op.  Errors: KDA_ERR_NULL_POINTER, KDA_ERR_BAD_SHAPE
+ * (bytes not a multiple of 16), KDA_ERR_MISALIGNED, KDA_ERR_ALIASING,
+ * KDA_ERR_HIP.
+ */
+kda_status_t kda_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+/*
  * Host-side check of a cu_seqlens array held in HOST memory: N >= 0,
  * cu[0] = 0, non-decreasing, cu[N] = T_total.  Returns KDA_OK or
  * KDA_ERR_BAD_SHAPE / KDA_ERR_NULL_POINTER.

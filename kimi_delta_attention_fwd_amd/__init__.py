@@ -27,7 +27,7 @@ __all__ = [
     "kda_chunk_fwd_ex", "kda_chunk_fwd_ex_f32", "kda_chunk_fwd_varlen_ex", "kda_chunk_fwd_varlen_ex_f32",
     "kda_recurrent_fwd_ex", "kda_recurrent_fwd_ex_f32", "variant",
     "kda_recurrent_step", "kda_recurrent_step_f32", "kda_recurrent_fwd", "kda_recurrent_fwd_f32",
-    "kda_check_cu_seqlens_host",
+    "kda_check_cu_seqlens_host", "kda_stream_copy",
     "kda_status_string", "kda_last_error", "kda_version",
     "chunk_fwd", "chunk_fwd_varlen", "recurrent_step", "recurrent_fwd",
 ]
@@ -91,6 +91,8 @@ def load():
     lib.kda_chunk_segmented_workspace_bytes.restype = Z
     lib.kda_chunk_auto_segments.argtypes = [I] * 7
     lib.kda_chunk_auto_segments.restype = I
+    lib.kda_stream_copy.argtypes = [P, P, Z, P]
+    lib.kda_stream_copy.restype = I
     lib.kda_check_cu_seqlens_host.argtypes = [P, I, I]
     lib.kda_check_cu_seqlens_host.restype = I
     lib.kda_status_string.argtypes = [I]
@@ -264,6 +266,12 @@ def kda_recurrent_fwd_ex_f32(q, k, v, log_alpha, beta, S, out, N, T, H, dk, dv, 
     _check("kda_recurrent_fwd_ex_f32", load().kda_recurrent_fwd_ex_f32(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(out), N, T, H, dk, dv, variant,
         _stream(stream)))
+
+
+def kda_stream_copy(src, dst, nbytes, stream=None):
+    """Bandwidth reference: copy nbytes from src to dst with the decode kernels'
+    16-byte nontemporal access pattern."""
+    _check("kda_stream_copy", load().kda_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
 
 
 def kda_check_cu_seqlens_host(cu_seqlens_host, N, T_total) -> int:

@@ -294,7 +294,9 @@ kda_status_t step_common(bool f32, const void *q, const void *k, const void *v, 
         return fail(KDA_ERR_UNSUPPORTED, "dk and dv must be 16, 32, 64 or 128 (got %d, %d)", dk, dv);
     const uint64_t nheads = (uint64_t)N * (uint64_t)H;
     const uint64_t ntok = nheads * (uint64_t)T;
-    if (nheads > (uint64_t)INT32_MAX || ntok * 128u > (uint64_t)1 << 60) return fail(KDA_ERR_BAD_SHAPE, "problem too large");
+    // the decode grid has up to 4 workgroups per head
+    if (nheads > (uint64_t)INT32_MAX / 4 || ntok * 128u > (uint64_t)1 << 60)
+        return fail(KDA_ERR_BAD_SHAPE, "problem too large");
     if (nheads == 0 || T == 0) return ok();
     if (!q || !k || !v || (gate != 2 && !log_alpha) || !beta || !S || !out)
         return fail(KDA_ERR_NULL_POINTER, "q, k, v, log_alpha, beta, S and out are required");
@@ -498,6 +500,18 @@ kda_status_t kda_recurrent_fwd_f32(const float *q, const float *k, const float *
                                    void *stream)
 {
     return step_common(true, q, k, v, log_alpha, beta, S, out, N, H, dk, dv, stream, T, true);
+}
+
+kda_status_t kda_stream_copy(const void *src, void *dst, size_t bytes, void *stream)
+{
+    if (bytes == 0) return ok();
+    if (!src || !dst) return fail(KDA_ERR_NULL_POINTER, "src and dst are required");
+    if (bytes % 16) return fail(KDA_ERR_BAD_SHAPE, "bytes must be a multiple of 16 (got %zu)", bytes);
+    if (!aligned(src, 16) || !aligned(dst, 16)) return fail(KDA_ERR_MISALIGNED, "src and dst must be 16-byte aligned");
+    if (overlap(src, bytes, dst, bytes)) return fail(KDA_ERR_ALIASING, "src and dst overlap");
+    const hipError_t e = kda::launch_stream_copy(src, dst, (long)(bytes / 16), (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "copy kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 kda_status_t kda_check_cu_seqlens_host(const int32_t *cu, int N, int T_total)

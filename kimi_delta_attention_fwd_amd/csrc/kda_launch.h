@@ -53,5 +53,6 @@ bool chunk_fits(bool f32, int dk, int BV, int C);
 // log_alpha, beta laid out [N, T, H, d]).  Defined in kda_decode.hip.
 hipError_t launch_decode(const DecodeArgs &, bool f32);
 hipError_t launch_decode_multi(const DecodeArgs &, int T, bool f32);
+hipError_t launch_stream_copy(const void *src, void *dst, long n16, hipStream_t stream);
 
 }  // namespace kda

@@ -280,3 +280,15 @@ def test_raw_input_variant_validation(lib):
     g_bytes = 2 * 100 * 4 * 64 * 2
     assert ex(8, out=A + 192 * MB + g_bytes) == 1 and "workspace" in kda.kda_last_error()
     assert ex(8, out=A + 192 * MB + g_bytes - 16) == 6
+
+
+def test_stream_copy_validation(lib):
+    # every check runs before the launch, so none of these touches a GPU
+    assert lib.kda_stream_copy(A, A + 64 * MB, 0, None) == 0
+    assert lib.kda_stream_copy(None, A, 16, None) == 1 and lib.kda_stream_copy(A, None, 16, None) == 1
+    assert lib.kda_stream_copy(A, A + 64 * MB, 24, None) == 2
+    assert "multiple of 16" in kda.kda_last_error()
+    assert lib.kda_stream_copy(A + 8, A + 64 * MB, 32, None) == 4
+    assert lib.kda_stream_copy(A, A + 64 * MB + 4, 32, None) == 4
+    assert lib.kda_stream_copy(A, A + 16, 32, None) == 6      # the ranges overlap
+    assert lib.kda_stream_copy(A + 16, A, 32, None) == 6

@@ -569,7 +569,10 @@ def test_long_workload_sampled(dev):
 # ---------------------------------------------------------------- decode step
 @pytest.mark.parametrize("N,H,dk,dv,dtype", [(3, 2, 64, 32, "bf16"), (2, 3, 128, 128, "bf16"),
                                              (4, 1, 16, 128, "f32"), (2, 2, 32, 64, "f32"),
-                                             (5, 2, 128, 16, "f32")])
+                                             (5, 2, 128, 16, "f32"),
+                                             # head counts that are multiples of 8, several
+                                             # workgroups per head: the XCD-grouped mapping
+                                             (4, 2, 64, 128, "f32"), (2, 4, 128, 64, "bf16")])
 def test_decode_steps(dev, N, H, dk, dv, dtype):
     steps = 40
     note(f"case decode N{N} H{H} dk{dk} dv{dv} {dtype} x{steps} steps")
@@ -692,3 +695,19 @@ def test_decode_is_deterministic(dev):
     o2 = [kda.recurrent_step(d.q[t], d.k[t], d.v[t], d.log_alpha[t], d.beta[t], S2) for t in range(3)]
     torch.cuda.synchronize()
     assert torch.equal(S1, S2) and all(torch.equal(a, b) for a, b in zip(o1, o2))
+
+
+@pytest.mark.parametrize("n16", [1, 256 * 1000 + 37])
+def test_stream_copy_is_exact(dev, n16):
+    # the bandwidth reference copies bit for bit, a partial last workgroup included,
+    # and the guard bands around dst
+    note(f"case stream copy {n16} x 16 B")
+    g = torch.Generator(device=dev).manual_seed(61)
+    src = torch.randn(4 * n16, generator=g, device=dev)
+    pad = 64
+    big = torch.full((4 * n16 + 2 * pad,), 5.0, device=dev)
+    dst = big[pad:pad + 4 * n16]
+    kda.kda_stream_copy(src, dst, 16 * n16)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    assert torch.all(big[:pad] == 5.0) and torch.all(big[pad + 4 * n16:] == 5.0)
