@@ -19,9 +19,8 @@
 // spans ceil(dv / RPP) workgroups (4 at d = 128), each lane holds one row
 // slice (four 16-byte loads in flight), and the head's token data is read by
 // each of them from cache: many small workgroups stream faster than a few
-// that keep several rows per lane in flight.  The multi-token kernel keeps
-// one workgroup per head with every row of the head in flight, since its
-// token loop waits on each token's data and the extra rows cover that wait.
+// that keep several rows per lane in flight.  The multi-token kernel splits
+// heads the same way and stages its tokens in LDS.
 #pragma once
 
 #include "kda_device.h"
@@ -158,66 +157,103 @@ decode_step_kernel(const In *__restrict__ q, const In *__restrict__ k, const In 
 // program per sequence, value head and value block looping the update over
 // the tokens).  Token t of sequence n sits at row (n T + t) H + h of the
 // [N, T, H, d] inputs.  Per token the arithmetic is the decode step's, in the
-// same order, so T = 1 matches kda_recurrent_step bit for bit.
+// same order, so T tokens match T calls of kda_recurrent_step bit for bit.
+//
+// Workgroups split a head's rows as in the single step.  The token loop would
+// wait on every token's loads, so the workgroup first stages a tile of up to
+// TT tokens in LDS (k, q, the decay factors alpha, beta, and v of its own
+// rows), with one set of loads in flight for the whole tile, and then runs
+// the tile's tokens from LDS.  Each alpha is computed once per workgroup.
 template <typename In, int DK, bool VAR>
 __global__ void __launch_bounds__(256)
 decode_multi_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
                     const float *__restrict__ log_alpha, const float *__restrict__ beta,
-                    float *__restrict__ S, In *__restrict__ out, int T, int H, int dv, int gate_arg,
-                    int add_arg, int prep_arg)
+                    float *__restrict__ S, In *__restrict__ out, int T, int H, int dv, int xcd_map,
+                    int gate_arg, int add_arg, int prep_arg)
 {
     const int gate = VAR ? gate_arg : 0, add = VAR ? add_arg : 0, prep = VAR ? prep_arg : 0;
     typedef In In4 __attribute__((ext_vector_type(4)));
     constexpr int LPR = DK / 16;
-    constexpr int RPP = 256 / LPR;
-    constexpr int MAXP = (128 + RPP - 1) / RPP;
-    const long head = blockIdx.x;
+    constexpr int RPP = 256 / LPR;        // rows per workgroup, as in the single step
+    constexpr int TT = 16;                // tokens staged per tile
+    constexpr int C4 = DK / 4;            // 4-channel groups per token
+    __shared__ __attribute__((aligned(16))) float s_a[TT][DK], s_k[TT][DK], s_q[TT][DK], s_v[TT][RPP], s_b[TT];
+    const int nsplit = (dv + RPP - 1) / RPP;
+    long head;
+    int part;
+    if (xcd_map) {
+        // workgroups are dealt to the 8 XCDs round-robin: the nsplit
+        // workgroups of a head share an XCD, so its tokens come from HBM once
+        // (the head count is a multiple of 8 here)
+        const long slot = blockIdx.x >> 3;
+        head = (slot / nsplit) * 8 + (blockIdx.x & 7);
+        part = (int)(slot % nsplit);
+    } else {
+        head = blockIdx.x / nsplit;
+        part = blockIdx.x % nsplit;
+    }
     const long n = head / H, h = head % H;
     const int tid = threadIdx.x, sub = tid % LPR, rloc = tid / LPR;
+    const int row = part * RPP + rloc;
+    const bool active = row < dv;         // whole groups of LPR lanes share a row
 
-    f32x4 s[MAXP][4];
+    f32x4 s[4];
+    if (active) {
+        const float *src = S + (head * dv + row) * DK + 4 * sub;
 #pragma unroll
-    for (int p = 0; p < MAXP; ++p) {
-        const int row = p * RPP + rloc;
-        if (row < dv) {
-            const float *src = S + (head * dv + row) * DK + 4 * sub;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) s[p][u] = __builtin_nontemporal_load((const f32x4 *)(src + 4 * LPR * u));
-        }
+        for (int u = 0; u < 4; ++u) s[u] = __builtin_nontemporal_load((const f32x4 *)(src + 4 * LPR * u));
     }
-    for (int t = 0; t < T; ++t) {
-        const long tok = (n * T + t) * H + h;
-        f32x4 a[4], kk[4], qq[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const long c = tok * DK + 4 * (sub + LPR * u);
-            const f32x4 la = decay_logs<In>(log_alpha, c, tok, gate, prep);
-            const In4 kv = *(const In4 *)(k + c);
-            const In4 qv = *(const In4 *)(q + c);
+    for (int t0 = 0; t0 < T; t0 += TT) {
+        const int nt = T - t0 < TT ? T - t0 : TT;
+        __syncthreads();   // the previous tile's reads are done
+        for (int i = tid; i < nt * C4; i += 256) {
+            const int tl = i / C4, c = 4 * (i % C4);
+            const long tok = (n * T + t0 + tl) * H + h;
+            const f32x4 la = decay_logs<In>(log_alpha, tok * DK + c, tok, gate, prep);
+            const In4 kv = *(const In4 *)(k + tok * DK + c);
+            const In4 qv = *(const In4 *)(q + tok * DK + c);
+            f32x4 av, kf, qf;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                a[u][j] = __expf(la[j]);
-                kk[u][j] = tof(kv[j]);
-                qq[u][j] = tof(qv[j]);
+                av[j] = __expf(la[j]);
+                kf[j] = tof(kv[j]);
+                qf[j] = tof(qv[j]);
             }
+            *(f32x4 *)&s_a[tl][c] = av;
+            *(f32x4 *)&s_k[tl][c] = kf;
+            *(f32x4 *)&s_q[tl][c] = qf;
         }
-        if (prep) {
-            normalise16<LPR>(kk);
-            normalise16<LPR>(qq);
+        for (int i = tid; i < nt * RPP; i += 256) {
+            const int tl = i / RPP, r = i % RPP;
+            const long tok = (n * T + t0 + tl) * H + h;
+            if (part * RPP + r < dv) s_v[tl][r] = tof(v[tok * dv + part * RPP + r]);
         }
-        const float b = beta[tok];
+        if (tid < nt) s_b[tid] = beta[(n * T + t0 + tid) * H + h];
+        __syncthreads();
+        for (int tl = 0; tl < nt; ++tl) {
+            f32x4 a[4], kk[4], qq[4];
 #pragma unroll
-        for (int p = 0; p < MAXP; ++p) {
-            const int row = p * RPP + rloc;
-            if (row < dv) {
-                const float vi = tof(v[tok * dv + row]);
+            for (int u = 0; u < 4; ++u) {
+                const int c = 4 * (sub + LPR * u);
+                a[u] = *(const f32x4 *)&s_a[tl][c];
+                kk[u] = *(const f32x4 *)&s_k[tl][c];
+                qq[u] = *(const f32x4 *)&s_q[tl][c];
+            }
+            if (prep) {
+                normalise16<LPR>(kk);
+                normalise16<LPR>(qq);
+            }
+            const float b = s_b[tl];
+            if (active) {
+                const long tok = (n * T + t0 + tl) * H + h;
+                const float vi = s_v[tl][rloc];
                 float pred = 0.f;
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        s[p][u][j] *= a[u][j];
-                        pred += s[p][u][j] * kk[u][j];
+                        s[u][j] *= a[u][j];
+                        pred += s[u][j] * kk[u][j];
                     }
                 pred = add ? 0.f : group_sum<LPR>(pred);
                 const float e = b * (vi - pred);
@@ -226,38 +262,37 @@ decode_multi_kernel(const In *__restrict__ q, const In *__restrict__ k, const In
                 for (int u = 0; u < 4; ++u)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        s[p][u][j] += e * kk[u][j];
-                        o += s[p][u][j] * qq[u][j];
+                        s[u][j] += e * kk[u][j];
+                        o += s[u][j] * qq[u][j];
                     }
                 o = group_sum<LPR>(o);
                 if (sub == 0) out[tok * dv + row] = fromf<In>(o);
             }
         }
     }
+    if (active) {
+        float *dst = S + (head * dv + row) * DK + 4 * sub;
 #pragma unroll
-    for (int p = 0; p < MAXP; ++p) {
-        const int row = p * RPP + rloc;
-        if (row < dv) {
-            float *dst = S + (head * dv + row) * DK + 4 * sub;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(s[p][u], (f32x4 *)(dst + 4 * LPR * u));
-        }
+        for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(s[u], (f32x4 *)(dst + 4 * LPR * u));
     }
 }
 
 template <typename In, int DK>
 hipError_t launch_decode_multi_t(const DecodeArgs &a, int T)
 {
-    const long grid = (long)a.N * a.H;
+    constexpr int RPP = 256 / (DK / 16);
+    const long nheads = (long)a.N * a.H, nsplit = (a.dv + RPP - 1) / RPP;
+    const long grid = nheads * nsplit;   // workgroups: RPP rows of one head each
     if (grid == 0) return hipSuccess;
+    const int xcd = (nsplit > 1 && nheads % 8 == 0) ? 1 : 0;
     if (a.gate != 0 || a.add != 0 || a.prep != 0)
         hipLaunchKernelGGL((decode_multi_kernel<In, DK, true>), dim3((unsigned)grid), dim3(256), 0, a.stream,
                            (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S,
-                           (In *)a.out, T, a.H, a.dv, a.gate, a.add, a.prep);
+                           (In *)a.out, T, a.H, a.dv, xcd, a.gate, a.add, a.prep);
     else
         hipLaunchKernelGGL((decode_multi_kernel<In, DK, false>), dim3((unsigned)grid), dim3(256), 0, a.stream,
                            (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S,
-                           (In *)a.out, T, a.H, a.dv, 0, 0, 0);
+                           (In *)a.out, T, a.H, a.dv, xcd, 0, 0, 0);
     return hipGetLastError();
 }
 

@@ -636,7 +636,11 @@ def test_decode_equals_chunk_prefill_on_same_stream(dev):
 # ---------------------------------------------------------------- multi-token decode
 @pytest.mark.parametrize("N,T,H,dk,dv,dtype", [(3, 2, 2, 64, 32, "bf16"), (2, 5, 3, 128, 128, "bf16"),
                                                (4, 16, 1, 16, 128, "f32"), (2, 7, 2, 32, 64, "f32"),
-                                               (5, 3, 2, 128, 16, "bf16"), (1, 64, 2, 128, 128, "bf16")])
+                                               (5, 3, 2, 128, 16, "bf16"), (1, 64, 2, 128, 128, "bf16"),
+                                               # head counts that are multiples of 8 (a head's
+                                               # workgroups grouped on one XCD), one and two token tiles
+                                               (4, 5, 2, 128, 128, "bf16"), (2, 3, 4, 64, 128, "f32"),
+                                               (2, 20, 4, 128, 128, "bf16")])
 def test_recurrent_fwd_matches_oracle(dev, N, T, H, dk, dv, dtype):
     note(f"case multi-token decode N{N} T{T} H{H} dk{dk} dv{dv} {dtype}")
     p = kda_synth.prefill(N, T, H, dk, dv, dtype=dtype, s0_sigma=0.1, seed=61 + T + dk + dv, device=dev)
@@ -649,8 +653,8 @@ def test_recurrent_fwd_matches_oracle(dev, N, T, H, dk, dv, dtype):
 
 def test_recurrent_fwd_equals_single_steps(dev):
     """T tokens in one launch give bit for bit what T single-step launches give."""
-    for dtype in ("bf16", "f32"):
-        N, T, H, dk, dv = 3, 6, 2, 128, 64
+    for dtype, (N, T, H, dk, dv) in (("bf16", (3, 6, 2, 128, 64)), ("f32", (3, 6, 2, 128, 64)),
+                                     ("bf16", (4, 19, 2, 128, 128)), ("f32", (2, 17, 4, 64, 128))):
         note(f"case multi-token vs single steps N{N} T{T} H{H} dk{dk} dv{dv} {dtype} (bitwise)")
         p = kda_synth.prefill(N, T, H, dk, dv, dtype=dtype, s0_sigma=0.1, seed=67, device=dev)
         S1 = p.S0.clone()
