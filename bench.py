@@ -9,7 +9,9 @@ Before the W warm-up steps, about 100 ms of untimed launches let the GPU
 clocks settle (they ramp up over the first ~30 ms of load).
 
 Extra fields measure the other entry points on their own workloads:
-  decode        256 sequences x 32 heads, 1024 one-token steps (steps/s)
+  decode        256 sequences x 32 heads, 1024 one-token steps (steps/s), one
+                launch per step from the host and, as graph_steps_per_s, the
+                same steps captured in one HIP graph
   decode_multi  the same sizes, 4 tokens per sequence and launch (tokens/s)
   fused_prep    mid sizes from raw q, k and bf16 gate pre-activations, against
                 separate preparation passes feeding the plain kernel (ms)
@@ -184,10 +186,26 @@ def bench_decode(args, torch, kda, kda_synth, stream):
     times = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     kms = sum(times) / steps
     nbytes = decode_bytes(N * H, dk, dv)
-    del d, S
+    # The same steps captured once in a HIP graph and replayed: no host work
+    # between launches.  The capture records on torch's capture stream.
+    g = torch.cuda.CUDAGraph()
+    Sg = d.S0.clone()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        hs = torch.cuda.current_stream().cuda_stream
+        for t in range(steps):
+            kda.kda_recurrent_step(d.q[t], d.k[t], d.v[t], d.log_alpha[t], d.beta[t], Sg, out, N, H, dk, dv, hs)
+    g.replay()   # untimed
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    gwall = time.perf_counter() - t0
+    del g, Sg, d, S
     return dict(
         workload="decode: 256 sequences x H=32, dk=dv=128, bf16 q/k/v, fp32 state, 1024 steps",
         steps_per_s=steps / wall, tokens_per_s=N * steps / wall, ms_per_step=wall * 1e3 / steps,
+        graph_steps_per_s=steps / gwall, graph_ms_per_step=gwall * 1e3 / steps,
         kernel_ms_mean=kms, kernel_ms_median=times[steps // 2],
         roofline=dict(bound="hbm", achieved=round(nbytes / (kms * 1e-3) / 1e9, 1), peak=HBM_PEAK_GBS,
                       unit="GB/s", frac=round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

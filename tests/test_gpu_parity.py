@@ -715,3 +715,53 @@ def test_stream_copy_is_exact(dev, n16):
     torch.cuda.synchronize()
     assert torch.equal(dst, src)
     assert torch.all(big[:pad] == 5.0) and torch.all(big[pad + 4 * n16:] == 5.0)
+
+
+def test_graph_capture_replays_match_eager(dev):
+    """Decode steps, a multi-token launch and chunk prefills (single pass and
+    segmented, whose three launches share a workspace) captured in one HIP
+    graph: every replay gives the eager result bit for bit, with eager work
+    and synchronisation between the replays."""
+    note("case HIP graph: 3 decode steps, multi T4, chunk single pass + 3 segments")
+    bf = torch.bfloat16
+    N, H, dk, dv = 8, 4, 128, 128
+    d = kda_synth.decode(N, H, dk, dv, 3, seed=71, device=dev)
+    pm = kda_synth.prefill(N, 4, H, dk, dv, dtype="bf16", s0_sigma=0.1, seed=72, device=dev)
+    pc = kda_synth.prefill(1, 300, 2, 64, 64, dtype="bf16", s0_sigma=0.1, seed=73, device=dev)
+    S_dec, S_multi = torch.empty_like(d.S0), torch.empty_like(pm.S0)
+    outs = [torch.empty((N, H, dv), dtype=bf, device=dev) for _ in range(3)]
+    out_m = torch.empty((N, 4, H, dv), dtype=bf, device=dev)
+    out_c = [torch.empty_like(pc.v) for _ in range(2)]
+    sf_c = [torch.empty_like(pc.S0) for _ in range(2)]
+    nseg = 3
+    ws_bytes = kda.kda_chunk_segmented_workspace_bytes(1, 2, 64, 64, nseg)
+    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device=dev)
+
+    def work():   # on the current stream (the capture stream inside the graph context)
+        for t in range(3):
+            kda.kda_recurrent_step(d.q[t], d.k[t], d.v[t], d.log_alpha[t], d.beta[t], S_dec, outs[t], N, H, dk, dv)
+        kda.kda_recurrent_fwd(pm.q, pm.k, pm.v, pm.log_alpha, pm.beta, S_multi, out_m, N, 4, H, dk, dv)
+        kda.kda_chunk_fwd(pc.q, pc.k, pc.v, pc.log_alpha, pc.beta, pc.S0, out_c[0], sf_c[0], 1, 300, 2, 64, 64, 64)
+        kda.kda_chunk_fwd_segmented(pc.q, pc.k, pc.v, pc.log_alpha, pc.beta, pc.S0, out_c[1], sf_c[1],
+                                    1, 300, 2, 64, 64, 64, nseg, ws, ws_bytes)
+
+    results = lambda: [S_dec, S_multi, out_m] + outs + out_c + sf_c
+    S_dec.copy_(d.S0)
+    S_multi.copy_(pm.S0)
+    work()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in results()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for replay in range(3):
+        S_dec.copy_(d.S0)   # eager work between the replays
+        S_multi.copy_(pm.S0)
+        for x in [out_m] + outs + out_c + sf_c:
+            x.fill_(float("nan"))
+        ws.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(results(), ref)):
+            assert torch.equal(a, b), f"replay {replay}: result {i} differs from the eager run"
