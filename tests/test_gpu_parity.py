@@ -549,6 +549,49 @@ def test_mid_workload_sampled(dev):
     assert_close("mid sampled", o_gpu, s_gpu, o_ref, s_ref, TOL["bf16"])
 
 
+def test_prep_workload_sampled(dev):
+    """The fused input preparation at the sizes the bench times it on: the mid
+    sizes with raw q, k and bf16 gate pre-activations (one launch of the
+    raw-input kernel), sampled heads against the oracle on the raw inputs."""
+    w = kda_synth.WORKLOADS["mid"]
+    B, T, H, dk, dv, C = w["B"], w["T"], w["H"], w["dk"], w["dv"], w["C"]
+    note("case fused preparation at mid sizes: B4 H32 T8192 d128, raw q, k, bf16 g (4 sampled heads)")
+    p = kda_synth.prefill_raw(B, T, H, dk, dv, dtype="bf16", g_mu=w["g_mu"], g_sigma=w["g_sigma"],
+                              seed=kda_synth.SEEDS["mid"], device=dev)
+    out = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    sf = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    kda.kda_chunk_fwd_ex(p.q, p.k, p.v, p.log_alpha, p.beta, None, out, sf, B, T, H, dk, dv, C,
+                         kda.variant(raw=True), 1, None, 0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(sf).all()
+    pairs = [(0, 2), (1, 29), (2, 14), (3, 31)]
+    pick = lambda t: torch.stack([t[b, :, h] for b, h in pairs]).unsqueeze(2)
+    qn, kn, la = oracle.prepare(f64(pick(p.q)), f64(pick(p.k)), f64(pick(p.log_alpha)), gate="channel")
+    o_ref, s_ref = oracle.forward(qn, kn, f64(pick(p.v)), la, f64(torch.stack([p.beta[b, :, h] for b, h in pairs]).unsqueeze(2)))
+    o_gpu = np.stack([f64(out[b, :, h]) for b, h in pairs])[:, :, None]
+    s_gpu = np.stack([f64(sf[b, h]) for b, h in pairs])[:, None]
+    assert_close("prep sampled", o_gpu, s_gpu, o_ref, s_ref, TOL["bf16"])
+
+
+def test_decode_multi_workload_sampled(dev):
+    """The multi-token launch the bench times: the decode workload's sizes
+    (256 sequences x 32 heads, d = 128) with 4 tokens per launch, sampled heads
+    against the oracle."""
+    w = kda_synth.WORKLOADS["decode"]
+    N, H, dk, dv, T = w["N"], w["H"], w["dk"], w["dv"], 4
+    note("case multi-token decode at decode sizes: N256 H32 d128, T4 (12 sampled heads)")
+    p = kda_synth.prefill(N, T, H, dk, dv, dtype="bf16", g_mu=w["g_mu"], g_sigma=w["g_sigma"],
+                          beta=w["beta"], s0_sigma=w["s0_sigma"], seed=kda_synth.SEEDS["decode"], device=dev)
+    S = p.S0.clone()
+    out = kda.recurrent_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S)
+    torch.cuda.synchronize()
+    pairs = [(n, h) for n, h in zip(range(5, 256, 21), range(1, 32, 3))]
+    o_ref, s_ref = sampled(p, pairs)
+    o_gpu = np.stack([f64(out[n, :, h]) for n, h in pairs])[:, :, None]
+    s_gpu = np.stack([f64(S[n, h]) for n, h in pairs])[:, None]
+    assert_close("multi-token decode sampled", o_gpu, s_gpu, o_ref, s_ref, TOL["bf16"])
+
+
 def test_long_workload_sampled(dev):
     """Both schedules of the long workload: the segment-parallel one with the
     library's segment count (what bench.py times) and the single pass."""
