@@ -387,7 +387,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(this build runs on a single MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
+              "(the kernels run on a single MI355X; batches would shard by sequence or head, one long "
+              "sequence by segments of its tokens)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -95,7 +95,7 @@ def prepare(q_raw, k_raw, g=None, gate: str = "channel"):
     q and k are divided by their L2 norm over the key channels (the "Kimi K3
     notes 1: KDA" page, sect. 4: q and k pass a feature map and an L2
     normalisation before the recurrence); a zero row stays zero.  The gate is
-    log_alpha = -softplus(g) = -log(1 + e^g), the parameterisation this build
+    log_alpha = -softplus(g) = -log(1 + e^g), the parameterisation the library
     reads for the pages' alpha in (0, 1] (elementwise, per channel, or one
     value per token and head broadcast to every channel; "none" gives 0).
     Returns (q, k, log_alpha [.., H, dk]).
