@@ -17,6 +17,8 @@ Extra fields measure the other entry points on their own workloads:
                 separate preparation passes feeding the plain kernel (ms)
   long_context  B=1, H=16, T=65536 with an initial state (tokens/s)
   varlen        8 packed sequences of U[2048, 16384] tokens x 16 heads (tokens/s)
+  small_configs the tiny fp32 and small bf16 prefills, bound by launch latency
+                (microseconds per launch and tokens/s, no roofline)
 
 roofline: the chunk kernel against HBM bandwidth.  `achieved` is the
 algorithmic bytes of one launch (one read of every input, one write of
@@ -349,6 +351,33 @@ def measure_copy_peak(torch, kda, stream, nbytes=1 << 30, reps=10):
     return 2 * nbytes / (ms[len(ms) // 2] * 1e-3) / 1e9
 
 
+def bench_small(args, torch, kda, kda_synth, stream, launches=200):
+    """The two small configurations, which are bound by launch latency and run
+    from cache: tiny (fp32, B=1 H=1 T=64 d=16, C=16) as microseconds per launch,
+    and small (bf16, B=2 H=4 T=1024 d=64, C=64, with S0) as tokens/s.  Kernel
+    time from HIP events around each launch; host time per launch from the wall
+    clock over back-to-back launches.  No roofline claim."""
+    res = {}
+    for name in ("tiny", "small"):
+        w = kda_synth.WORKLOADS[name]
+        p = kda_synth.workload(name, device="cuda")
+        B, T, H, dk, dv, C = w["B"], w["T"], w["H"], w["dk"], w["dv"], w["C"]
+        out = torch.empty_like(p.v)
+        sf = torch.empty((B, H, dv, dk), dtype=torch.float32, device="cuda")
+        fn = kda.kda_chunk_fwd_f32 if w["dtype"] == "f32" else kda.kda_chunk_fwd
+        h = stream.cuda_stream
+
+        def launch():
+            fn(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out, sf, B, T, H, dk, dv, C, h)
+
+        wall, kms = time_launches(launch, stream, launches, 20, torch)
+        res[name] = dict(workload=f"{name}: B={B} H={H} T={T} dk=dv={dk} {w['dtype']} C={C}",
+                         kernel_us=round(kms * 1e3, 2), us_per_launch=round(wall * 1e6 / launches, 2),
+                         tokens_per_s=round(B * T * launches / wall, 1))
+        del p, out, sf
+    return res
+
+
 def cpu_baseline(p, kda_synth, target_s=10.0, max_passes=8):
     """Float64 oracle on the whole mid workload (every sequence, head and token),
     repeated until about `target_s` seconds of CPU work have been timed."""
@@ -375,9 +404,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--extras", default="decode,multi,long,varlen,prep",
+    ap.add_argument("--extras", default="decode,multi,long,varlen,prep,small",
                     help="comma-separated extra workloads to run after the mid prefill "
-                         "(decode, long, varlen; 'none' for the mid prefill only)")
+                         "(decode, multi, long, varlen, prep, small; 'none' for the mid prefill only)")
     ap.add_argument("--no-extras", action="store_true", help="same as --extras none")
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="fewer decode steps (profiling runs; the default is the workload's 1024)")
@@ -441,12 +470,12 @@ def main():
     del p_mid
     torch.cuda.empty_cache()
     extras = set() if args.no_extras or args.extras == "none" else set(args.extras.split(","))
-    unknown = extras - {"decode", "multi", "long", "varlen", "prep"}
+    unknown = extras - {"decode", "multi", "long", "varlen", "prep", "small"}
     if unknown:
         raise SystemExit(f"unknown --extras entries: {sorted(unknown)}")
     for name, key, fn in (("decode", "decode", bench_decode), ("multi", "decode_multi", bench_decode_multi),
                           ("long", "long_context", bench_long), ("varlen", "varlen", bench_varlen),
-                          ("prep", "fused_prep", bench_prep)):
+                          ("prep", "fused_prep", bench_prep), ("small", "small_configs", bench_small)):
         if name in extras:
             result[key] = fn(args, torch, kda, kda_synth, stream)
             torch.cuda.empty_cache()
