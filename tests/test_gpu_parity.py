@@ -450,6 +450,26 @@ def test_chunk_raw_inputs(dev, gate, write, dtype):
         assert_close(f"raw {gate}/{write} segments={segments}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
 
 
+@pytest.mark.parametrize("dtype,dk,C", [("bf16", 128, 64), ("bf16", 64, 64), ("f32", 64, 32)])
+def test_chunk_raw_inputs_strong_and_mixed_decay(dev, dtype, dk, C):
+    """Raw gates where some chunks decay by more than 80 nats in some key
+    channels (g = 2: about 2.1 nats per token, 34 per 16-token block): waves
+    whose channels all stay within 80 nats over the chunk take the products
+    path, the others the log-domain path with block references, inside one
+    sequence; per-channel and scalar gates."""
+    B, T, H, dv = 2, 300, 2, 64
+    note(f"case raw inputs, strong and mixed decay: B{B} T{T} H{H} dk{dk} dv{dv} {dtype} C{C}")
+    p = kda_synth.prefill_raw(B, T, H, dk, dv, dtype=dtype, s0_sigma=0.1, seed=97, device=dev)
+    p.log_alpha[:, 70:140, :, : dk // 4] = 2.0      # a quarter of the key channels (one operand wave's)
+    p.log_alpha[1, 200:260, 1] = 1.5                 # every channel of one head
+    for gate in ("channel", "scalar"):
+        o_ref, s_ref = oracle_raw(p, gate)
+        out, sf = kda.chunk_fwd(p.q, p.k, p.v, raw_gate_arg(p, gate), p.beta, S0=p.S0, C=C, segments=1,
+                                gate=gate, raw=True)
+        torch.cuda.synchronize()
+        assert_close(f"raw strong/mixed {gate}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+
+
 def test_chunk_raw_inputs_varlen_and_zero_rows(dev):
     lengths = [150, 1, 0, 97]
     note(f"case raw inputs varlen lengths {lengths} H2 d128 bf16, zero q and k rows")
