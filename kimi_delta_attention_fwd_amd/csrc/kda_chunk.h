@@ -317,7 +317,7 @@ struct ChunkCfg {
 // the dv real rows start at zero.  After the segment the real rows hold N and
 // the virtual rows M of S_end = S_start M + N, written to seg_map[(head, seg)];
 // no output is written and q is not read.
-template <typename In, int DK, int BV, int C, bool MAP, bool VAR>
+template <typename In, int DK, int BV, int C, bool MAP, int VAR>
 __global__ void __launch_bounds__((ChunkCfg<In, DK, BV, C>::NT), 1)
 chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
                  const float *__restrict__ log_alpha, const float *__restrict__ beta,
@@ -325,8 +325,11 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                  const int *__restrict__ cu_seqlens, int T, int H, int dv, int xcd_map,
                  int nsegs, const float *seg_start, float *seg_map, int gate_arg, int add_arg, int prep_arg)
 {
-    // the plain recurrence (VAR = false) has the variant arguments folded away
-    const int gate = VAR ? gate_arg : 0, add = VAR ? add_arg : 0, prep = VAR ? prep_arg : 0;
+    // VAR = 0: the plain recurrence, the variant arguments folded away; 1: any
+    // variant, read from the arguments; 2: raw inputs with the per-channel gate
+    // and the delta write (the usual projection outputs), folded in
+    const int gate = VAR == 1 ? gate_arg : 0, add = VAR == 1 ? add_arg : 0;
+    const int prep = VAR == 2 ? 1 : (VAR == 1 ? prep_arg : 0);
     typedef ChunkCfg<In, DK, BV, C> K;
     typedef typename V4T<In>::type V4;
     constexpr int NB = K::NB, NDK = K::NDK, PK = K::PK, PC = K::PC, PT = K::PT, RS = K::RS;
@@ -1064,7 +1067,7 @@ __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const
 
 // One pass of the chunk kernel over nsu segments per sequence and nrows state
 // rows per head.
-template <typename In, int DK, int BV, int C, bool MAP, bool VAR>
+template <typename In, int DK, int BV, int C, bool MAP, int VAR>
 hipError_t launch_chunk_pass_v(const ChunkArgs &a, int nsu, int nrows)
 {
     typedef ChunkCfg<In, DK, BV, C> K;
@@ -1084,8 +1087,9 @@ hipError_t launch_chunk_pass_v(const ChunkArgs &a, int nsu, int nrows)
 template <typename In, int DK, int BV, int C, bool MAP>
 hipError_t launch_chunk_pass(const ChunkArgs &a, int nsu, int nrows)
 {
-    if (a.gate != 0 || a.add != 0 || a.prep != 0) return launch_chunk_pass_v<In, DK, BV, C, MAP, true>(a, nsu, nrows);
-    return launch_chunk_pass_v<In, DK, BV, C, MAP, false>(a, nsu, nrows);
+    if (a.prep != 0 && a.gate == 0 && a.add == 0) return launch_chunk_pass_v<In, DK, BV, C, MAP, 2>(a, nsu, nrows);
+    if (a.gate != 0 || a.add != 0 || a.prep != 0) return launch_chunk_pass_v<In, DK, BV, C, MAP, 1>(a, nsu, nrows);
+    return launch_chunk_pass_v<In, DK, BV, C, MAP, 0>(a, nsu, nrows);
 }
 
 // The whole prefill: one pass, or (nsegs > 1) the map pass over all segments
