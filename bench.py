@@ -374,6 +374,22 @@ def bench_small(args, torch, kda, kda_synth, stream, launches=200):
         res[name] = dict(workload=f"{name}: B={B} H={H} T={T} dk=dv={dk} {w['dtype']} C={C}",
                          kernel_us=round(kms * 1e3, 2), us_per_launch=round(wall * 1e6 / launches, 2),
                          tokens_per_s=round(B * T * launches / wall, 1))
+        # the library's own schedule choice (kda_chunk_auto_segments), through
+        # the segmented entry point with a workspace allocated once
+        nseg = kda.kda_chunk_auto_segments(B, T, H, dk, dv, C, w["dtype"] == "f32")
+        if nseg > 1:
+            wsb = kda.kda_chunk_segmented_workspace_bytes(B, H, dk, dv, nseg)
+            ws = torch.empty(wsb // 4 + 64, dtype=torch.float32, device="cuda")
+            seg = kda.kda_chunk_fwd_segmented_f32 if w["dtype"] == "f32" else kda.kda_chunk_fwd_segmented
+
+            def launch_seg():
+                seg(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out, sf, B, T, H, dk, dv, C, nseg, ws, wsb, h)
+
+            wall, kms = time_launches(launch_seg, stream, launches, 20, torch)
+            res[name]["auto_schedule"] = dict(segments=nseg, kernel_us=round(kms * 1e3, 2),
+                                              us_per_launch=round(wall * 1e6 / launches, 2),
+                                              tokens_per_s=round(B * T * launches / wall, 1))
+            del ws
         del p, out, sf
     return res
 

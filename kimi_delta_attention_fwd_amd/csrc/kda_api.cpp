@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -133,10 +134,13 @@ uint64_t seg_workspace_bytes(uint64_t nheads, int dk, int dv, int nseg)
 }
 
 // Segment count for a dense batch from a model of the run time in chunk steps:
-// a pass of g workgroups that each walk L chunks takes ceil(g / CUs) L steps
-// (one workgroup per compute unit), the map pass about 0.85 of a step per chunk
-// (no q, no outputs), the composition a fraction of a step per segment, and
-// the two extra launches a few steps.
+// a pass of g workgroups that each walk L chunks takes ceil(g / CUs) (L + 1)
+// steps (one workgroup per compute unit; the extra step is the prologue: the
+// first chunk's operands, the incoming state and the final store), the map
+// pass about 0.85 of a step per chunk (no q, no outputs), the serial
+// composition 0.6 (dk / 64)^1.5 steps per segment, and the two extra launches
+// about one step.  Fitted to measured runs: 1 segment for B=4 H=32 T=8192,
+// 8 for B=1 H=16 T=65536 (d = 128), 4 for B=2 H=4 T=1024 (d = 64).
 int auto_segments(bool f32, int B, int T, int H, int dk, int dv, int C)
 {
     if (B <= 0 || T <= 0 || H <= 0 || !supported_d(dk) || !supported_d(dv) || !supported_c(C)) return 1;
@@ -154,10 +158,11 @@ int auto_segments(bool f32, int B, int T, int H, int dk, int dv, int C)
         if (bv == 0) continue;
         const long L = (nch + s - 1) / s;
         const long g3 = nheads * s * (dv / bv);
-        double cost = (double)((g3 + cus - 1) / cus) * (double)L;
+        double cost = (double)((g3 + cus - 1) / cus) * (double)(L + 1);
         if (s > 1) {
             const long g1 = nheads * (s - 1) * ((dv + dk) / bv);
-            cost += 0.85 * (double)((g1 + cus - 1) / cus) * (double)L + 0.3 * s + 3.0;   // + two more launches
+            const double per_seg = 0.6 * std::pow(dk / 64.0, 1.5);
+            cost += 0.85 * (double)((g1 + cus - 1) / cus) * (double)(L + 1) + per_seg * s + 1.0;
         }
         if (s == 1 || cost < best) {
             best = cost;
