@@ -27,14 +27,15 @@
 // on BV/16 "state" waves, one per 16 value rows.  The state update needs only
 // the chunk's own E and double-buffered operands, so it closes the state
 // waves' first segment; their second segment forms the next chunk's P tiles
-// and off-diagonal A tiles (with a single state wave: the off-diagonal P tiles
-// only, the operand waves keep the rest).  Value rows of the state evolve independently, so each
-// state wave runs its whole chain alone: its 16 x DK slice of the fp32 state
-// stays in MFMA accumulator registers across the whole sequence, and every
-// accumulator tile feeds the next product directly as an operand (a tile held
-// as lane l <-> D[4(l>>4)+i][l&15] is both the B operand over its rows and the
-// A operand of its transpose).  The two groups meet at two workgroup barriers
-// per chunk; everything the state waves read is double-buffered in LDS.
+// and off-diagonal A tiles (with a single state wave: the off-diagonal P
+// tiles only, the operand waves keep the rest).  Value rows of the state
+// evolve independently, so each state wave runs its whole chain alone: its
+// 16 x DK slice of the fp32 state stays in MFMA accumulator registers across
+// the whole sequence, and every accumulator tile feeds the next product
+// directly as an operand (a tile held as lane l <-> D[4(l>>4)+i][l&15] is both
+// the B operand over its rows and the A operand of its transpose).  The two
+// groups meet at two workgroup barriers per chunk; everything the state waves
+// read is double-buffered in LDS.
 //
 // Decay factoring.  e^{G_r - G_j} is never formed pairwise.  Rows are split
 // into 16-token blocks and every key channel c gets a reference rho_I[c] per
