@@ -26,6 +26,11 @@ LIB = os.path.join(PKG, "libkda.so")
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are disabled in all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The chunk kernels are scheduled with LLVM's memory-clause strategy: with the
+# same results bit for bit, it ran the B=4 H=32 T=8192 prefill 1.2% and the
+# segmented T=65536 one 1.5% faster than the default (occupancy) strategy
+# (max-ILP was 9% slower).
+CHUNK_FLAGS = ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
 
@@ -54,7 +59,7 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     for f32 in (0, 1):
         for dk in (16, 32, 64, 128):
             obj = os.path.join(BUILD, f"kda_chunk_{'f32' if f32 else 'bf16'}_{dk}.o")
-            units.append([hipcc, *COMMON, *DEVICE_FLAGS, f"-DKDA_INST_F32={f32}", f"-DKDA_INST_DK={dk}",
+            units.append([hipcc, *COMMON, *DEVICE_FLAGS, *CHUNK_FLAGS, f"-DKDA_INST_F32={f32}", f"-DKDA_INST_DK={dk}",
                           "-c", os.path.join(CSRC, "kda_chunk_inst.hip"), "-o", obj])
     units.append([hipcc, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, "kda_decode.hip"),
                   "-o", os.path.join(BUILD, "kda_decode.o")])
