@@ -386,8 +386,8 @@ def test_chunk_variant_varlen_and_wide_heads(dev):
 
 @pytest.mark.parametrize("gate,write", VARIANTS)
 def test_decode_variants(dev, gate, write):
-    for dtype in ("bf16", "f32"):
-        N, T, H, dk, dv = 3, 5, 2, 128, 64
+    for dtype, T in (("bf16", 5), ("f32", 5), ("bf16", 19), ("f32", 19)):   # 19: two token tiles
+        N, H, dk, dv = 3, 2, 128, 64
         note(f"case decode variant gate={gate} write={write} N{N} T{T} H{H} dk{dk} dv{dv} {dtype}")
         p = kda_synth.prefill(N, T, H, dk, dv, dtype=dtype, s0_sigma=0.1, seed=85, device=dev)
         la, la_full = variant_inputs(p, gate)
@@ -396,6 +396,8 @@ def test_decode_variants(dev, gate, write):
         out = kda.recurrent_fwd(p.q, p.k, p.v, la, p.beta, S, gate=gate, write=write)
         torch.cuda.synchronize()
         assert_close(f"decode {gate}/{write} T={T}", f64(out), f64(S), o_ref, s_ref, TOL[dtype])
+        if T > 5:
+            continue
         # one token per launch through the same entry point (the step kernel)
         S = p.S0.clone()
         outs = [kda.recurrent_fwd(p.q[:, t:t + 1].contiguous(), p.k[:, t:t + 1].contiguous(),
@@ -495,7 +497,7 @@ def test_chunk_raw_inputs_varlen_and_zero_rows(dev):
 @pytest.mark.parametrize("gate", ["channel", "scalar", "none"])
 def test_decode_raw_inputs(dev, gate):
     for dtype in ("bf16", "f32"):
-        N, T, H, dk, dv = 3, 4, 2, 64, 128
+        N, T, H, dk, dv = 4, 21, 2, 64, 128   # two token tiles; 8 heads, 2 workgroups each
         note(f"case decode raw inputs gate={gate} N{N} T{T} H{H} dk{dk} dv{dv} {dtype}")
         p = kda_synth.prefill_raw(N, T, H, dk, dv, dtype=dtype, s0_sigma=0.1, q_sigma=3.0, k_sigma=0.3, seed=95,
                                   device=dev)
