@@ -158,6 +158,30 @@ def test_chunk_edge_cases(dev):
     assert none is None and torch.equal(out2, out)
 
 
+SWEEP = [(dtype, dk, dv, C, H) for dtype in ("bf16", "f32")
+         for dk, dv in ((16, 16), (32, 64), (64, 64), (128, 128), (64, 32))
+         for C in (16, 32, 64) for H in (2, 8)]
+
+
+@pytest.mark.parametrize("dtype,dk,dv,C,H", SWEEP)
+def test_chunk_config_sweep(dev, dtype, dk, dv, C, H):
+    """The single-pass kernel over input type x (dk, dv) x C x head count on a
+    ragged T = 130 (2 and 8 heads take different value-block widths and
+    workgroup mappings); the one combination that does not fit the LDS is
+    rejected up front."""
+    note(f"case sweep {dtype} dk{dk} dv{dv} C{C} H{H} T130")
+    p = kda_synth.prefill(1, 130, H, dk, dv, dtype=dtype, s0_sigma=0.1, seed=5, device=dev)
+    if dtype == "f32" and dk == 128 and C == 64:
+        with pytest.raises(kda.KdaError) as err:
+            kda.chunk_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S0=p.S0, C=C, segments=1)
+        assert err.value.status == 3
+        return
+    out, sf = kda.chunk_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S0=p.S0, C=C, segments=1)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_dense(p)
+    assert_close(f"sweep {dtype} dk{dk} dv{dv} C{C} H{H}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+
+
 def test_chunk_decay_at_precondition_edge(dev):
     """log_alpha = -4.9 in every channel: 78 nats of decay per 16-token block,
     just inside the kernel's documented range."""
