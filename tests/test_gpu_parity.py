@@ -677,6 +677,26 @@ def test_decode_steps(dev, N, H, dk, dv, dtype):
     assert_close("decode", f64(out), f64(S), o_ref, s_ref, TOL[dtype])
 
 
+DECODE_SWEEP = [(dtype, dk, dv, T, N) for dtype in ("bf16", "f32")
+                for dk, dv in ((16, 16), (32, 64), (64, 128), (128, 128), (128, 32))
+                for T in (1, 3, 17) for N in (3, 4)]
+
+
+@pytest.mark.parametrize("dtype,dk,dv,T,N", DECODE_SWEEP)
+def test_decode_config_sweep(dev, dtype, dk, dv, T, N):
+    """Both decode kernels over input type x (dk, dv) x T (1: the step kernel;
+    17: two token tiles of the multi-token kernel) x head count (N x 2 = 6 or
+    8 heads: a head's workgroups grouped on one XCD for 8)."""
+    H = 2
+    note(f"case decode sweep {dtype} dk{dk} dv{dv} T{T} N{N} H{H}")
+    p = kda_synth.prefill(N, T, H, dk, dv, dtype=dtype, s0_sigma=0.1, seed=7 + T, device=dev)
+    S = p.S0.clone()
+    out = kda.recurrent_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_dense(p)
+    assert_close(f"decode sweep {dtype} dk{dk} dv{dv} T{T} N{N}", f64(out), f64(S), o_ref, s_ref, TOL[dtype])
+
+
 def test_decode_workload_sampled(dev):
     w = kda_synth.WORKLOADS["decode"]
     note("case decode workload: 256 seq x H32 d128 bf16, 1024 steps (16 sampled heads, every step)")
