@@ -116,6 +116,9 @@ kda_status_t kda_chunk_fwd_f32(const float *q, const float *k, const float *v,
  * [N, H, dv, dk].  cu_seqlens is DEVICE memory, int32 [N+1]; precondition
  * (not checked on the device): cu_seqlens[0] = 0, non-decreasing,
  * cu_seqlens[N] = T_total.  kda_check_cu_seqlens_host() checks a host copy.
+ * The kernel clamps each sequence's [start, end) to [0, T_total] with
+ * end >= start, so offsets that break the precondition give unspecified
+ * outputs and states but never touch memory outside the buffers.
  */
 kda_status_t kda_chunk_fwd_varlen(const void *q, const void *k, const void *v,
                                   const float *log_alpha, const float *beta,

@@ -266,7 +266,7 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
     a.S_final = S_final;
     a.cu_seqlens = varlen ? cu_seqlens : nullptr;
     a.nseq = nseq;
-    a.T = varlen ? 0 : T;
+    a.T = varlen ? T_total : T;
     a.H = H;
     a.dk = dk;
     a.dv = dv;

@@ -365,9 +365,11 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     const int head = unit / nsu, seg = unit % nsu;
     const int seq = head / H, h = head % H;
     long tok0, len;
-    if (cu_seqlens) {
-        tok0 = cu_seqlens[seq];
-        len = (long)cu_seqlens[seq + 1] - tok0;
+    if (cu_seqlens) {   // T is the stream length here; offsets clamped to [0, T] keep every access inside it
+        const long a0 = min(max((long)cu_seqlens[seq], 0L), (long)T);
+        const long a1 = min(max((long)cu_seqlens[seq + 1], a0), (long)T);
+        tok0 = a0;
+        len = a1 - a0;
     } else {
         tok0 = (long)seq * T;
         len = T;

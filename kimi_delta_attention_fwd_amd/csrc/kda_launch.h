@@ -12,7 +12,7 @@ struct ChunkArgs {
     void *out;
     float *S_final;
     const int *cu_seqlens;   // device; NULL for the dense [B, T, H, d] layout
-    int nseq, T, H, dk, dv, C, BV;
+    int nseq, T, H, dk, dv, C, BV;   // T: tokens per sequence, or T_total with cu_seqlens
     // segment-parallel schedule (nsegs > 1): caller-owned workspace,
     // seg_map [nseq*H][nsegs-1][dv+dk][dk] and seg_start [nseq*H][nsegs][dv][dk] fp32
     int nsegs;

@@ -561,6 +561,42 @@ def test_varlen_equals_dense_per_sequence(dev):
         assert torch.equal(out[:, a:b], o_n) and torch.equal(sf[n:n + 1], s_n)
 
 
+def test_varlen_malformed_offsets_stay_in_bounds(dev):
+    """cu_seqlens that break the precondition (negative, decreasing, past
+    T_total): the kernel clamps each sequence to [0, T_total] with end >= start.
+    Inputs sit between NaN bands and out between sentinel bands; the bands are
+    neither read (states stay finite) nor written, and every output row and state
+    that one clamped sequence alone owns matches the oracle on that sequence."""
+    T_total, H, dk, dv, pad = 100, 2, 64, 64, 256
+    cu = [-3, 0, 40, 30, T_total + 50]   # clamped: [0, 0), [0, 40), [40, 40), [30, 100)
+    note(f"case varlen malformed offsets {cu} T_total {T_total} H{H} d64 bf16")
+    p = kda_synth.prefill_varlen([T_total], H, dk, dv, dtype="bf16", s0_sigma=None, seed=24, device=dev)
+    g = torch.Generator(device=dev).manual_seed(25)
+    S0 = torch.randn((4, H, dv, dk), generator=g, device=dev) * 0.1
+
+    def banded(t, fill):
+        big = torch.full((1, T_total + 2 * pad) + tuple(t.shape[2:]), fill, dtype=t.dtype, device=dev)
+        big[:, pad:pad + T_total] = t
+        return big, big[:, pad:pad + T_total]
+
+    ins = [banded(t, float("nan")) for t in (p.q, p.k, p.v, p.log_alpha, p.beta)]
+    big_out, out = banded(torch.empty_like(p.v), 9.0)
+    big_out[:, pad:pad + T_total] = 9.0
+    sf = torch.empty_like(S0)
+    cu_dev = torch.tensor(cu, dtype=torch.int32, device=dev)
+    kda.kda_chunk_fwd_varlen(*(view for _, view in ins), S0, out, sf, cu_dev, 4, T_total, H, dk, dv, 64)
+    torch.cuda.synchronize()
+    assert torch.all(big_out[:, :pad] == 9.0) and torch.all(big_out[:, pad + T_total:] == 9.0)
+    assert torch.all(torch.isfinite(sf))
+    assert torch.equal(sf[0], S0[0]) and torch.equal(sf[2], S0[2])   # empty after clamping
+    for n, (a, b), own in ((1, (0, 40), (0, 30)), (3, (30, 100), (40, 100))):
+        o_ref, s_ref = oracle.forward(f64(p.q[:, a:b]), f64(p.k[:, a:b]), f64(p.v[:, a:b]),
+                                      f64(p.log_alpha[:, a:b]), f64(p.beta[:, a:b]), S0=f64(S0[n:n + 1]))
+        lo, hi = own[0] - a, own[1] - a
+        assert_close(f"clamped sequence {n}", f64(out[:, own[0]:own[1]]), f64(sf[n:n + 1]),
+                     o_ref[:, lo:hi], s_ref, TOL["bf16"])
+
+
 def test_varlen_workload_sampled(dev):
     w = kda_synth.WORKLOADS["varlen"]
     note("case varlen workload: 8 sequences U[2048,16384] x H16 d128 bf16 C64 (sampled heads)")
