@@ -263,7 +263,8 @@ struct ChunkCfg {
     // "all channels referenced to the chunk start" flags [NXW]
     static constexpr int SC_GL = NB * DK, SC_BETA = NB * DK + DK, SC_FLAG = SC_BETA + C;
     // input preparation (raw q, k): per-wave partial squared norms of k and q
-    // [NXW][C], then per token beta / |k|^2, |k| and 1 / |q|
+    // [C][NXW] (a token's four partials in one 16-byte LDS read), then per
+    // token beta / |k|^2, |k| and 1 / |q|
     static constexpr int SC_PK = SC_FLAG + NXW, SC_PQ = SC_PK + NXW * C, SC_BH = SC_PQ + NXW * C;
     static constexpr int SC_KN = SC_BH + C, SC_QI = SC_KN + C, SC_END = SC_QI + C;
     static constexpr float FAST_NATS = 80.f;
@@ -394,8 +395,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     auto beta_hat = [&](const float *scc, int r) __attribute__((always_inline)) {
         float sk = 0.f;
 #pragma unroll
-        for (int w = 0; w < K::NXW; ++w) sk += scc[K::SC_PK + w * C + r];
-        return sk > 0.f ? scc[K::SC_BETA + r] / sk : 0.f;
+        for (int w = 0; w < K::NXW; ++w) sk += scc[K::SC_PK + r * K::NXW + w];
+        return sk > 0.f ? scc[K::SC_BETA + r] * __builtin_amdgcn_rcpf(sk) : 0.f;
     };
     auto tile_job = [&](long ch, int p, bool doA, bool doP, f32x4 *lt = nullptr) __attribute__((always_inline)) {
         int I = p, J = p;
@@ -651,8 +652,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                     if (act && cg == 0) {
 #pragma unroll
                         for (int i = 0; i < RS; ++i) {
-                            sc[K::SC_PK + xw * C + r0 + i] = sk[i];
-                            sc[K::SC_PQ + xw * C + r0 + i] = sq[i];
+                            sc[K::SC_PK + (r0 + i) * K::NXW + xw] = sk[i];
+                            sc[K::SC_PQ + (r0 + i) * K::NXW + xw] = sq[i];
                         }
                     }
                 }
@@ -732,10 +733,10 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 float sk = 0.f, sq = 0.f;
 #pragma unroll
                 for (int w = 0; w < K::NXW; ++w) {
-                    sk += sc[K::SC_PK + w * C + lane];
-                    sq += sc[K::SC_PQ + w * C + lane];
+                    sk += sc[K::SC_PK + lane * K::NXW + w];
+                    sq += sc[K::SC_PQ + lane * K::NXW + w];
                 }
-                sc[K::SC_BH + lane] = sk > 0.f ? sc[K::SC_BETA + lane] / sk : 0.f;
+                sc[K::SC_BH + lane] = sk > 0.f ? sc[K::SC_BETA + lane] * __builtin_amdgcn_rcpf(sk) : 0.f;
                 sc[K::SC_KN + lane] = __builtin_sqrtf(sk);
                 sc[K::SC_QI + lane] = sq > 0.f ? __builtin_amdgcn_rsqf(sq) : 0.f;
             }
