@@ -394,6 +394,18 @@ def bench_small(args, torch, kda, kda_synth, stream, launches=200):
     return res
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (empty where there is none)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(p, kda_synth, target_s=10.0, max_passes=8):
     """Float64 oracle on the whole mid workload (every sequence, head and token),
     repeated until about `target_s` seconds of CPU work have been timed."""
@@ -409,6 +421,7 @@ def cpu_baseline(p, kda_synth, target_s=10.0, max_passes=8):
         passes += 1
     del args
     return dict(value=round(passes * B * T / dt, 2), unit="tokens/s", cores=threads, kind="oracle",
+                host_cpu=host_cpu_model(), host_threads=os.cpu_count(),
                 sample=f"the whole mid workload (B={B}, T={T}, H={H}, dk=dv=128, zero initial state) "
                        f"through the float64 token-by-token recurrence, {passes} pass(es) in {dt:.1f} s, "
                        f"OpenMP over the {B * H} (sequence, head) pairs")
