@@ -785,7 +785,9 @@ def test_decode_equals_chunk_prefill_on_same_stream(dev):
                                                # head counts that are multiples of 8 (a head's
                                                # workgroups grouped on one XCD), one and two token tiles
                                                (4, 5, 2, 128, 128, "bf16"), (2, 3, 4, 64, 128, "f32"),
-                                               (2, 20, 4, 128, 128, "bf16")])
+                                               (2, 20, 4, 128, 128, "bf16"),
+                                               # longer streams: five token tiles with a ragged tail
+                                               (2, 67, 4, 128, 128, "bf16"), (3, 45, 2, 64, 128, "f32")])
 def test_recurrent_fwd_matches_oracle(dev, N, T, H, dk, dv, dtype):
     note(f"case multi-token decode N{N} T{T} H{H} dk{dk} dv{dv} {dtype}")
     p = kda_synth.prefill(N, T, H, dk, dv, dtype=dtype, s0_sigma=0.1, seed=61 + T + dk + dv, device=dev)
