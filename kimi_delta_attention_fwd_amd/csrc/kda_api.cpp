@@ -76,10 +76,14 @@ kda_status_t check_aliasing(const Buf &out, const Buf *ins, int nin, const Buf &
 }
 
 // Value-block width of the chunk kernel: the widest block (at most maxbv) that
-// still gives every compute unit a workgroup (256 CUs), else the narrowest that
-// fits.  `units` counts (sequence, head, segment) triples.  KDA_CHUNK_BV
-// overrides the choice for tuning.
-int choose_bv(bool f32, int dk, int dv, int C, long units, int maxbv = 64)
+// fits the LDS.  A workgroup walks all chunks of its sequence (or segment)
+// whatever its width, so a narrower block never shortens the serial chain: it
+// only repeats the operand waves' work in more workgroups and leaves more tile
+// jobs to each state wave (one state wave at BV = 16).  Measured on one MI355X:
+// B1 H16 T65536 d128 single pass 4.44 ms at BV = 64 against 5.23 ms at 16, and
+// B2 H4 T1024 d64 63 against 67 us.  KDA_CHUNK_BV overrides the choice (tests
+// and tuning).
+int choose_bv(bool f32, int dk, int dv, int C, int maxbv = 64)
 {
     if (const char *env = std::getenv("KDA_CHUNK_BV")) {
         const int bv = std::atoi(env);
@@ -87,8 +91,6 @@ int choose_bv(bool f32, int dk, int dv, int C, long units, int maxbv = 64)
             return bv;
     }
     for (int bv : {64, 32, 16})
-        if (bv <= dv && bv <= maxbv && kda::chunk_fits(f32, dk, bv, C) && units * (dv / bv) >= 256) return bv;
-    for (int bv : {16, 32, 64})
         if (bv <= dv && bv <= maxbv && kda::chunk_fits(f32, dk, bv, C)) return bv;
     return 0;
 }
@@ -140,7 +142,7 @@ uint64_t seg_workspace_bytes(uint64_t nheads, int dk, int dv, int nseg)
 // pass about 0.85 of a step per chunk (no q, no outputs), the serial
 // composition 0.6 (dk / 64)^1.5 steps per segment, and the two extra launches
 // about one step.  Fitted to measured runs: 1 segment for B=4 H=32 T=8192,
-// 8 for B=1 H=16 T=65536 (d = 128), 4 for B=2 H=4 T=1024 (d = 64).
+// 8 for B=1 H=16 T=65536 (d = 128), 8 for B=2 H=4 T=1024 (d = 64).
 int auto_segments(bool f32, int B, int T, int H, int dk, int dv, int C)
 {
     if (B <= 0 || T <= 0 || H <= 0 || !supported_d(dk) || !supported_d(dv) || !supported_c(C)) return 1;
@@ -154,7 +156,7 @@ int auto_segments(bool f32, int B, int T, int H, int dk, int dv, int C)
     double best = 0.0;
     int best_s = 1;
     for (int s = 1; s <= 64 && s <= nch; ++s) {
-        const int bv = choose_bv(f32, dk, dv, C, nheads * s, s > 1 ? dk : 64);
+        const int bv = choose_bv(f32, dk, dv, C, s > 1 ? dk : 64);
         if (bv == 0) continue;
         const long L = (nch + s - 1) / s;
         const long g3 = nheads * s * (dv / bv);
@@ -248,7 +250,7 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
                 return fail(KDA_ERR_ALIASING, "workspace overlaps %s", b.name);
     }
 
-    const int BV = choose_bv(f32, dk, dv, C, (long)(nheads * nseg), nseg > 1 ? dk : 64);
+    const int BV = choose_bv(f32, dk, dv, C, nseg > 1 ? dk : 64);
     if (BV == 0)
         return fail(KDA_ERR_UNSUPPORTED, "no %s kernel fits LDS for dk=%d, dv=%d, C=%d",
                     f32 ? "fp32" : "bf16", dk, dv, C);

@@ -166,9 +166,8 @@ SWEEP = [(dtype, dk, dv, C, H) for dtype in ("bf16", "f32")
 @pytest.mark.parametrize("dtype,dk,dv,C,H", SWEEP)
 def test_chunk_config_sweep(dev, dtype, dk, dv, C, H):
     """The single-pass kernel over input type x (dk, dv) x C x head count on a
-    ragged T = 130 (2 and 8 heads take different value-block widths and
-    workgroup mappings); the one combination that does not fit the LDS is
-    rejected up front."""
+    ragged T = 130 (8 heads group a head's value blocks on one XCD, 2 do
+    not); the one combination that does not fit the LDS is rejected up front."""
     note(f"case sweep {dtype} dk{dk} dv{dv} C{C} H{H} T130")
     p = kda_synth.prefill(1, 130, H, dk, dv, dtype=dtype, s0_sigma=0.1, seed=5, device=dev)
     if dtype == "f32" and dk == 128 and C == 64:
@@ -474,6 +473,32 @@ def test_chunk_raw_inputs(dev, gate, write, dtype):
                                 gate=gate, write=write, raw=True)
         torch.cuda.synchronize()
         assert_close(f"raw {gate}/{write} segments={segments}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+
+
+NARROW = [(1, 200, 2, 128, 128, 64, "bf16"), (2, 150, 2, 64, 64, 32, "f32"), (1, 130, 3, 128, 64, 16, "bf16")]
+
+
+@pytest.mark.parametrize("bv", ["16", "32"])
+def test_chunk_narrow_value_blocks(dev, bv, monkeypatch):
+    """The library takes the widest value block that fits, so the one- and
+    two-state-wave kernels serve dv = 16 and 32 by default; KDA_CHUNK_BV selects
+    them for wider heads too.  Single pass, segmented and raw inputs against
+    the oracle."""
+    monkeypatch.setenv("KDA_CHUNK_BV", bv)
+    for B, T, H, dk, dv, C, dtype in NARROW:
+        note(f"case value block {bv}: B{B} T{T} H{H} dk{dk} dv{dv} C{C} {dtype}")
+        p = kda_synth.prefill(B, T, H, dk, dv, dtype=dtype, s0_sigma=0.1, seed=31 + T, device=dev)
+        o_ref, s_ref = oracle_dense(p)
+        for segments in (1, 3):
+            out, sf = gpu_chunk(p, C, segments=segments)
+            assert_close(f"BV={bv} segments={segments}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+    p = kda_synth.prefill_raw(1, 170, 2, 128, 128, dtype="bf16", s0_sigma=0.1, q_sigma=2.0, k_sigma=0.5, seed=33,
+                              device=dev)
+    o_ref, s_ref = oracle_raw(p, "channel", "delta")
+    out, sf = kda.chunk_fwd(p.q, p.k, p.v, raw_gate_arg(p, "channel"), p.beta, S0=p.S0, C=64, segments=1,
+                            gate="channel", write="delta", raw=True)
+    torch.cuda.synchronize()
+    assert_close(f"BV={bv} raw", f64(out), f64(sf), o_ref, s_ref, TOL["bf16"])
 
 
 @pytest.mark.parametrize("dtype,dk,C", [("bf16", 128, 64), ("bf16", 64, 64), ("f32", 64, 32)])
