@@ -300,7 +300,8 @@ def bench_long(args, torch, kda, kda_synth, stream, steps=3):
     nbytes = prefill_bytes(B * T * H, dk, dv, B * H, s0=True, sfinal=True)
     del p, out, sf, ws
     return dict(workload="long prefill: B=1 H=16 T=65536 dk=dv=128 bf16 C=64, S0 in, S_final out",
-                schedule=f"segment-parallel, {nseg} segments per sequence (map pass, composition, rerun)",
+                schedule=f"segment-parallel, {nseg} segments per sequence (map launch with the lead segment's whole pass, "
+                         f"composition, second pass)",
                 tokens_per_s=B * T * steps / wall, kernel_ms=kms, single_pass_kernel_ms=kms1,
                 hbm_gbs=round(nbytes / (kms * 1e-3) / 1e9, 1),
                 hbm_frac=round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))

@@ -142,15 +142,18 @@ kda_status_t kda_chunk_fwd_varlen_f32(const float *q, const float *k, const floa
  * incoming state; so is a run of chunks: S_end = S_start M + N, with M
  * (dk x dk) and N (dv x dk) independent of S_start (derived from the chunk
  * equations, not stated on the pages).  The chunks of every sequence are cut
- * into nseg consecutive segments of ceil(chunks / nseg) chunks, and three
- * passes run on `stream`:
- *   1. every segment but the last, in parallel, runs from S_start = 0 with dk
- *      extra state rows that start at the identity and see v = 0: the real
- *      rows end at N, the extra rows at M;
- *   2. the segments' incoming states are composed in order, in fp32,
- *      starting from S0;
- *   3. every segment, in parallel, reruns from its incoming state, writing
- *      out and (last segment) S_final.
+ * into nseg consecutive segments, and three passes run on `stream`:
+ *   1. segment 0 runs its whole pass from S0 (writing its outputs and segment
+ *      1's incoming state) while segments 1 .. nseg-2, in parallel, run from
+ *      S_start = 0 with dk extra state rows that start at the identity and
+ *      see v = 0: the real rows end at N, the extra rows at M;
+ *   2. the later segments' incoming states are composed in order, in fp32;
+ *   3. segments 1 .. nseg-1, in parallel, run from their incoming states,
+ *      writing out and (last segment) S_final.
+ * Segment 0 is longer than the others, so that its pass takes about as long
+ * as the maps beside it; segments may be empty for short sequences.  The
+ * environment variable KDA_SEG_LEAD (a length ratio in tenths; 0 = equal
+ * segments, segment 0 mapped like the others) overrides the split.
  * nseg = 1 is the plain single pass (workspace may be NULL).
  *
  *   nseg       1 .. 1024; kda_chunk_auto_segments() picks one for a dense batch.

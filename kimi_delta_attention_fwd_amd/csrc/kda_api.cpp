@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -135,36 +136,73 @@ uint64_t seg_workspace_bytes(uint64_t nheads, int dk, int dv, int nseg)
     return seg_map_bytes(nheads, dk, dv, nseg) + nheads * (uint64_t)nseg * (uint64_t)dv * (uint64_t)dk * 4u;
 }
 
-// Segment count for a dense batch from a model of the run time in chunk steps:
-// a pass of g workgroups that each walk L chunks takes ceil(g / CUs) (L + 1)
+// Compute units of the current device, queried once per device (256, the
+// MI355X count, when the query fails).
+int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int m = 0;
+    if (hipDeviceGetAttribute(&m, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || m <= 0) m = 256;
+    if (dev < 64) cache[dev].store(m, std::memory_order_relaxed);
+    return m;
+}
+
+// Lead segment of the segmented schedule (tenths of a later segment's length).
+// The map launch holds segment 0's whole pass (nheads * dv / bv workgroups)
+// beside the maps of segments 1 .. nseg - 2 ((dv + dk) / bv each); a map chunk
+// costs about 0.85 of a full one, so segment 0 gets 0.85 chunks per chunk of a
+// map times the launch's rounds of workgroups.  KDA_SEG_LEAD overrides it
+// (0: equal segments, segment 0 mapped like the others).
+int seg_lead(long nheads, int dk, int dv, int bv, int nseg, int cus)
+{
+    if (nseg < 2) return 0;
+    if (const char *env = std::getenv("KDA_SEG_LEAD")) {
+        const int v = std::atoi(env);
+        if (v >= 0 && v <= 1000) return v;
+    }
+    const long g1 = nheads * ((long)(nseg - 2) * ((dv + dk) / bv) + dv / bv);
+    const long rounds = (g1 + cus - 1) / cus;
+    return (int)(8.5 * (double)rounds + 0.5);
+}
+
+// Segment count for a dense batch from a model of the run time in chunk steps.
+// A pass of g workgroups that each walk L chunks takes ceil(g / CUs) (L + 1)
 // steps (one workgroup per compute unit; the extra step is the prologue: the
-// first chunk's operands, the incoming state and the final store), the map
-// pass about 0.85 of a step per chunk (no q, no outputs), the serial
-// composition 0.6 (dk / 64)^1.5 steps per segment, and the two extra launches
-// about one step.  Fitted to measured runs: 1 segment for B=4 H=32 T=8192,
-// 8 for B=1 H=16 T=65536 (d = 128), 8 for B=2 H=4 T=1024 (d = 64).
+// first chunk's operands, the incoming state and the final store).  With s
+// segments the map launch takes max(L0 + 1, 0.85 ceil(g1 / CUs) (L + 1)) (the
+// lead segment's whole pass beside the maps, a map chunk being about 0.85 of a
+// full one), the serial composition 0.6 (dk / 64)^1.5 steps per segment, the
+// second pass ceil(g3 / CUs) (L + 1) over segments 1 .. s - 1, and the two
+// extra launches about one step.  Fitted to measured runs: 1 segment for B=4
+// H=32 T=8192, 9 for B=1 H=16 T=65536 (d = 128), 8 for B=2 H=4 T=1024 (d = 64).
 int auto_segments(bool f32, int B, int T, int H, int dk, int dv, int C)
 {
     if (B <= 0 || T <= 0 || H <= 0 || !supported_d(dk) || !supported_d(dv) || !supported_c(C)) return 1;
-    int cus = 256;
-    int dev = 0;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int m = 0;
-        if (hipDeviceGetAttribute(&m, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && m > 0) cus = m;
-    }
+    const int cus = device_cus();
     const long nch = (T + C - 1) / C, nheads = (long)B * H;
     double best = 0.0;
     int best_s = 1;
     for (int s = 1; s <= 64 && s <= nch; ++s) {
         const int bv = choose_bv(f32, dk, dv, C, s > 1 ? dk : 64);
         if (bv == 0) continue;
-        const long L = (nch + s - 1) / s;
-        const long g3 = nheads * s * (dv / bv);
-        double cost = (double)((g3 + cus - 1) / cus) * (double)(L + 1);
-        if (s > 1) {
-            const long g1 = nheads * (s - 1) * ((dv + dk) / bv);
-            const double per_seg = 0.6 * std::pow(dk / 64.0, 1.5);
-            cost += 0.85 * (double)((g1 + cus - 1) / cus) * (double)(L + 1) + per_seg * s + 1.0;
+        const long nvA = dv / bv, nvB = (dv + dk) / bv;
+        double cost;
+        if (s == 1) {
+            cost = (double)((nheads * nvA + cus - 1) / cus) * (double)(nch + 1);
+        } else {
+            const int lead = seg_lead(nheads, dk, dv, bv, s, cus);
+            const long L = (10 * nch + 10 * (s - 1) + lead - 1) / (10 * (s - 1) + lead);
+            const long L0 = nch - (s - 1) * L > 0 ? nch - (s - 1) * L : 0;
+            const long g1 = nheads * ((s - 2) * nvB + nvA), g3 = nheads * (s - 1) * nvA;
+            const double map = 0.85 * (double)((g1 + cus - 1) / cus) * (double)(L + 1);
+            cost = (map > (double)(L0 + 1) ? map : (double)(L0 + 1)) + 0.6 * std::pow(dk / 64.0, 1.5) * s +
+                   (double)((g3 + cus - 1) / cus) * (double)(L + 1) + 1.0;
         }
         if (s == 1 || cost < best) {
             best = cost;
@@ -278,6 +316,7 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
     a.gate = gate;
     a.add = (variant >> 2) & 1;
     a.prep = (variant >> 3) & 1;
+    a.lead = nseg > 1 ? seg_lead((long)nheads, dk, dv, BV, nseg, device_cus()) : 0;
     a.seg_map = nseg > 1 ? (float *)workspace : nullptr;
     a.seg_start = nseg > 1 ? (float *)((char *)workspace + seg_map_bytes(nheads, dk, dv, nseg)) : nullptr;
     a.stream = (hipStream_t)stream;

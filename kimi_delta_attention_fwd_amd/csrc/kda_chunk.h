@@ -325,7 +325,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                  const float *__restrict__ log_alpha, const float *__restrict__ beta,
                  const float *S0, In *__restrict__ out, float *S_final,
                  const int *__restrict__ cu_seqlens, int T, int H, int dv, int xcd_map,
-                 int nsegs, const float *seg_start, float *seg_map, int gate_arg, int add_arg, int prep_arg)
+                 int nsegs, float *seg_start, float *seg_map, int gate_arg, int add_arg, int prep_arg,
+                 int lead)
 {
     // VAR = 0: the plain recurrence, the variant arguments folded away; 1: any
     // variant, read from the arguments; 2: raw inputs with the per-channel gate
@@ -349,21 +350,51 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) index
     const int n = lane & 15, g = lane >> 4;
-    const int nsu = MAP ? nsegs - 1 : nsegs;         // segments per sequence in this grid
-    const int nvb = (MAP ? dv + DK : dv) / BV;       // value blocks (of the augmented state)
-    int unit, vb;                                    // unit = (head, segment)
-    if (xcd_map) {
-        // Workgroups are dealt to the 8 XCDs round-robin; keep all value blocks
-        // of one unit on one XCD so their shared q / k / log_alpha reads hit
-        // the same L2.
-        const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
-        unit = (slot / nvb) * 8 + x;
-        vb = slot % nvb;
+    // Work units are (head, segment) pairs, each split into value blocks of BV
+    // state rows.  Segments (nsegs > 1): the map launch (MAP) takes every
+    // segment but the last and the later launch every segment from its
+    // incoming state.  With a lead segment (lead > 0) segment 0 needs no map:
+    // its units in the map launch run the whole pass from S0 (outputs
+    // included, its final state being segment 1's incoming one), in the first
+    // nA workgroups, beside the maps of segments 1 .. nsegs - 2; the later
+    // launch then takes segments 1 .. nsegs - 1.
+    const int nvA = dv / BV, nvB = (dv + DK) / BV;   // value blocks of a plain / augmented unit
+    // Workgroups are dealt to the 8 XCDs round-robin; with the remap (a flag
+    // per region) all value blocks of one unit sit on one XCD, so their shared
+    // q / k / log_alpha reads hit the same L2.
+    auto place = [&](int b, int nvb, bool xcd, int &unit, int &vb_) {
+        if (xcd) {
+            const int x = b & 7, slot = b >> 3;
+            unit = (slot / nvb) * 8 + x;
+            vb_ = slot % nvb;
+        } else {
+            unit = b / nvb;
+            vb_ = b % nvb;
+        }
+    };
+    int head, seg, vb;
+    bool lead_full = false;                          // the lead segment's whole pass in the map launch
+    if (MAP && lead > 0) {
+        const int nA = (int)(gridDim.x / (nvA + (nsegs - 2) * nvB)) * nvA;
+        int unit;
+        if ((int)blockIdx.x < nA) {
+            place(blockIdx.x, nvA, xcd_map & 1, unit, vb);
+            head = unit;
+            seg = 0;
+            lead_full = true;
+        } else {
+            place(blockIdx.x - nA, nvB, xcd_map & 2, unit, vb);
+            head = unit / (nsegs - 2);
+            seg = 1 + unit % (nsegs - 2);
+        }
     } else {
-        unit = blockIdx.x / nvb;
-        vb = blockIdx.x % nvb;
+        const int nsu = (MAP || lead > 0) ? nsegs - 1 : nsegs;   // segments per sequence in this grid
+        int unit;
+        place(blockIdx.x, MAP ? nvB : nvA, xcd_map & 1, unit, vb);
+        head = unit / nsu;
+        seg = unit % nsu + ((!MAP && lead > 0) ? 1 : 0);
     }
-    const int head = unit / nsu, seg = unit % nsu;
+    const bool map = MAP && !lead_full;              // augmented state, no outputs
     const int seq = head / H, h = head % H;
     long tok0, len;
     if (cu_seqlens) {   // T is the stream length here; offsets clamped to [0, T] keep every access inside it
@@ -376,9 +407,22 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         len = T;
     }
     if (nsegs > 1) {
-        // segment seg: chunks [c0, c1) of the sequence, ceil(nch / nsegs) each
-        const long nch_all = (len + C - 1) / C, L = (nch_all + nsegs - 1) / nsegs;
-        const long c0 = min((long)seg * L, nch_all), c1 = min(c0 + L, nch_all);
+        // segment seg: chunks [c0, c1) of the sequence's n.  Uniform: ceil(n /
+        // nsegs) each.  Lead: segments 1 .. nsegs - 1 take L = ceil(10 n /
+        // (10 (nsegs - 1) + lead)) each from the end, segment 0 the rest (about
+        // lead / 10 L; none when the sequence is short).
+        const long n = (len + C - 1) / C;
+        long c0, c1;
+        if (lead > 0) {
+            const long L = (10 * n + 10 * (nsegs - 1) + lead - 1) / (10 * (nsegs - 1) + lead);
+            const long l0 = max(0L, n - (nsegs - 1) * L);
+            c0 = seg == 0 ? 0 : min(l0 + (seg - 1) * L, n);
+            c1 = seg == 0 ? l0 : min(c0 + L, n);
+        } else {
+            const long L = (n + nsegs - 1) / nsegs;
+            c0 = min((long)seg * L, n);
+            c1 = min(c0 + L, n);
+        }
         tok0 += c0 * C;
         len = max(0L, min(len - c0 * C, (c1 - c0) * C));
     }
@@ -521,7 +565,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             }
         };
         auto prefetch_q = [&](long t0) __attribute__((always_inline)) {
-            if constexpr (MAP) return;
+            if (map) return;
             const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + (hrow + t0 * H) * DK, chunk_valid(t0) * rowb_in);
 #pragma unroll
             for (int i = 0; i < RS; ++i) qr[i] = buf_load<In4>(rq, voff_in, i * rowb_in);
@@ -626,16 +670,16 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                         pp[j] *= al[i][j];
                         const float kf = tof(kr[i][j]);
                         vkr[j] = kf * pp[j];                       // k e^{G - ref}
-                        if constexpr (!MAP) vqr[j] = tof(qr[i][j]) * pp[j];   // q e^{G - ref}
+                        if (!map) vqr[j] = tof(qr[i][j]) * pp[j];   // q e^{G - ref}
                         if (prep) {
                             sk[i] += kf * kf;
-                            if constexpr (!MAP) sq[i] += tof(qr[i][j]) * tof(qr[i][j]);
+                            if (!map) sq[i] += tof(qr[i][j]) * tof(qr[i][j]);
                         }
                     }
                     if (act) {
                         const int r = r0 + i;
                         store4(Kr + r * PK + c0, vkr);
-                        if constexpr (!MAP) store4(Qr + r * PK + c0, vqr);
+                        if (!map) store4(Qr + r * PK + c0, vqr);
                         if (!lane_fast) {
 #pragma unroll
                             for (int j = 0; j < 4; ++j) vkd[j] = tof(kr[i][j]) * __builtin_amdgcn_rcpf(pp[j]);   // k e^{ref - G}
@@ -741,7 +785,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 sc[K::SC_QI + lane] = sq > 0.f ? __builtin_amdgcn_rsqf(sq) : 0.f;
             }
             if (add) {   // no A: only the diagonal P tiles of a single state wave
-                if constexpr (K::NBV == 1 && !MAP) {
+                if (K::NBV == 1 && !map) {
                     for (int p = xw; p < NB; p += K::NXW) tile_job(ch, p, false, true);
                 }
                 return;
@@ -757,7 +801,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                     // they cancel, about 1e-4 relative at worst: fine for the bf16
                     // kernels, the fp32 ones use the substitution below.)
                     f32x4 lt[2];
-                    tile_job(ch, p, true, K::NBV == 1 && !MAP, lt);
+                    tile_job(ch, p, true, K::NBV == 1 && !map, lt);
                     auto mm = [](f32x4 x, f32x4 y) {   // acc(X^T Y)
                         const f32x4 a[1] = {x}, b[1] = {y};
                         return mma_tiles<4, float, 1>(zero4(), a, b);
@@ -777,7 +821,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                     // fp32 kernels: column n of D_p by forward substitution over the
                     // rows of the stored tile (lanes of the other 16-lane rows repeat
                     // the work and store nothing)
-                    tile_job(ch, p, true, K::NBV == 1 && !MAP);
+                    tile_job(ch, p, true, K::NBV == 1 && !map);
                     float *At = sA + p * 16 * PT;
                     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
                     float x[16];
@@ -833,7 +877,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         // =============== state waves: value rows 16 cb .. 16 cb + 15 of the block
         const int cb = wave;
         const int row = vb * BV + 16 * cb + n;     // this lane's state row (of the augmented state in MAP mode)
-        const bool vreal = !MAP || vb * BV < dv;   // real value rows (virtual ones see v = 0)
+        const bool vreal = !map || vb * BV < dv;   // real value rows (virtual ones see v = 0)
         // bf16: lane (n, g) loads row 16 (2 u + g/2) + n, columns 8 (g&1) .. +7;
         // fp32: row 16 u + n, columns 4g .. 4g+3 (u = load index)
         const int rowb_v = HDV * (int)sizeof(In);
@@ -844,12 +888,16 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         // State, transposed, in accumulator layout: Sacc[ct][i] = S[16 cb + n][16 ct + 4g + i].
         // Where it comes from and goes to: S0 / S_final for a whole sequence;
         // the segment's incoming state / S_final (last segment only) for a
-        // segment; zero or the identity / the segment's map in MAP mode.
+        // segment; zero or the identity / the segment's map in MAP mode; S0 /
+        // segment 1's incoming state for the lead segment in the map launch.
         f32x4 Sacc[NDK];
         const float *s0row = nullptr;
         float *sfrow = nullptr;
-        if constexpr (MAP) {
+        if (map) {
             sfrow = seg_map + (((long)head * (nsegs - 1) + seg) * (dv + DK) + row) * DK;
+        } else if (MAP) {
+            if (S0) s0row = S0 + ((long)head * dv + row) * DK;
+            sfrow = seg_start + (((long)head * nsegs + 1) * dv + row) * DK;
         } else if (nsegs > 1) {
             s0row = seg_start + (((long)head * nsegs + seg) * dv + row) * DK;
             if (seg == nsegs - 1 && S_final) sfrow = S_final + ((long)head * dv + row) * DK;
@@ -859,7 +907,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         }
 #pragma unroll
         for (int ct = 0; ct < NDK; ++ct) {
-            if constexpr (MAP) {
+            if (map) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) Sacc[ct][i] = (row - dv == 16 * ct + 4 * g + i) ? 1.f : 0.f;
             } else {
@@ -894,15 +942,16 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         // diagonal P tiles, else the off-diagonal P tiles (MAP mode: no P tiles).
         // Jobs are dealt in snake order so the heavier pairs spread evenly over
         // the waves.
-        constexpr int NJOB = MAP ? (K::NBV >= 2 ? K::NOFF : 0) : (K::NBV >= 2 ? K::NPAIR : K::NOFF);
-        constexpr int NROUND = (NJOB + K::NBV - 1) / K::NBV;
+        constexpr int NJOB_MAP = K::NBV >= 2 ? K::NOFF : 0, NJOB_FULL = K::NBV >= 2 ? K::NPAIR : K::NOFF;
+        const int njob = map ? NJOB_MAP : NJOB_FULL;
+        constexpr int NROUND = (NJOB_FULL + K::NBV - 1) / K::NBV;   // NJOB_MAP <= NJOB_FULL
         auto y_tiles = [&](long ch) __attribute__((always_inline)) {
 #pragma unroll
             for (int r = 0; r < NROUND; ++r) {
                 const int s = r * K::NBV + ((r & 1) ? K::NBV - 1 - cb : cb);
-                if (s < NJOB) {
+                if (s < njob) {
                     const int p = s < K::NOFF ? NB + s : s - K::NOFF;
-                    tile_job(ch, p, K::NBV >= 2 && p >= NB && !add, !MAP);
+                    tile_job(ch, p, K::NBV >= 2 && p >= NB && !add, !map);
                 }
             }
         };
@@ -927,10 +976,10 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 #pragma unroll
                 for (int ct = 0; ct < NDK; ++ct) {
                     if (!add) ak[ct] = *(const V4 *)(Kr + (16 * I + n) * PK + 16 * ct + 4 * g);
-                    if constexpr (!MAP) bq[ct] = *(const V4 *)(Qr + (16 * I + n) * PK + 16 * ct + 4 * g);
+                    if (!map) bq[ct] = *(const V4 *)(Qr + (16 * I + n) * PK + 16 * ct + 4 * g);
                 }
                 R[I] = add ? zero4() : mma_tiles<K::KD, In, NDK>(zero4(), ak, ss);    // [16I + 4g + i][n]
-                if constexpr (!MAP) O1[I] = mma_tiles<K::KD, In, NDK>(zero4(), ss, bq);   // [v = 4g + i][16I + n]
+                if (!map) O1[I] = mma_tiles<K::KD, In, NDK>(zero4(), ss, bq);   // [v = 4g + i][16I + n]
             };
             if (allfast) {
 #pragma unroll
@@ -986,7 +1035,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             // ---- O^T = (Qbar S^T)^T + E^T P^T, written as O rows (rows past the end dropped)
             const __amdgpu_buffer_rsrc_t ro = buf_rsrc(out + vcol + t0 * HDV, (unsigned)nval * rowb_v);
 #pragma unroll
-            for (int I = 0; I < (MAP ? 0 : NB); ++I) {
+            for (int I = 0; I < (map ? 0 : NB); ++I) {
                 V4 pb[NB];
 #pragma unroll
                 for (int J = 0; J < NB; ++J)
@@ -1029,7 +1078,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 // throughout.
 template <int DK>
 __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const float *seg_map,
-                                                          float *seg_start, int dv, int nsegs)
+                                                          float *seg_start, int dv, int nsegs, int p0)
 {
     constexpr int CPT = DK / 16;                  // columns per thread
     constexpr int MR = DK > 64 ? DK / 2 : DK;     // rows of M staged at a time
@@ -1041,8 +1090,10 @@ __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const
     const int row = rb * 16 + r;
     float acc[CPT];
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) acc[j] = S0 ? S0[((long)head * dv + row) * DK + c0 + j] : 0.f;
-    for (int p = 0;; ++p) {
+    for (int j = 0; j < CPT; ++j)
+        acc[j] = p0 > 0 ? seg_start[(((long)head * nsegs + p0) * dv + row) * DK + c0 + j]
+                        : (S0 ? S0[((long)head * dv + row) * DK + c0 + j] : 0.f);
+    for (int p = p0;; ++p) {
         float *dst = seg_start + (((long)head * nsegs + p) * dv + row) * DK + c0;
 #pragma unroll
         for (int j = 0; j < CPT; ++j) dst[j] = acc[j];
@@ -1069,35 +1120,34 @@ __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const
     }
 }
 
-// One pass of the chunk kernel over nsu segments per sequence and nrows state
-// rows per head.
+// One launch of the chunk kernel over `grid` workgroups (xcd_map: the per-region
+// XCD remap flags, each set only where its region's unit count is a multiple of 8).
 template <typename In, int DK, int BV, int C, bool MAP, int VAR>
-hipError_t launch_chunk_pass_v(const ChunkArgs &a, int nsu, int nrows)
+hipError_t launch_chunk_grid_v(const ChunkArgs &a, long grid, int xcd_map)
 {
     typedef ChunkCfg<In, DK, BV, C> K;
-    const long units = (long)a.nseq * a.H * nsu;
-    const long grid = units * (nrows / BV);
     if (grid == 0) return hipSuccess;
-    const int xcd_map = (units % 8 == 0) ? 1 : 0;
     // the kernel divides by the segment count: never pass less than 1
     hipLaunchKernelGGL((chunk_fwd_kernel<In, DK, BV, C, MAP, VAR>), dim3((unsigned)grid), dim3(K::NT), 0,
                        a.stream, (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S0,
                        (In *)a.out, a.S_final, a.cu_seqlens, a.T, a.H, a.dv, xcd_map, a.nsegs < 1 ? 1 : a.nsegs,
-                       a.seg_start, a.seg_map, a.gate, a.add, a.prep);
+                       a.seg_start, a.seg_map, a.gate, a.add, a.prep, a.nsegs > 1 ? a.lead : 0);
     return hipGetLastError();
 }
 
 // The same, with the kernel specialised for the plain recurrence or not.
 template <typename In, int DK, int BV, int C, bool MAP>
-hipError_t launch_chunk_pass(const ChunkArgs &a, int nsu, int nrows)
+hipError_t launch_chunk_grid(const ChunkArgs &a, long grid, int xcd_map)
 {
-    if (a.prep != 0 && a.gate == 0 && a.add == 0) return launch_chunk_pass_v<In, DK, BV, C, MAP, 2>(a, nsu, nrows);
-    if (a.gate != 0 || a.add != 0 || a.prep != 0) return launch_chunk_pass_v<In, DK, BV, C, MAP, 1>(a, nsu, nrows);
-    return launch_chunk_pass_v<In, DK, BV, C, MAP, 0>(a, nsu, nrows);
+    if (a.prep != 0 && a.gate == 0 && a.add == 0) return launch_chunk_grid_v<In, DK, BV, C, MAP, 2>(a, grid, xcd_map);
+    if (a.gate != 0 || a.add != 0 || a.prep != 0) return launch_chunk_grid_v<In, DK, BV, C, MAP, 1>(a, grid, xcd_map);
+    return launch_chunk_grid_v<In, DK, BV, C, MAP, 0>(a, grid, xcd_map);
 }
 
-// The whole prefill: one pass, or (nsegs > 1) the map pass over all segments
-// but the last, the composition of the maps, and the pass over all segments.
+// The whole prefill: one pass, or (nsegs > 1) the map launch (the maps of every
+// segment but the last; with a lead segment, segment 0's whole pass beside the
+// maps of segments 1 .. nsegs - 2), the composition of the maps, and the pass
+// over every segment that still needs one.
 template <typename In, int DK, int BV, int C>
 hipError_t launch_chunk_t(const ChunkArgs &a)
 {
@@ -1105,20 +1155,32 @@ hipError_t launch_chunk_t(const ChunkArgs &a)
     if constexpr (!K::fits) {
         return hipErrorInvalidConfiguration;
     } else {
-        if (a.nsegs <= 1) return launch_chunk_pass<In, DK, BV, C, false>(a, 1, a.dv);
+        const long nheads = (long)a.nseq * a.H, nvA = a.dv / BV;
+        if (a.nsegs <= 1) return launch_chunk_grid<In, DK, BV, C, false>(a, nheads * nvA, nheads % 8 == 0);
         if constexpr (DK % BV != 0) {
             return hipErrorInvalidConfiguration;   // the virtual rows fill whole value blocks
         } else {
-            hipError_t e = launch_chunk_pass<In, DK, BV, C, true>(a, a.nsegs - 1, a.dv + DK);
+            const long nvB = (a.dv + DK) / BV;
+            const bool lead = a.lead > 0;
+            hipError_t e;
+            if (lead) {
+                const long unitsB = nheads * (a.nsegs - 2);
+                e = launch_chunk_grid<In, DK, BV, C, true>(a, nheads * nvA + unitsB * nvB,
+                                                            (nheads % 8 == 0 ? 1 : 0) | (unitsB % 8 == 0 ? 2 : 0));
+            } else {
+                const long units = nheads * (a.nsegs - 1);
+                e = launch_chunk_grid<In, DK, BV, C, true>(a, units * nvB, units % 8 == 0);
+            }
             if (e != hipSuccess) return e;
             const long ncomp = (long)a.nseq * a.H * (a.dv / 16);
             if (ncomp > 0) {
                 hipLaunchKernelGGL((seg_compose_kernel<DK>), dim3((unsigned)ncomp), dim3(256), 0, a.stream, a.S0,
-                                   (const float *)a.seg_map, a.seg_start, a.dv, a.nsegs);
+                                   (const float *)a.seg_map, a.seg_start, a.dv, a.nsegs, lead ? 1 : 0);
                 e = hipGetLastError();
                 if (e != hipSuccess) return e;
             }
-            return launch_chunk_pass<In, DK, BV, C, false>(a, a.nsegs, a.dv);
+            const long units = nheads * (lead ? a.nsegs - 1 : a.nsegs);
+            return launch_chunk_grid<In, DK, BV, C, false>(a, units * nvA, units % 8 == 0);
         }
     }
 }

@@ -17,6 +17,9 @@ struct ChunkArgs {
     // seg_map [nseq*H][nsegs-1][dv+dk][dk] and seg_start [nseq*H][nsegs][dv][dk] fp32
     int nsegs;
     float *seg_map, *seg_start;
+    // lead > 0: segment 0 is about lead / 10 times as long as each later one and
+    // runs its whole pass in the map launch (nsegs >= 2); 0: equal segments
+    int lead;
     // variant: gate 0 per channel, 1 scalar per token and head, 2 none;
     // add 1 = additive write; prep 1 = raw q, k and gate pre-activations
     int gate, add, prep;
