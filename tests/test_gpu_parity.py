@@ -347,6 +347,26 @@ def test_segmented_varlen(dev):
         assert_close(f"segmented varlen {dtype}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
 
 
+@pytest.mark.parametrize("lead", ["0", "10", "25", "60"])
+def test_segmented_lead_ratios(dev, lead, monkeypatch):
+    """KDA_SEG_LEAD sets segment 0's length relative to the others (0: equal
+    segments, segment 0 mapped like the rest): dense and packed inputs, with
+    sequences short enough that segment 0 is empty."""
+    monkeypatch.setenv("KDA_SEG_LEAD", lead)
+    note(f"case segment lead {lead}: B1 T1000 H2 d64 bf16 C64, 5 segments; varlen, 4 segments")
+    p = kda_synth.prefill(1, 1000, 2, 64, 64, dtype="bf16", s0_sigma=0.1, seed=47, device=dev)
+    o_ref, s_ref = oracle_dense(p)
+    out, sf = gpu_chunk(p, 64, segments=5)
+    assert_close(f"lead {lead} dense", f64(out), f64(sf), o_ref, s_ref, TOL["bf16"])
+    lengths = [700, 5, 0, 130, 64]
+    p = kda_synth.prefill_varlen(lengths, 2, 128, 64, dtype="bf16", s0_sigma=0.1, seed=48, device=dev)
+    out, sf = kda.chunk_fwd_varlen(p.q, p.k, p.v, p.log_alpha, p.beta, p.cu_seqlens, S0=p.S0, C=32, segments=4)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.forward_varlen(f64(p.q), f64(p.k), f64(p.v), f64(p.log_alpha), f64(p.beta),
+                                         np.array(p.cu_host), S0=f64(p.S0))
+    assert_close(f"lead {lead} varlen", f64(out), f64(sf), o_ref, s_ref, TOL["bf16"])
+
+
 def test_segmented_is_deterministic(dev):
     note("case segmented determinism B1 T900 H2 d128 bf16, 4 segments (two runs, bitwise)")
     p = kda_synth.prefill(1, 900, 2, 128, 128, dtype="bf16", s0_sigma=0.1, seed=47, device=dev)
