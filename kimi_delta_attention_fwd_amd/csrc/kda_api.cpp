@@ -153,6 +153,22 @@ int device_cus()
     return m;
 }
 
+// Rounds of workgroups in the map launch: g workgroups, one per CU, the first
+// nA of them (segment 0's whole pass) holding their CUs for the whole launch.
+// Workgroups are dealt to the 8 XCDs round-robin and, within one, to its 4
+// shader engines round-robin (cus / 32 CUs each), so a later round fits only
+// where the engine holding the most lead workgroups has CUs left for its
+// share.  (Measured: 496 workgroups with 16 lead ones take three rounds, 480
+// with 32 take two.)
+long map_launch_rounds(long g, long nA, int cus)
+{
+    if (g <= cus) return 1;
+    const long per_se = cus / 32 > 0 ? cus / 32 : 1;
+    const long free_se = per_se - (nA + 31) / 32;
+    if (free_se <= 0) return 1L << 30;
+    return 1 + (g - cus + 32 * free_se - 1) / (32 * free_se);
+}
+
 // Lead segment of the segmented schedule (tenths of a later segment's length).
 // The map launch holds segment 0's whole pass (nheads * dv / bv workgroups)
 // beside the maps of segments 1 .. nseg - 2 ((dv + dk) / bv each); a map chunk
@@ -166,21 +182,22 @@ int seg_lead(long nheads, int dk, int dv, int bv, int nseg, int cus)
         const int v = std::atoi(env);
         if (v >= 0 && v <= 1000) return v;
     }
-    const long g1 = nheads * ((long)(nseg - 2) * ((dv + dk) / bv) + dv / bv);
-    const long rounds = (g1 + cus - 1) / cus;
-    return (int)(8.5 * (double)rounds + 0.5);
+    const long nA = nheads * (dv / bv);
+    const long rounds = map_launch_rounds(nheads * (long)(nseg - 2) * ((dv + dk) / bv) + nA, nA, cus);
+    return rounds > 100 ? 1000 : (int)(8.5 * (double)rounds + 0.5);
 }
 
 // Segment count for a dense batch from a model of the run time in chunk steps.
 // A pass of g workgroups that each walk L chunks takes ceil(g / CUs) (L + 1)
 // steps (one workgroup per compute unit; the extra step is the prologue: the
 // first chunk's operands, the incoming state and the final store).  With s
-// segments the map launch takes max(L0 + 1, 0.85 ceil(g1 / CUs) (L + 1)) (the
+// segments the map launch takes max(L0 + 1, 0.85 rounds (L + 1)) (the
 // lead segment's whole pass beside the maps, a map chunk being about 0.85 of a
 // full one), the serial composition 0.6 (dk / 64)^1.5 steps per segment, the
 // second pass ceil(g3 / CUs) (L + 1) over segments 1 .. s - 1, and the two
-// extra launches about one step.  Fitted to measured runs: 1 segment for B=4
-// H=32 T=8192, 9 for B=1 H=16 T=65536 (d = 128), 8 for B=2 H=4 T=1024 (d = 64).
+// extra launches about one step; rounds as in map_launch_rounds.  Fitted to
+// measured runs: 1 segment for B=4 H=32 T=8192, 9 for B=1 H=16 T=65536
+// (d = 128), 9 for B=2 H=4 T=1024 (d = 64).
 int auto_segments(bool f32, int B, int T, int H, int dk, int dv, int C)
 {
     if (B <= 0 || T <= 0 || H <= 0 || !supported_d(dk) || !supported_d(dv) || !supported_c(C)) return 1;
@@ -200,7 +217,7 @@ int auto_segments(bool f32, int B, int T, int H, int dk, int dv, int C)
             const long L = (10 * nch + 10 * (s - 1) + lead - 1) / (10 * (s - 1) + lead);
             const long L0 = nch - (s - 1) * L > 0 ? nch - (s - 1) * L : 0;
             const long g1 = nheads * ((s - 2) * nvB + nvA), g3 = nheads * (s - 1) * nvA;
-            const double map = 0.85 * (double)((g1 + cus - 1) / cus) * (double)(L + 1);
+            const double map = 0.85 * (double)map_launch_rounds(g1, nheads * nvA, cus) * (double)(L + 1);
             cost = (map > (double)(L0 + 1) ? map : (double)(L0 + 1)) + 0.6 * std::pow(dk / 64.0, 1.5) * s +
                    (double)((g3 + cus - 1) / cus) * (double)(L + 1) + 1.0;
         }

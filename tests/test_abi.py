@@ -203,6 +203,14 @@ def test_auto_segments_model(lib):
     # measured (44-46 us against 63 for one pass)
     assert kda.kda_chunk_auto_segments(1, 65536, 16, 128, 128, 64, False) == 9
     assert kda.kda_chunk_auto_segments(2, 1024, 4, 64, 64, 64, False) == 9
+    # more long-sequence shapes, each pick the measured best over 1..20
+    # segments on one MI355X (ms): B1 T32768 H16 d128 -> 9 (0.74), B2 T32768
+    # H16 -> 5 (1.19), B1 T65536 H32 -> 5 (2.34), B1 T16384 H16 -> 9 (0.41),
+    # B1 T131072 H8 -> 16 (1.67; 17 takes 2.02: its map launch needs a third
+    # round of workgroups), B1 T65536 H16 d64 -> 16 (0.68)
+    for (B, T, H, d), want in (((1, 32768, 16, 128), 9), ((2, 32768, 16, 128), 5), ((1, 65536, 32, 128), 5),
+                               ((1, 16384, 16, 128), 9), ((1, 131072, 8, 128), 16), ((1, 65536, 16, 64), 16)):
+        assert kda.kda_chunk_auto_segments(B, T, H, d, d, 64, False) == want, (B, T, H, d)
     # never more segments than chunks, never below 1
     assert kda.kda_chunk_auto_segments(1, 100, 1, 64, 64, 64, False) <= 2
     assert kda.kda_chunk_auto_segments(0, 0, 1, 64, 64, 64, True) == 1
