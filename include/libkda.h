@@ -31,8 +31,9 @@
  *
  * OWNERSHIP AND EXECUTION.  Every pointer is device memory owned by the
  * caller (the segmented entry points take their scratch space as a
- * caller-owned workspace).  The library allocates nothing, keeps no mutable global state and is
- * thread-safe.  Work is enqueued asynchronously on `stream` (a hipStream_t
+ * caller-owned workspace).  The library allocates nothing and is thread-safe;
+ * its only global state is a per-thread message for kda_last_error() and a
+ * per-device cache of the compute-unit count.  Work is enqueued asynchronously on `stream` (a hipStream_t
  * passed as void*; NULL is the default stream).  KDA_OK means "validated and
  * enqueued"; faults inside a kernel surface at the caller's next
  * synchronisation of that stream.
@@ -93,6 +94,10 @@ typedef enum {
  *   S_final  fp32 [B,H,dv,dk] state after token T-1; NULL = not written.
  *            May be the same pointer as S0 (in-place continuation).
  *   C        chunk length; T need not be a multiple of C.
+ * Each workgroup takes one (sequence, head) and a block of value rows, the
+ * widest of 64, 32 or 16 that fits; the environment variable KDA_CHUNK_BV
+ * (16, 32 or 64) overrides that schedule choice, as it does for every chunk
+ * entry point.
  */
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v,
                            const float *log_alpha, const float *beta,
