@@ -312,13 +312,17 @@ struct ChunkCfg {
 //
 // MAP = false: the prefill itself.  With nsegs > 1 each workgroup runs one of
 // nsegs consecutive segments of its sequence's chunks, from the incoming state
-// seg_start[(head, seg)] (segment 0 included, which holds S0); only the last
-// segment writes S_final.
-// MAP = true: the affine map of each segment but the last.  The state is
-// augmented with DK "virtual" rows that start at the identity and see v = 0;
-// the dv real rows start at zero.  After the segment the real rows hold N and
-// the virtual rows M of S_end = S_start M + N, written to seg_map[(head, seg)];
-// no output is written and q is not read.
+// seg_start[(head, seg)]; only the last segment writes S_final.  With equal
+// segments (lead = 0) that is every segment, segment 0's incoming state being
+// S0; with a lead segment (lead > 0) segments 1 .. nsegs - 1.
+// MAP = true: the affine map of each segment but the last (lead > 0: but the
+// first and the last).  The state is augmented with DK "virtual" rows that
+// start at the identity and see v = 0; the dv real rows start at zero.  After
+// the segment the real rows hold N and the virtual rows M of
+// S_end = S_start M + N, written to seg_map[(head, seg)]; no output is written
+// and q is not read.  With a lead segment the launch's first workgroups run
+// segment 0 as a plain pass instead (a runtime flag, folded away when MAP is
+// false): from S0, writing its outputs and seg_start[(head, 1)].
 template <typename In, int DK, int BV, int C, bool MAP, int VAR>
 __global__ void __launch_bounds__((ChunkCfg<In, DK, BV, C>::NT), 1)
 chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
