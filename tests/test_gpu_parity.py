@@ -289,8 +289,9 @@ SEG_SHAPES = [
 
 @pytest.mark.parametrize("B,T,H,dk,dv,C,dtype,nseg,with_s0", SEG_SHAPES)
 def test_segmented_matches_oracle(dev, B, T, H, dk, dv, C, dtype, nseg, with_s0):
-    """The segment-parallel schedule (map pass, composition, rerun) against the
-    oracle, and against the single pass on the same inputs."""
+    """The segment-parallel schedule (map launch with the lead segment,
+    composition, second pass) against the oracle, and against the single pass
+    on the same inputs."""
     note(f"case segmented B{B} T{T} H{H} dk{dk} dv{dv} C{C} {dtype} segments={nseg} S0={with_s0}")
     p = kda_synth.prefill(B, T, H, dk, dv, dtype=dtype, s0_sigma=0.1 if with_s0 else None,
                           seed=2000 + T + dk + dv + nseg, device=dev)
