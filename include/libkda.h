@@ -319,7 +319,12 @@ kda_status_t kda_recurrent_step_f32(const float *q, const float *k, const float 
  *   log_alpha fp32 [N,T,H,dk];  beta fp32 [N,T,H]
  *   S         fp32 [N,H,dv,dk], updated IN PLACE from S_{t-1} to S_{t+T-1}.
  *
- * T = 0 is a no-op.  T = 1 gives exactly kda_recurrent_step's result.
+ * T = 0 is a no-op.  T = 1 gives exactly kda_recurrent_step's result, and
+ * any T the same bits as T single steps.  The per-token work is serial inside
+ * a workgroup: from about T = 16 on, the chunk schedule on the same tensors
+ * (kda_chunk_fwd with B = N, S0 = S_final = S, C = 16 below T = 32, else 32)
+ * is faster.  Measured at N = 256, H = 32, d = 128: T = 8 0.24 ms here against
+ * 0.26; T = 16 0.38 against 0.27; T = 64 1.25 against 0.45.
  */
 kda_status_t kda_recurrent_fwd(const void *q, const void *k, const void *v,
                                const float *log_alpha, const float *beta,
