@@ -378,7 +378,11 @@ def recurrent_step(q, k, v, log_alpha, beta, S, out=None, stream=None):
 
 def recurrent_fwd(q, k, v, log_alpha, beta, S, out=None, stream=None, gate="channel", write="delta", raw=False):
     """T decode tokens per sequence on [N, T, H, d] tensors in one launch; S
-    [N, H, dv, dk] fp32 is updated in place.  Returns out [N, T, H, dv]."""
+    [N, H, dv, dk] fp32 is updated in place.  Returns out [N, T, H, dv].
+
+    The result has the bits of T single steps.  From about T = 16 on,
+    ``chunk_fwd(q, k, v, log_alpha, beta, S0=S, C=16 or 32)`` on the same
+    tensors is faster (same result up to rounding)."""
     import torch
     f32 = _mode(q)
     N, T, H, dk = q.shape
