@@ -32,9 +32,11 @@
  * OWNERSHIP AND EXECUTION.  Every pointer is device memory owned by the
  * caller (the segmented entry points take their scratch space as a
  * caller-owned workspace).  The library allocates nothing and is thread-safe;
- * its only global state is a per-thread message for kda_last_error() and a
- * per-device cache of the compute-unit count.  Work is enqueued asynchronously on `stream` (a hipStream_t
- * passed as void*; NULL is the default stream).  KDA_OK means "validated and
+ * its only global state is a per-thread message for kda_last_error(), a
+ * per-device cache of the compute-unit count, and the fixed scratch array of
+ * kda_chunk_fwd_segmented_noalloc (with its per-device address).  Work is
+ * enqueued asynchronously on `stream` (a hipStream_t passed as void*; NULL is
+ * the default stream).  KDA_OK means "validated and
  * enqueued"; faults inside a kernel surface at the caller's next
  * synchronisation of that stream.
  *
@@ -184,6 +186,36 @@ kda_status_t kda_chunk_fwd_segmented_f32(const float *q, const float *k, const f
                                          int B, int T, int H, int dk, int dv, int C,
                                          int nseg, void *workspace, size_t workspace_bytes,
                                          void *stream);
+
+/*
+ * kda_chunk_fwd_segmented without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving loops
+ * and harnesses that forbid hipMalloc.  The scratch space is a fixed device
+ * array inside the library of KDA_NOALLOC_SCRATCH_BYTES (64 MiB), one copy per
+ * GPU, held from the library's load until the process ends; this call
+ * allocates nothing (no hipMalloc, no hipFree, no allocating library call).
+ *
+ *   - A request whose workspace (kda_chunk_segmented_workspace_bytes) exceeds
+ *     KDA_NOALLOC_SCRATCH_BYTES is rejected with KDA_ERR_UNSUPPORTED before
+ *     any HIP call.  At d = 128 one segment of one (sequence, head) needs
+ *     192 KiB (B=1, H=16 takes up to 22 segments).
+ *   - Every call on one GPU uses that GPU's one array.  Calls that overlap in
+ *     time on the same GPU (two streams, two threads) race and give undefined
+ *     results; calls on one stream are ordered and safe.  Nothing needs
+ *     clearing between calls: every scratch byte a call reads, the same call
+ *     wrote first.
+ *   - The first call on a device looks up the array's device address there
+ *     (hipGetSymbolAddress, after the argument checks); a failed lookup is
+ *     KDA_ERR_HIP.
+ * Operation, layouts, other arguments and results (bit for bit) as in
+ * kda_chunk_fwd_segmented with the same nseg.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+kda_status_t kda_chunk_fwd_segmented_noalloc(const void *q, const void *k, const void *v,
+                                             const float *log_alpha, const float *beta,
+                                             const float *S0, void *out, float *S_final,
+                                             int B, int T, int H, int dk, int dv, int C,
+                                             int nseg, void *stream);
 
 /* Packed-sequence variants: every sequence is cut into nseg segments. */
 kda_status_t kda_chunk_fwd_varlen_segmented(const void *q, const void *k, const void *v,

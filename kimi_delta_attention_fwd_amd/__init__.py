@@ -24,6 +24,7 @@ __all__ = [
     "kda_chunk_fwd", "kda_chunk_fwd_f32", "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_f32",
     "kda_chunk_fwd_segmented", "kda_chunk_fwd_segmented_f32", "kda_chunk_fwd_varlen_segmented",
     "kda_chunk_fwd_varlen_segmented_f32", "kda_chunk_segmented_workspace_bytes", "kda_chunk_auto_segments",
+    "kda_chunk_fwd_segmented_noalloc", "NOALLOC_SCRATCH_BYTES",
     "kda_chunk_fwd_ex", "kda_chunk_fwd_ex_f32", "kda_chunk_fwd_varlen_ex", "kda_chunk_fwd_varlen_ex_f32",
     "kda_recurrent_fwd_ex", "kda_recurrent_fwd_ex_f32", "variant",
     "kda_recurrent_step", "kda_recurrent_step_f32", "kda_recurrent_fwd", "kda_recurrent_fwd_f32",
@@ -87,6 +88,8 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = I
+    lib.kda_chunk_fwd_segmented_noalloc.argtypes = [P] * 8 + [I] * 7 + [P]
+    lib.kda_chunk_fwd_segmented_noalloc.restype = I
     lib.kda_chunk_segmented_workspace_bytes.argtypes = [I] * 5
     lib.kda_chunk_segmented_workspace_bytes.restype = Z
     lib.kda_chunk_auto_segments.argtypes = [I] * 7
@@ -181,6 +184,18 @@ def kda_chunk_fwd_varlen_segmented_f32(q, k, v, log_alpha, beta, S0, out, S_fina
     _check("kda_chunk_fwd_varlen_segmented_f32", load().kda_chunk_fwd_varlen_segmented_f32(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_final),
         _ptr(cu_seqlens), N, T_total, H, dk, dv, C, nseg, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def kda_chunk_fwd_segmented_noalloc(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, dk, dv, C, nseg,
+                                    stream=None):
+    """kda_chunk_fwd_segmented with the library's static scratch array instead
+    of a workspace (no device allocation; calls overlapping on one GPU race)."""
+    _check("kda_chunk_fwd_segmented_noalloc", load().kda_chunk_fwd_segmented_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_final),
+        B, T, H, dk, dv, C, nseg, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def kda_chunk_segmented_workspace_bytes(nseq, H, dk, dv, nseg) -> int:

@@ -3,6 +3,7 @@
 Translation units:
   csrc/kda_chunk_inst.hip  x 8   chunk prefill kernels, one per (input type, dk)
   csrc/kda_decode.hip            decode-step kernels
+  csrc/kda_noalloc.hip           allocation-free segmented entry point (static scratch)
   csrc/kda_api.cpp               C ABI: validation and dispatch (host only)
 
 Objects go to <repo>/_build/, the library to kimi_delta_attention_fwd_amd/libkda.so.
@@ -63,6 +64,8 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
                           "-c", os.path.join(CSRC, "kda_chunk_inst.hip"), "-o", obj])
     units.append([hipcc, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, "kda_decode.hip"),
                   "-o", os.path.join(BUILD, "kda_decode.o")])
+    units.append([hipcc, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, "kda_noalloc.hip"),
+                  "-o", os.path.join(BUILD, "kda_noalloc.o")])
     units.append([hipcc, *COMMON, "-c", os.path.join(CSRC, "kda_api.cpp"),
                   "-o", os.path.join(BUILD, "kda_api.o")])
     jobs = jobs or min(8, os.cpu_count() or 4)

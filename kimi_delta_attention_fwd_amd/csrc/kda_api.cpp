@@ -247,7 +247,8 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
                           const float *log_alpha, const float *beta, const float *S0, void *out,
                           float *S_final, const int32_t *cu_seqlens, int nseq, int T, int T_total,
                           int H, int dk, int dv, int C, void *stream, int nseg = 1, void *workspace = nullptr,
-                          uint64_t workspace_bytes = 0, int variant = 0)
+                          uint64_t workspace_bytes = 0, int variant = 0,
+                          const kda::StaticScratch *scratch = nullptr)
 {
     if (!valid_variant(variant)) return fail(KDA_ERR_BAD_SHAPE, "invalid variant %d", variant);
     const int gate = variant & 3;
@@ -292,7 +293,15 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
                                      Buf{S0, S0 ? ns * 4 : 0, "S0"});
     if (st != KDA_OK) return st;
     const uint64_t wsb = seg_workspace_bytes(nheads, dk, dv, nseg);
-    if (nseg > 1) {
+    if (nseg > 1 && scratch) {
+        // the library's own fixed-size array: it aliases nothing the caller owns
+        if (wsb > scratch->bytes)
+            return fail(KDA_ERR_UNSUPPORTED,
+                        "the segmented schedule needs %llu bytes of scratch here, more than the %llu-byte "
+                        "static array of the allocation-free entry point (use fewer segments or the "
+                        "workspace entry point)",
+                        (unsigned long long)wsb, (unsigned long long)scratch->bytes);
+    } else if (nseg > 1) {
         if (!workspace) return fail(KDA_ERR_NULL_POINTER, "the segmented schedule needs a workspace");
         if (!aligned(workspace, 256)) return fail(KDA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
         if (workspace_bytes < wsb)
@@ -311,6 +320,11 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
                     f32 ? "fp32" : "bf16", dk, dv, C);
     if (nheads == 0 || (ntok == 0 && !S_final)) return ok();
     if (ntok == 0) nseg = 1;   // nothing to split: S0 (or zeros) is copied to S_final
+    if (nseg > 1 && scratch) {   // every check has passed: now the (first) HIP call
+        const char *why = "unknown";
+        workspace = scratch->get(&why);
+        if (!workspace) return fail(KDA_ERR_HIP, "static scratch array not available: %s", why);
+    }
 
     kda::ChunkArgs a;
     a.q = q;
@@ -398,6 +412,15 @@ kda_status_t step_common(bool f32, const void *q, const void *k, const void *v, 
 }
 
 }  // namespace
+
+int kda::chunk_segmented_static(const void *q, const void *k, const void *v, const float *log_alpha,
+                                const float *beta, const float *S0, void *out, float *S_final, int B, int T,
+                                int H, int dk, int dv, int C, int nseg, const StaticScratch &scratch,
+                                void *stream)
+{
+    return chunk_common(false, false, q, k, v, log_alpha, beta, S0, out, S_final, nullptr, B, T, 0, H, dk, dv, C,
+                        stream, nseg, nullptr, 0, 0, &scratch);
+}
 
 extern "C" {
 

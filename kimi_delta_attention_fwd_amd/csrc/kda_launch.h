@@ -58,4 +58,20 @@ hipError_t launch_decode(const DecodeArgs &, bool f32);
 hipError_t launch_decode_multi(const DecodeArgs &, int T, bool f32);
 hipError_t launch_stream_copy(const void *src, void *dst, long n16, hipStream_t stream);
 
+// A fixed-size device array that stands in for the caller's workspace of the
+// segmented schedule (kda_noalloc.hip).  `get` returns its address on the
+// current device (looked up once per device), or NULL with a message in *err.
+struct StaticScratch {
+    unsigned long long bytes;
+    void *(*get)(const char **err);
+};
+
+// kda_chunk_fwd_segmented with the workspace taken from `scratch` instead of
+// the caller: every argument check runs first (a workspace larger than
+// scratch.bytes is rejected there), then scratch.get(), then the launches.
+// Defined in kda_api.cpp.
+int chunk_segmented_static(const void *q, const void *k, const void *v, const float *log_alpha,
+                           const float *beta, const float *S0, void *out, float *S_final, int B, int T, int H,
+                           int dk, int dv, int C, int nseg, const StaticScratch &scratch, void *stream);
+
 }  // namespace kda

@@ -304,3 +304,16 @@ def test_stream_copy_validation(lib):
     assert lib.kda_stream_copy(A, A + 64 * MB + 4, 32, None) == 4
     assert lib.kda_stream_copy(A, A + 16, 32, None) == 6      # the ranges overlap
     assert lib.kda_stream_copy(A + 16, A, 32, None) == 6
+
+
+def test_noalloc_rejects_requests_beyond_its_scratch_before_any_hip_call(lib):
+    # B=4 H=32 d=128 in 16 segments needs about 96 MiB of scratch, more than the static 64 MiB
+    lib.kda_chunk_fwd_segmented_noalloc.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int] * 7 + [ctypes.c_void_p]
+    st = lib.kda_chunk_fwd_segmented_noalloc(A, A + 64 * MB, A + 128 * MB, A + 192 * MB, A + 256 * MB, None,
+                                             A + 320 * MB, A + 384 * MB, 4, 100, 32, 128, 128, 64, 16, None)
+    assert st == 3
+    assert "scratch" in kda.kda_last_error()
+    # and the usual argument checks come first
+    st = lib.kda_chunk_fwd_segmented_noalloc(None, A + 64 * MB, A + 128 * MB, A + 192 * MB, A + 256 * MB, None,
+                                             A + 320 * MB, A + 384 * MB, 1, 100, 2, 64, 64, 64, 3, None)
+    assert st == 1
