@@ -54,10 +54,10 @@
  * VALUE PRECONDITIONS (documented, not checked): log_alpha finite and <= 0;
  * beta in [0, 1]; q and k L2-normalised by the caller ("Kimi K3 notes 1"
  * page, sect. 4: q, k pass a feature map and an L2 normalisation first).
- * The chunk kernels factor the intra-chunk decay relative to 16-token
- * sub-blocks; they need every key channel to decay by less than 80 nats
- * (e^-80) inside any 16-token sub-block of the chunk grid, which holds
- * whenever log_alpha >= -5.
+ * There is no lower bound on log_alpha: a key channel may decay by any
+ * amount, down to a complete clear (log_alpha = -1e4 gives alpha = 0 in
+ * fp32), in every schedule; the per-channel gate exists to keep some channels
+ * while clearing others ("KDA derivation summary" page, sect. 5).
  */
 #ifndef LIBKDA_H
 #define LIBKDA_H

@@ -37,23 +37,31 @@
 // groups meet at two workgroup barriers per chunk; everything the state waves
 // read is double-buffered in LDS.
 //
-// Decay factoring.  e^{G_r - G_j} is never formed pairwise.  Rows are split
+// Decay factoring.  e^{G_r - G_j} is not formed pairwise.  Rows are split
 // into 16-token blocks and every key channel c gets a reference rho_I[c] per
 // block I: 0 (the chunk start) when the channel decays by at most 80 nats over
-// the whole chunk, else G just before block I.  The operand waves store, per
+// the whole chunk, else G just before block I.  With B_I the channel's decay
+// inside block I (a sum of log-decays, <= 0), the operand waves store, per
 // token r of block I,
-//   Kr = k e^{G_r - rho_I},  Qr = q e^{G_r - rho_I}   (both <= |k|, |q|)
-//   Kd = k e^{rho_I - G_r}                             (<= |k| e^{80})
-// and per channel e^{rho_I} and w_IJ = e^{rho_I - rho_J} (J < I, <= 1).  Then
-//   A/P tile (I, J) = [Kr|Qr]_I (Kd_J w_IJ)^T,  Kbar S^T = Kr (S Diag(e^{rho_I}))^T,
+//   Kr = k e^{G_r - rho_I},  Qr = q e^{G_r - rho_I}        (<= |k|, |q|)
+//   Kc = k e^{-G_r} (chunk-start channels, <= |k| e^{80}),
+//        k e^{rho_{I+1} - G_r} (block-referenced ones, <= |k|)
+// and per channel e^{rho_I} and a column scale s_IJ per tile pair: 1 for
+// chunk-start channels, else e^{B_{J+1} + .. + B_{I-1}} (J < I, <= 1) and
+// e^{-B_I} (J = I).  Then
+//   A/P tile (I, J) = [Kr|Qr]_I (Kc_J s_IJ)^T,  Kbar S^T = Kr (S Diag(e^{rho_I}))^T,
 // and Ktil = k e^{G_last - G_r} <= |k|.  When every channel of a chunk takes
-// the chunk-start reference, e^{rho_I} = w_IJ = 1 and both consumers skip the
-// scaling.  Every factor stays in range as long as no key channel decays by
-// more than 80 nats inside one 16-token block (the precondition in the public
-// header).  The factors come from alpha = e^{log_alpha} by running prefix and
-// suffix products inside each lane's tokens, times one exponential per
-// channel of the partial sums across lanes (all exponents <= 0).
-//
+// the chunk-start reference all scales are 1 and the consumers skip them.  A
+// channel whose decay inside block I exceeds 80 nats cannot take e^{-B_I}: it
+// gets s_II = 0 and its pairs of that diagonal tile are formed apart, as
+// products of per-token decays split by halves (hard_block_fn), so any decay,
+// down to a complete clear (alpha = 0), is exact.  The factors come from
+// alpha = e^{log_alpha} by prefix and suffix products over each lane's tokens,
+// times one exponential per channel of sums of the other lanes' log-decays,
+// taken inside the block for block-referenced channels: exponents are sums of
+// log-decays, never differences of cumulative ones, so a deep decay early in
+// a chunk costs no precision later.
+
 // (I + A) E = R is solved by block forward substitution over the 16-row
 // blocks, E_b = D_b (R_b - sum_{J<b} A_bJ E_J) with D_b the inverse of the
 // b-th diagonal block of I + A.  In the bf16 kernels the fp32 A, D_b and the
@@ -260,12 +268,14 @@ struct ChunkCfg {
     static constexpr int NSEG = C / RS;
     static constexpr int NACT = NCG * NSEG;
     // scales block: e^{rho_I} [NB][DK], e^{G_last} [DK], beta [C], per-wave
-    // "all channels referenced to the chunk start" flags [NXW]
+    // "all channels referenced to the chunk start" flags [NXW], per-wave masks
+    // of the blocks with a channel too deep to factor (bit I: block I) [NXW]
     static constexpr int SC_GL = NB * DK, SC_BETA = NB * DK + DK, SC_FLAG = SC_BETA + C;
+    static constexpr int SC_HARD = SC_FLAG + NXW;
     // input preparation (raw q, k): per-wave partial squared norms of k and q
     // [C][NXW] (a token's four partials in one 16-byte LDS read), then per
     // token beta / |k|^2, |k| and 1 / |q|
-    static constexpr int SC_PK = SC_FLAG + NXW, SC_PQ = SC_PK + NXW * C, SC_BH = SC_PQ + NXW * C;
+    static constexpr int SC_PK = SC_HARD + NXW, SC_PQ = SC_PK + NXW * C, SC_BH = SC_PQ + NXW * C;
     static constexpr int SC_KN = SC_BH + C, SC_QI = SC_KN + C, SC_END = SC_QI + C;
     static constexpr float FAST_NATS = 80.f;
 
@@ -273,7 +283,7 @@ struct ChunkCfg {
     static constexpr size_t SZ_R = al(size_t(C) * PK * sizeof(In));     // Kr, Qr, Kd
     static constexpr size_t SZ_KT = al(size_t(DK) * PC * sizeof(In));   // Ktil^T
     static constexpr size_t SZ_SC = al(size_t(SC_END) * sizeof(float));
-    static constexpr size_t SZ_W = al(size_t(NOFF > 0 ? NOFF : 1) * DK * sizeof(float));
+    static constexpr size_t SZ_W = al(size_t(NPAIR) * DK * sizeof(float));   // column scales per tile pair
     static constexpr size_t SZ_A = al(size_t(NPAIR) * 16 * PT * sizeof(float));
     static constexpr size_t SZ_P = al(size_t(NPAIR) * 16 * PT * sizeof(In));
     // double-buffered: written by the operand waves for chunk t+1 while the
@@ -296,8 +306,234 @@ struct ChunkCfg {
     static_assert(16 % RS == 0, "a lane's tokens stay inside one 16-token block");
     static_assert(NACT <= 64, "one operand wave covers its channels");
     static_assert((NSEG & (NSEG - 1)) == 0, "segment scan over a power of two");
-    static_assert(NSEG >= NB && NSEG >= NOFF, "a segment of lanes per scale and w vector");
+    static_assert(NSEG >= NB, "a segment of lanes per block scale vector");
 };
+
+// D = (I + L)^{-1} for the strictly lower 16 x 16 diagonal tile L of A, stored
+// over that tile (At, row pitch PT) so that lane (n, g) writes row n, columns
+// 4g..4g+3.  bf16 kernels: (I - L)(I + L^2)(I + L^4)(I + L^8) (L^16 = 0), from
+// L and L^T in accumulator layout (lt0[i] = L[4g + i][n], lt1[i] = L[n][4g + i]);
+// one fp32 MFMA product of two accumulator tiles gives acc(X^T Y).  (The powers
+// of L can grow like binomial coefficients before they cancel, about 1e-4
+// relative at worst: fine for the bf16 kernels.)
+__device__ __forceinline__ void diag_inverse_bf16(float *At, int PT, int n, int g, f32x4 lt0, f32x4 lt1)
+{
+    auto mm = [](f32x4 x, f32x4 y) {   // acc(X^T Y)
+        const f32x4 a[1] = {x}, b[1] = {y};
+        return mma_tiles<4, float, 1>(zero4(), a, b);
+    };
+    const f32x4 L1 = lt0, U1 = lt1;
+    const f32x4 U2 = mm(L1, U1), L2 = mm(U1, L1);
+    const f32x4 U3 = mm(L1, U2), L4 = mm(U2, L2), U4 = mm(L2, U2);
+    const f32x4 L8 = mm(U4, L4);
+    f32x4 id;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) id[i] = (4 * g + i == n) ? 1.f : 0.f;
+    const f32x4 M1t = id - U1 + U2 - U3;              // ((I - L)(I + L^2))^T
+    const f32x4 M2t = M1t + mm(L4, M1t);              // ... (I + L^4)
+    const f32x4 Dt = M2t + mm(L8, M2t);               // ... (I + L^8)
+    *(f32x4 *)(At + n * PT + 4 * g) = Dt;
+}
+
+// fp32 kernels: column n of D by forward substitution over the rows of the
+// stored tile L (lanes of the other 16-lane rows repeat the work and store
+// nothing).
+__device__ __forceinline__ void diag_inverse_f32(float *At, int PT, int n, int lane)
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float *Lr = At + i * PT;
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int kk = 0; kk + 1 < i; kk += 2) {
+            s0 += Lr[kk] * x[kk];
+            s1 += Lr[kk + 1] * x[kk + 1];
+        }
+        if (i & 1) s0 += Lr[i - 1] * x[i - 1];
+        x[i] = ((i == n) ? 1.f : 0.f) - (s0 + s1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if (lane < 16) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) At[i * PT + n] = x[i];
+    }
+}
+
+// beta / |k|^2 of token r from the operand waves' partial squared norms in a
+// scales block (0 for a zero key: identity tokens past the end of a sequence)
+template <typename K>
+__device__ __forceinline__ float beta_hat(const float *scc, int r)
+{
+    float sk = 0.f;
+#pragma unroll
+    for (int w = 0; w < K::NXW; ++w) sk += scc[K::SC_PK + r * K::NXW + w];
+    return sk > 0.f ? scc[K::SC_BETA + r] * __builtin_amdgcn_rcpf(sk) : 0.f;
+}
+
+// Hard-block correction of diagonal tile I of chunk ch, for the key
+// channels whose decay inside the block is too deep to factor through one
+// reference (their column scale s_II is 0, so the A and P tiles above left
+// them out).  Their pairwise decays e^{G_r - G_j} = prod_{s=j+1..r} alpha_s
+// (r >= j in the block) are split by halves: for h = 8, 4, 2, 1 and tokens
+// r, j of one aligned 2h-token group, r in its upper and j in its lower
+// half, the product is (prod from the upper half's first token to r) x
+// (prod from j + 1 to the lower half's last token), and both factors are
+// <= 1.  Each level is one MFMA product of the two scaled operands, masked
+// to its pairs; the diagonal of P (r = j, no decay) adds q_r . k_r.  Every
+// pair r > j is in exactly one level.  The products come from the chunk's
+// raw inputs, reloaded (they were just read, so they come from L2): lane
+// (n, g) takes token 16 I + n and channels 16 t + 4 g + e.  The corrected
+// A tile is inverted like the others.  Run by one wave per block.
+// Kept out of line (it runs only in chunks with such blocks): the chunk loop's
+// code and schedule stay those of the common case.  LDS arrays arrive as
+// generic pointers.
+template <typename In, int DK, int C>
+__device__ __noinline__ void hard_block_fn(const In *__restrict__ k, const In *__restrict__ q,
+                                           const float *__restrict__ log_alpha, const float *__restrict__ beta,
+                                           long hrow, long t0, long len, int H, int gate, int add, int prep, bool map,
+                                           const float *sW, float *sA, In *sP, const float *scc, int I)
+{
+    typedef ChunkCfg<In, DK, 16, C> K;   // the scales block does not depend on the value-block width
+    typedef typename V4T<In>::type V4;
+    constexpr int NDK = K::NDK, PT = K::PT;
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    const int HDK = H * DK;
+        const unsigned nv = (unsigned)((len - t0 < C) ? len - t0 : C);
+    const int r = 16 * I + n;
+    const int rowb = HDK * (int)sizeof(In);
+    const int voff = r * rowb + 4 * g * (int)sizeof(In);
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + (hrow + t0 * H) * DK, nv * rowb);
+    const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + (hrow + t0 * H) * DK, map ? 0u : nv * rowb);
+    const In *gp = (const In *)log_alpha;
+    const __amdgpu_buffer_rsrc_t rg =
+        prep ? (gate == 1 ? buf_rsrc(gp + hrow + t0 * H, nv * H * (int)sizeof(In))
+                          : buf_rsrc(gp + (hrow + t0 * H) * DK, gate == 0 ? nv * rowb : 0u))
+             : (gate == 1 ? buf_rsrc(log_alpha + hrow + t0 * H, nv * H * 4)
+                          : buf_rsrc(gate == 0 ? log_alpha + (hrow + t0 * H) * DK : beta,
+                                     gate == 0 ? nv * HDK * 4 : 0u));
+    constexpr int TPS = K::KD == 32 ? 2 : 1;   // 16-channel tiles per MFMA step
+    f32x4 accA[4], accP[4], accD = zero4();
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        accA[b] = zero4();
+        accP[b] = zero4();
+    }
+    // one MFMA step of channels at a time (a rolled loop keeps the live
+    // registers few; this path is rare)
+#pragma unroll 1
+    for (int s = 0; s < NDK / TPS; ++s) {
+        V4 kk[TPS], qq[TPS], km[TPS];
+        f32x4 al[TPS];
+#pragma unroll
+        for (int u = 0; u < TPS; ++u) {
+            const int c = 16 * (s * TPS + u);       // this tile's first channel
+            kk[u] = buf_load<V4>(rk, voff + c * (int)sizeof(In), 0);
+            qq[u] = map ? V4{} : buf_load<V4>(rq, voff + c * (int)sizeof(In), 0);
+            if (prep) {   // g in the input type; log_alpha = -softplus(g), 0 past the end
+                if (gate == 1) {
+                    const float x = tof(buf_load<In>(rg, r * H * (int)sizeof(In), 0));
+                    al[u] = f32x4{x, x, x, x};
+                } else {
+                    al[u] = to_f32<In>(buf_load<V4>(rg, voff + c * (int)sizeof(In), 0));
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) al[u][e] = (gate == 2 || r >= (int)nv) ? 0.f : neg_softplus(al[u][e]);
+            } else if (gate == 1) {
+                const float x = buf_load<float>(rg, r * H * 4, 0);
+                al[u] = f32x4{x, x, x, x};
+            } else {
+                al[u] = buf_load<f32x4>(rg, r * HDK * 4 + (c + 4 * g) * 4, 0);
+            }
+            // alpha, and k masked to the hard channels (s_II == 0) for the column side
+            const f32x4 sd = *(const f32x4 *)(sW + I * DK + c + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                al[u][e] = fexp(al[u][e]);
+                km[u][e] = sd[e] == 0.f ? kk[u][e] : fromf<In>(0.f);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int h = 1 << b, pos = n & (h - 1);
+            const bool up = (n >> b) & 1;
+            V4 ya[TPS], xk[TPS], xq[TPS];
+#pragma unroll
+            for (int u = 0; u < TPS; ++u) {
+                f32x4 vk, vq, vy;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // inclusive prefix products (x) and suffix products (y) of
+                    // alpha inside aligned h-token groups
+                    float x = al[u][e], y = al[u][e];
+                    if (h > 1) {
+                        const float a = row_shr<1>(x, 1.f), c = row_shl<1>(y, 1.f);
+                        if (pos >= 1) x *= a;
+                        if (pos + 1 < h) y *= c;
+                    }
+                    if (h > 2) {
+                        const float a = row_shr<2>(x, 1.f), c = row_shl<2>(y, 1.f);
+                        if (pos >= 2) x *= a;
+                        if (pos + 2 < h) y *= c;
+                    }
+                    if (h > 4) {
+                        const float a = row_shr<4>(x, 1.f), c = row_shl<4>(y, 1.f);
+                        if (pos >= 4) x *= a;
+                        if (pos + 4 < h) y *= c;
+                    }
+                    float suf = 1.f;   // exclusive: from the next token to the group's end
+                    if (h > 1) {
+                        const float c = row_shl<1>(y, 1.f);
+                        if (pos < h - 1) suf = c;
+                    }
+                    vk[e] = up ? tof(kk[u][e]) * x : 0.f;
+                    vq[e] = up ? tof(qq[u][e]) * x : 0.f;
+                    vy[e] = up ? 0.f : tof(km[u][e]) * suf;
+                }
+                xk[u] = to_op<In>(vk);
+                xq[u] = to_op<In>(vq);
+                ya[u] = to_op<In>(vy);
+            }
+            if (!add) accA[b] = mma_tiles<K::KD, In, TPS>(accA[b], ya, xk);
+            if (!map) accP[b] = mma_tiles<K::KD, In, TPS>(accP[b], ya, xq);
+        }
+        if (!map) accD = mma_tiles<K::KD, In, TPS>(accD, km, qq);   // P's diagonal: q_r . k_r
+    }
+    // pair (r = n, j = 4g + i) belongs to level b when r and j share their
+    // aligned 2h-token group (the operands keep only r upper, j lower)
+    f32x4 dA = zero4(), dP = zero4();
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool same = ((n ^ (4 * g + i)) >> (b + 1)) == 0;
+            dA[i] += same ? accA[b][i] : 0.f;
+            dP[i] += same ? accP[b][i] : 0.f;
+        }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dP[i] += (4 * g + i == n) ? accD[i] : 0.f;
+        if (!map) {
+        In *pt = sP + I * 16 * PT + n * PT + 4 * g;
+        store4(pt, to_f32<In>(*(const V4 *)pt) + dP);
+    }
+    if (!add) {
+        const float bb = prep ? beta_hat<K>(scc, r) : scc[K::SC_BETA + r];
+        float *at = sA + I * 16 * PT + n * PT + 4 * g;
+        const f32x4 lt1 = *(const f32x4 *)at + dA * bb;   // L[n][4g + i]
+        *(f32x4 *)at = lt1;
+        if constexpr (K::F32) {
+            diag_inverse_f32(sA + I * 16 * PT, PT, n, lane);
+        } else {
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            f32x4 lt0;                                    // L[4g + i][n]
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lt0[i] = sA[I * 16 * PT + (4 * g + i) * PT + n];
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            diag_inverse_bf16(sA + I * 16 * PT, PT, n, g, lt0, lt1);
+        }
+    }
+}
 
 // Variants (uniform arguments, read only when VAR): gate 0 = per-channel log_alpha [.., H, DK],
 // 1 = one log_alpha per token and head [.., H] shared by all key channels,
@@ -438,14 +674,6 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     // strictly lower on the diagonal) and / or the P tile (lower incl. the
     // diagonal).  Tiles are computed transposed, d[i] = X[16I + n][16J + 4g + i],
     // so each lane stores four consecutive columns of one row.
-    // beta / |k|^2 of token r from the operand waves' partial squared norms
-    // (0 for a zero key: identity tokens past the end of a sequence)
-    auto beta_hat = [&](const float *scc, int r) __attribute__((always_inline)) {
-        float sk = 0.f;
-#pragma unroll
-        for (int w = 0; w < K::NXW; ++w) sk += scc[K::SC_PK + r * K::NXW + w];
-        return sk > 0.f ? scc[K::SC_BETA + r] * __builtin_amdgcn_rcpf(sk) : 0.f;
-    };
     auto tile_job = [&](long ch, int p, bool doA, bool doP, f32x4 *lt = nullptr) __attribute__((always_inline)) {
         int I = p, J = p;
         if (p >= NB) {
@@ -460,8 +688,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         V4 cf[NDK];
 #pragma unroll
         for (int t = 0; t < NDK; ++t) cf[t] = *(const V4 *)(sKd + (16 * J + n) * PK + 16 * t + 4 * g);
-        if (I > J && !allfast) {   // Kd_J w_IJ = k e^{rho_I - G} <= |k|
-            const float *wr = sW + (I * (I - 1) / 2 + J) * DK + 4 * g;
+        if (!allfast) {   // the pair's column scale: Kc_J s_IJ = k e^{rho_I - G}
+            const float *wr = sW + p * DK + 4 * g;
 #pragma unroll
             for (int t = 0; t < NDK; ++t) {
                 const f32x4 w4 = *(const f32x4 *)(wr + 16 * t);
@@ -474,7 +702,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 #pragma unroll
             for (int t = 0; t < NDK; ++t) rk[t] = *(const V4 *)(Kr + (16 * I + n) * PK + 16 * t + 4 * g);
             const f32x4 da = mma_tiles<K::KD, In, NDK>(zero4(), cf, rk);
-            const float b = prep ? beta_hat(scc, 16 * I + n) : scc[K::SC_BETA + 16 * I + n];
+            const float b = prep ? beta_hat<K>(scc, 16 * I + n) : scc[K::SC_BETA + 16 * I + n];
             f32x4 va;
 #pragma unroll
             for (int i = 0; i < 4; ++i) va[i] = (I > J || 4 * g + i < n) ? da[i] * b : 0.f;
@@ -486,7 +714,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 f32x4 b4 = *(const f32x4 *)(scc + K::SC_BETA + 16 * I + 4 * g);
                 if (prep) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) b4[i] = beta_hat(scc, 16 * I + 4 * g + i);
+                    for (int i = 0; i < 4; ++i) b4[i] = beta_hat<K>(scc, 16 * I + 4 * g + i);
                 }
                 f32x4 vl;
 #pragma unroll
@@ -508,6 +736,26 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         }
     };
 
+    // Blocks of chunk ch with a key channel too deep to factor (bit I: block I),
+    // from the operand waves' masks; workgroup-uniform after the first barrier.
+    auto hard_mask = [&](long ch) __attribute__((always_inline)) {
+        static_assert(K::NXW == 4 && K::SC_HARD % 4 == 0, "the four masks are one 16-byte LDS read");
+        const f32x4 m4 = *(const f32x4 *)(bufSc(ch) + K::SC_HARD);
+        int m = 0;
+#pragma unroll
+        for (int w = 0; w < K::NXW; ++w) m |= __builtin_bit_cast(int, m4[w]);
+        return __builtin_amdgcn_readfirstlane(m);
+    };
+
+    auto inv_bf16 = [&](int p, f32x4 lt0, f32x4 lt1) __attribute__((always_inline)) {
+        diag_inverse_bf16(sA + p * 16 * PT, PT, n, g, lt0, lt1);
+    };
+    auto inv_f32 = [&](int p) __attribute__((always_inline)) { diag_inverse_f32(sA + p * 16 * PT, PT, n, lane); };
+    auto hard_block = [&](long ch, int I) {
+        hard_block_fn<In, DK, C>(k, q, log_alpha, beta, hrow, ch * C, len, H, gate, add, prep, map, sW, sA, sP,
+                                 bufSc(ch), I);
+    };
+
     if (wave >= K::NBV) {
         // =============== operand waves: chunk t+1 while the state waves run chunk t
         const int xw = wave - K::NBV;
@@ -515,7 +763,6 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         const bool act = lane < K::NACT;
         const int c0 = xw * K::CPW + 4 * cg;        // this lane's channels c0 .. c0+3
         const int r0 = seg * RS;                    // and tokens r0 .. r0+RS-1 (inactive lanes: >= C)
-        const int blk_src = ((r0 / 16) * (16 / RS)) * K::NCG + cg;   // lane holding rho of my block
         typedef typename V4T<In>::type In4;
 
         // Global loads, a chunk ahead, through buffer descriptors bounded to the
@@ -617,7 +864,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                     const float y = __shfl_up(inc[j], d * K::NCG, 64);
                     if (seg >= d) inc[j] += y;
                 }
-            float rhoI[NB][4], ref[4], glast[4];
+            float glast[4];
             bool fastc[4], lane_fast = true;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -627,23 +874,104 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 lane_fast = lane_fast && fastc[j];
             }
             const bool wave_fast = __all(lane_fast);
+            // Exponents at the start of the forward (prefix) pass, of the backward
+            // (suffix) pass for Ktil, and (block-referenced channels) of the
+            // backward pass for the column operand; block sums of log_alpha.
+            float pst[4], sst[4], bst[4], Bt[NB][4];
             if (wave_fast) {   // every channel of the wave takes the chunk-start reference
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    ref[j] = 0.f;
+                    pst[j] = exc[j];
+                    sst[j] = glast[j] - inc[j];
+                    bst[j] = 0.f;
 #pragma unroll
-                    for (int I = 0; I < NB; ++I) rhoI[I][j] = 0.f;
+                    for (int I = 0; I < NB; ++I) Bt[I][j] = 0.f;
                 }
             } else {
+                // Block-local scans of the lane sums: every exponent below is a sum
+                // of log-decays, never a difference of cumulative ones, so a deep
+                // decay earlier in the chunk costs no precision later.
+                constexpr int LPB = 16 / RS;            // lanes of one channel group per 16-token block
+                const int sib = seg % LPB, myI = r0 / 16;
+                float incb[4], sufb[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float rb = __shfl(exc[j], blk_src, 64);               // G before my block
-                    ref[j] = fastc[j] ? 0.f : rb;
+                    incb[j] = tot[j];
+                    sufb[j] = tot[j];
+                }
+#pragma unroll
+                for (int d = 1; d < LPB; d <<= 1)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float y = __shfl_up(incb[j], d * K::NCG, 64);
+                        const float z = __shfl_down(sufb[j], d * K::NCG, 64);
+                        if (sib >= d) incb[j] += y;
+                        if (sib + d < LPB) sufb[j] += z;
+                    }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float y = __shfl_up(incb[j], K::NCG, 64);
+                    const float z = __shfl_down(sufb[j], K::NCG, 64);
+                    const float excb = sib > 0 ? y : 0.f;          // my block's decay before my tokens
+                    const float sufx = sib < LPB - 1 ? z : 0.f;    // ... and after them
+                    float aft = 0.f;                               // the later blocks' decay
 #pragma unroll
                     for (int I = 0; I < NB; ++I) {
-                        const float r = __shfl(exc[j], (I * (16 / RS)) * K::NCG + cg, 64);
-                        rhoI[I][j] = fastc[j] ? 0.f : r;
+                        Bt[I][j] = __shfl(incb[j], ((I + 1) * LPB - 1) * K::NCG + cg, 64);
+                        if (I > myI) aft += Bt[I][j];
                     }
+                    pst[j] = fastc[j] ? exc[j] : excb;
+                    sst[j] = fastc[j] ? glast[j] - inc[j] : sufx + aft;
+                    bst[j] = sufx;
+                }
+            }
+            // per-channel scales, one 4-channel vector store per lane: e^{G_last}
+            // by the first segment's lanes, e^{rho_I} by segment I, the column
+            // scale s_p of tile pair p by segment p mod NSEG.  For a block-
+            // referenced channel (rho_I = G before block I, B_I = block I's decay)
+            //   s_IJ = e^{B_{J+1} + .. + B_{I-1}} (J < I, <= 1),  s_II = e^{-B_I};
+            // a channel whose decay inside block I is too deep for e^{-B_I}
+            // (B_I < -80) gets s_II = 0 and its pairs of that diagonal tile are
+            // formed apart (the hard-block correction).  Chunk-start channels
+            // take 1 everywhere.  The scales are stored also when all are 1: other
+            // waves may take block references, and then the tiles read them for
+            // every channel.
+            float *sc = bufSc(ch);
+            int hard = 0;   // blocks with a channel too deep to factor (bit I)
+            if (!wave_fast) {   // (all factors 1: stored at the end of the stage)
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    if (seg == I) {
+                        f32x4 e;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            float rho = 0.f;
+#pragma unroll
+                            for (int m = 0; m < I; ++m) rho += Bt[m][j];
+                            e[j] = fastc[j] ? 1.f : fexp(rho);
+                        }
+                        *(f32x4 *)(sc + I * DK + c0) = e;
+                    }
+#pragma unroll
+                    for (int J = 0; J <= I; ++J) {
+                        const int p = tile_index(NB, I, J);
+                        if (seg == p % K::NSEG) {
+                            f32x4 w;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                float x = 0.f;
+#pragma unroll
+                                for (int m = J + 1; m < I; ++m) x += Bt[m][j];
+                                const float sd = Bt[I][j] >= -K::FAST_NATS ? fexp(-Bt[I][j]) : 0.f;
+                                w[j] = fastc[j] ? 1.f : (J < I ? fexp(x) : sd);
+                            }
+                            *(f32x4 *)(sW + p * DK + c0) = w;
+                        }
+                    }
+                    bool deep = false;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) deep = deep || (!fastc[j] && Bt[I][j] < -K::FAST_NATS);
+                    if (__ballot(act && deep) != 0) hard |= 1 << I;
                 }
             }
             float al[RS][4];
@@ -656,17 +984,15 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             __asm__ volatile("" ::: "memory");
             if (ch + 1 < nch) prefetch_g(t0 + C);
             In *Kr = bufKr(ch), *Qr = bufQr(ch), *Kt = bufKt(ch);
-            float *sc = bufSc(ch);
-            // forward over my tokens: e^{G - ref} by prefix products -> Kr, Qr
-            // (and Kd = k / e^{G - ref} where some channel keeps a block reference)
+            // forward over my tokens: e^{G - rho} by prefix products -> Kr, Qr
             {
                 float pp[4];
                 float sk[RS], sq[RS];   // prep: squared norms over this wave's channels
 #pragma unroll
-                for (int j = 0; j < 4; ++j) pp[j] = fexp(exc[j] - ref[j]);
+                for (int j = 0; j < 4; ++j) pp[j] = fexp(pst[j]);
 #pragma unroll
                 for (int i = 0; i < RS; ++i) {
-                    f32x4 vkr, vqr, vkd;
+                    f32x4 vkr, vqr;
                     sk[i] = 0.f;
                     sq[i] = 0.f;
 #pragma unroll
@@ -684,11 +1010,6 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                         const int r = r0 + i;
                         store4(Kr + r * PK + c0, vkr);
                         if (!map) store4(Qr + r * PK + c0, vqr);
-                        if (!lane_fast) {
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) vkd[j] = tof(kr[i][j]) * __builtin_amdgcn_rcpf(pp[j]);   // k e^{ref - G}
-                            store4(sKd + r * PK + c0, vkd);
-                        }
                     }
                 }
                 if (prep) {   // per token over the channel group's lanes, stored by its first lane
@@ -709,71 +1030,74 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             // q is free: request the next chunk's q
             __asm__ volatile("" ::: "memory");
             if (ch + 1 < nch) prefetch_q(t0 + C);
-            // backward: e^{G_last - G} by suffix products -> Ktil, and Kd = Ktil e^{-G_last}
-            // where every channel of the lane takes the chunk-start reference
+            // backward: e^{G_last - G} by suffix products -> Ktil, and the column
+            // operand Kc: Ktil e^{-G_last} = k e^{-G} for channels referenced to the
+            // chunk start, k e^{rho_{I+1} - G} (the block's own suffix products,
+            // <= |k|) for block-referenced ones
             {
                 float sf[4], gli[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    sf[j] = fexp(glast[j] - inc[j]);
-                    gli[j] = fexp(-glast[j]);
+                    sf[j] = fexp(sst[j]);
+                    gli[j] = fexp(-glast[j]);   // used for chunk-start channels only (G_last >= -80)
                 }
                 In kt[4][RS];
+                if (wave_fast) {   // a uniform branch: the common case keeps its short loop
 #pragma unroll
-                for (int i = RS - 1; i >= 0; --i) {
-                    f32x4 vkd;
+                    for (int i = RS - 1; i >= 0; --i) {
+                        f32x4 vkd;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float ktf = tof(kr[i][j]) * sf[j];   // k e^{G_last - G}
-                        kt[j][i] = fromf<In>(ktf);
-                        vkd[j] = ktf * gli[j];                     // k e^{-G}
-                        sf[j] *= al[i][j];
+                        for (int j = 0; j < 4; ++j) {
+                            const float ktf = tof(kr[i][j]) * sf[j];   // k e^{G_last - G}
+                            kt[j][i] = fromf<In>(ktf);
+                            vkd[j] = ktf * gli[j];                     // k e^{-G}
+                            sf[j] *= al[i][j];
+                        }
+                        if (act) store4(sKd + (r0 + i) * PK + c0, vkd);
                     }
-                    if (act && lane_fast) store4(sKd + (r0 + i) * PK + c0, vkd);
+                } else {
+                    float sb[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sb[j] = fexp(bst[j]);
+#pragma unroll
+                    for (int i = RS - 1; i >= 0; --i) {
+                        f32x4 vkd;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float kf = tof(kr[i][j]);
+                            const float ktf = kf * sf[j];
+                            kt[j][i] = fromf<In>(ktf);
+                            vkd[j] = fastc[j] ? ktf * gli[j] : kf * sb[j];
+                            sf[j] *= al[i][j];
+                            sb[j] *= al[i][j];
+                        }
+                        if (act) store4(sKd + (r0 + i) * PK + c0, vkd);
+                    }
                 }
                 if (act) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) store_row_swz<In, RS>(Kt, c0 + j, r0, PC, K::SWZ, kt[j]);
                 }
             }
-            // per-channel scales, one 4-channel vector store per lane: e^{G_last}
-            // by the first segment's lanes, e^{rho_I} by segment I, w_IJ by
-            // segment I(I-1)/2 + J.  w is stored also when all factors are 1:
-            // other waves may take block references, and then the tiles read w
-            // for every channel.
             if (seg == 0) *(f32x4 *)(sc + K::SC_GL + c0) = f32x4{fexp(glast[0]), fexp(glast[1]), fexp(glast[2]), fexp(glast[3])};
             if (wave_fast) {   // a uniform branch: no exponentials when every factor is 1
                 const f32x4 one{1.f, 1.f, 1.f, 1.f};
                 if (seg < NB) *(f32x4 *)(sc + seg * DK + c0) = one;
-                if (seg < K::NOFF) *(f32x4 *)(sW + seg * DK + c0) = one;
-            } else {
 #pragma unroll
-                for (int I = 0; I < NB; ++I) {
-                    if (seg == I) {
-                        f32x4 e;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) e[j] = fexp(rhoI[I][j]);
-                        *(f32x4 *)(sc + I * DK + c0) = e;
-                    }
-#pragma unroll
-                    for (int J = 0; J < I; ++J) {
-                        if (seg == I * (I - 1) / 2 + J) {
-                            f32x4 w;
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) w[j] = fexp(rhoI[I][j] - rhoI[J][j]);
-                            *(f32x4 *)(sW + (I * (I - 1) / 2 + J) * DK + c0) = w;
-                        }
-                    }
-                }
+                for (int p = 0; p < K::NPAIR; p += K::NSEG)
+                    if (p + seg < K::NPAIR) *(f32x4 *)(sW + (p + seg) * DK + c0) = one;
             }
-            if (lane == 0) sc[K::SC_FLAG + xw] = wave_fast ? 1.f : 0.f;
+            if (lane == 0) {
+                sc[K::SC_FLAG + xw] = wave_fast ? 1.f : 0.f;
+                sc[K::SC_HARD + xw] = __builtin_bit_cast(float, hard);
+            }
             if (xw == 0 && lane < C) sc[K::SC_BETA + lane] = (lane < nval) ? betar : 0.f;
         };
 
         // ---- stage B: the diagonal A tiles and their block inverses (with P
         //      when there is a single state wave, which then also leaves the
         //      off-diagonal A tiles here)
-        auto stage_b = [&](long ch) __attribute__((always_inline)) {
+        auto stage_b = [&](long ch, int hard) __attribute__((always_inline)) {
             if (prep && xw == 0 && lane < C) {
                 // per-token factors for the state waves' next chunk: beta / |k|^2,
                 // |k| and 1 / |q| (zero vectors give 0)
@@ -794,79 +1118,35 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 }
                 return;
             }
+            // a diagonal tile of a hard block keeps L here: the hard-block
+            // correction completes it and inverts it after the next barrier
             for (int p = xw; p < (K::NBV == 1 ? K::NPAIR : NB); p += K::NXW) {
                 if (p < NB && !K::F32) {
-                    // D_p = (I + L)^{-1} for the strictly lower diagonal tile L, as
-                    // (I - L)(I + L^2)(I + L^4)(I + L^8) (L^16 = 0).  With two
-                    // tiles in accumulator layout, one fp32 MFMA product gives
-                    // acc(X^T Y); D_p^T is built that way from acc(L), acc(L^T)
-                    // and stored so that lane (n, g) writes row n, columns 4g..4g+3.
-                    // (The powers of L can grow like binomial coefficients before
-                    // they cancel, about 1e-4 relative at worst: fine for the bf16
-                    // kernels, the fp32 ones use the substitution below.)
                     f32x4 lt[2];
                     tile_job(ch, p, true, K::NBV == 1 && !map, lt);
-                    auto mm = [](f32x4 x, f32x4 y) {   // acc(X^T Y)
-                        const f32x4 a[1] = {x}, b[1] = {y};
-                        return mma_tiles<4, float, 1>(zero4(), a, b);
-                    };
-                    const f32x4 L1 = lt[0], U1 = lt[1];
-                    const f32x4 U2 = mm(L1, U1), L2 = mm(U1, L1);
-                    const f32x4 U3 = mm(L1, U2), L4 = mm(U2, L2), U4 = mm(L2, U2);
-                    const f32x4 L8 = mm(U4, L4);
-                    f32x4 id;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) id[i] = (4 * g + i == n) ? 1.f : 0.f;
-                    const f32x4 M1t = id - U1 + U2 - U3;              // ((I - L)(I + L^2))^T
-                    const f32x4 M2t = M1t + mm(L4, M1t);              // ... (I + L^4)
-                    const f32x4 Dt = M2t + mm(L8, M2t);               // ... (I + L^8)
-                    *(f32x4 *)(sA + p * 16 * PT + n * PT + 4 * g) = Dt;
+                    if (!((hard >> p) & 1)) inv_bf16(p, lt[0], lt[1]);
                 } else if (p < NB) {
-                    // fp32 kernels: column n of D_p by forward substitution over the
-                    // rows of the stored tile (lanes of the other 16-lane rows repeat
-                    // the work and store nothing)
                     tile_job(ch, p, true, K::NBV == 1 && !map);
-                    float *At = sA + p * 16 * PT;
-                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                    float x[16];
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float *Lr = At + i * PT;
-                        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-                        for (int kk = 0; kk + 1 < i; kk += 2) {
-                            s0 += Lr[kk] * x[kk];
-                            s1 += Lr[kk + 1] * x[kk + 1];
-                        }
-                        if (i & 1) s0 += Lr[i - 1] * x[i - 1];
-                        x[i] = ((i == n) ? 1.f : 0.f) - (s0 + s1);
-                    }
-                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                    if (lane < 16) {
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) At[i * PT + n] = x[i];
-                    }
+                    if (!((hard >> p) & 1)) inv_f32(p);
                 } else {
                     tile_job(ch, p, true, false);
                 }
             }
         };
 
-        // Same barrier sequence as the state waves: two per chunk plus two.
+        // Same barrier sequence as the state waves: two per step, steps -1 .. nch - 1
+        // (step -1 prepares chunk 0; one copy of each stage keeps the code small),
+        // and one more after the tiles of a chunk with hard blocks (the state
+        // waves' hard-block correction).
         if (nch > 0) {
             prefetch_g(0);
             prefetch_q(0);
             prefetch_k(0);
-            stage_a(0);
-            if (nch > 1) prefetch_k(C);
         }
-        __syncthreads();
-        if (nch > 0) stage_b(0);
-        __syncthreads();
         // Stage A sets the pace of the first segment, where each operand wave
         // shares its SIMD with a state wave that has time to spare: the operand
         // waves issue first there (wave priority, this workgroup only).
-        for (long ch = 0; ch < nch; ++ch) {
+        for (long ch = -1; ch < nch; ++ch) {
             __builtin_amdgcn_s_setprio(3);
             if (ch + 1 < nch) {
                 stage_a(ch + 1);
@@ -874,7 +1154,9 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             }
             __builtin_amdgcn_s_setprio(0);
             __syncthreads();
-            if (ch + 1 < nch) stage_b(ch + 1);
+            const int hard = ch + 1 < nch ? hard_mask(ch + 1) : 0;
+            if (ch + 1 < nch) stage_b(ch + 1, hard);
+            if (hard) __syncthreads();
             __syncthreads();
         }
     } else {
@@ -959,111 +1241,122 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 }
             }
         };
+        // Chunks with hard blocks take one more barrier after their tiles; then
+        // the state waves correct those blocks' diagonal tiles.
+        auto hard_phase = [&](long ch, int hm) __attribute__((always_inline)) {
+            if (hm) {
+                __syncthreads();
+                for (int I = cb; I < NB; I += K::NBV)
+                    if ((hm >> I) & 1) hard_block(ch, I);
+            }
+        };
         if (nch > 0) prefetch_v(0);
-        __syncthreads();
-        if (nch > 0) y_tiles(0);
-        __syncthreads();
 
         V4 Eb[NB];   // corrected errors of the chunk, operand type: E[16b + 4g + i][n]
-        for (long ch = 0; ch < nch; ++ch) {
-            const long t0 = ch * C;
-            const int nval = (int)((len - t0 < C) ? len - t0 : C);
-            const In *Kr = bufKr(ch), *Qr = bufQr(ch);
-            const float *sc = bufSc(ch);
-            const float *fl = sc + K::SC_FLAG;
-            const bool allfast = all_flags<K::NXW>(fl);
-            // ---- R = beta (V - Kbar S^T) and (Qbar S^T)^T, per 16-token block I
-            f32x4 R[NB], O1[NB];
-            V4 ss[NDK];
-            auto rows = [&](int I) __attribute__((always_inline)) {
-                V4 ak[NDK], bq[NDK];
-#pragma unroll
-                for (int ct = 0; ct < NDK; ++ct) {
-                    if (!add) ak[ct] = *(const V4 *)(Kr + (16 * I + n) * PK + 16 * ct + 4 * g);
-                    if (!map) bq[ct] = *(const V4 *)(Qr + (16 * I + n) * PK + 16 * ct + 4 * g);
-                }
-                R[I] = add ? zero4() : mma_tiles<K::KD, In, NDK>(zero4(), ak, ss);    // [16I + 4g + i][n]
-                if (!map) O1[I] = mma_tiles<K::KD, In, NDK>(zero4(), ss, bq);   // [v = 4g + i][16I + n]
-            };
-            if (allfast) {
-#pragma unroll
-                for (int ct = 0; ct < NDK; ++ct) ss[ct] = to_op<In>(Sacc[ct]);
-#pragma unroll
-                for (int I = 0; I < NB; ++I) rows(I);
-            } else {
-#pragma unroll
-                for (int I = 0; I < NB; ++I) {
+        for (long ch = -1; ch < nch; ++ch) {   // step -1: only the tiles of chunk 0
+            if (ch >= 0) {
+                const long t0 = ch * C;
+                const int nval = (int)((len - t0 < C) ? len - t0 : C);
+                const In *Kr = bufKr(ch), *Qr = bufQr(ch);
+                const float *sc = bufSc(ch);
+                const float *fl = sc + K::SC_FLAG;
+                const bool allfast = all_flags<K::NXW>(fl);
+                // ---- R = beta (V - Kbar S^T) and (Qbar S^T)^T, per 16-token block I
+                f32x4 R[NB], O1[NB];
+                V4 ss[NDK];
+                auto rows = [&](int I) __attribute__((always_inline)) {
+                    V4 ak[NDK], bq[NDK];
 #pragma unroll
                     for (int ct = 0; ct < NDK; ++ct) {
-                        const f32x4 er = *(const f32x4 *)(sc + I * DK + 16 * ct + 4 * g);
-                        ss[ct] = to_op<In>(Sacc[ct] * er);        // S Diag(e^{rho_I}), transposed
+                        if (!add) ak[ct] = *(const V4 *)(Kr + (16 * I + n) * PK + 16 * ct + 4 * g);
+                        if (!map) bq[ct] = *(const V4 *)(Qr + (16 * I + n) * PK + 16 * ct + 4 * g);
                     }
-                    rows(I);
-                }
-            }
+                    R[I] = add ? zero4() : mma_tiles<K::KD, In, NDK>(zero4(), ak, ss);    // [16I + 4g + i][n]
+                    if (!map) O1[I] = mma_tiles<K::KD, In, NDK>(zero4(), ss, bq);   // [v = 4g + i][16I + n]
+                };
+                if (allfast) {
 #pragma unroll
-            for (int I = 0; I < NB; ++I) {
-                const f32x4 b4 = *(const f32x4 *)(sc + (prep ? K::SC_BH : K::SC_BETA) + 16 * I + 4 * g);
-                f32x4 vt;                                           // V[16I + 4g + i][n]
-                if constexpr (K::F32) {
-                    const V4 va[1] = {vr[I]}, vi[1] = {ident[0]};
-                    vt = mma_tiles<4, In, 1>(zero4(), va, vi);
+                    for (int ct = 0; ct < NDK; ++ct) ss[ct] = to_op<In>(Sacc[ct]);
+#pragma unroll
+                    for (int I = 0; I < NB; ++I) rows(I);
                 } else {
-                    vt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[I / 2], ident[I & 1], zero4(), 0, 0, 0);
-                }
-                if (prep) vt = vt * *(const f32x4 *)(sc + K::SC_KN + 16 * I + 4 * g);   // |k| v
 #pragma unroll
-                for (int i = 0; i < 4; ++i) R[I][i] = b4[i] * (vt[i] - R[I][i]);
-            }
-            if (ch + 1 < nch) prefetch_v(t0 + C);
-
-            // ---- (I + A) E = R, block forward substitution (additive write: E = R)
-            if (add) {
+                    for (int I = 0; I < NB; ++I) {
 #pragma unroll
-                for (int b = 0; b < NB; ++b) Eb[b] = to_op<In>(R[b]);
-            } else {
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    f32x4 y = zero4();
-#pragma unroll
-                    for (int J = 0; J < b; ++J) {
-                        const f32x4 a = *(const f32x4 *)(sA + tile_index(NB, b, J) * 16 * PT + n * PT + 4 * g);
-                        y = mma_fp32a<In>(y, a, Eb[J]);
+                        for (int ct = 0; ct < NDK; ++ct) {
+                            const f32x4 er = *(const f32x4 *)(sc + I * DK + 16 * ct + 4 * g);
+                            ss[ct] = to_op<In>(Sacc[ct] * er);        // S Diag(e^{rho_I}), transposed
+                        }
+                        rows(I);
                     }
-                    const f32x4 d = *(const f32x4 *)(sA + b * 16 * PT + n * PT + 4 * g);
-                    const f32x4 e = mma_fp32ab<In>(d, R[b] - y);
-                    Eb[b] = to_op<In>(e);
                 }
-            }
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    const f32x4 b4 = *(const f32x4 *)(sc + (prep ? K::SC_BH : K::SC_BETA) + 16 * I + 4 * g);
+                    f32x4 vt;                                           // V[16I + 4g + i][n]
+                    if constexpr (K::F32) {
+                        const V4 va[1] = {vr[I]}, vi[1] = {ident[0]};
+                        vt = mma_tiles<4, In, 1>(zero4(), va, vi);
+                    } else {
+                        vt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[I / 2], ident[I & 1], zero4(), 0, 0, 0);
+                    }
+                    if (prep) vt = vt * *(const f32x4 *)(sc + K::SC_KN + 16 * I + 4 * g);   // |k| v
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) R[I][i] = b4[i] * (vt[i] - R[I][i]);
+                }
+                if (ch + 1 < nch) prefetch_v(t0 + C);
 
-            // ---- O^T = (Qbar S^T)^T + E^T P^T, written as O rows (rows past the end dropped)
-            const __amdgpu_buffer_rsrc_t ro = buf_rsrc(out + vcol + t0 * HDV, (unsigned)nval * rowb_v);
+                // ---- (I + A) E = R, block forward substitution (additive write: E = R)
+                if (add) {
 #pragma unroll
-            for (int I = 0; I < (map ? 0 : NB); ++I) {
-                V4 pb[NB];
+                    for (int b = 0; b < NB; ++b) Eb[b] = to_op<In>(R[b]);
+                } else {
 #pragma unroll
-                for (int J = 0; J < NB; ++J)
-                    pb[J] = (J <= I) ? *(const V4 *)(sP + tile_index(NB, I, J) * 16 * PT + n * PT + 4 * g) : V4{};
-                f32x4 o = O1[I] + mma_tiles<K::KC, In, NB>(zero4(), Eb, pb);   // O[16I + n][16cb + 4g + i]
-                if (prep) o = o * sc[K::SC_QI + 16 * I + n];                   // / |q|
-                buf_store(to_op<In>(o), ro, voff_o, 16 * I * rowb_v);
-            }
-            // ---- S^T <- Diag(e^{G_last}) S^T + Ktil^T E (Ktil and the scales of this chunk are
-            //      double-buffered, so this needs no barrier)
-            const In *Kt = bufKt(ch);
+                    for (int b = 0; b < NB; ++b) {
+                        f32x4 y = zero4();
 #pragma unroll
-            for (int ct = 0; ct < NDK; ++ct) {
-                const f32x4 gl = *(const f32x4 *)(sc + K::SC_GL + 16 * ct + 4 * g);
-                V4 ka[NB];
+                        for (int J = 0; J < b; ++J) {
+                            const f32x4 a = *(const f32x4 *)(sA + tile_index(NB, b, J) * 16 * PT + n * PT + 4 * g);
+                            y = mma_fp32a<In>(y, a, Eb[J]);
+                        }
+                        const f32x4 d = *(const f32x4 *)(sA + b * 16 * PT + n * PT + 4 * g);
+                        const f32x4 e = mma_fp32ab<In>(d, R[b] - y);
+                        Eb[b] = to_op<In>(e);
+                    }
+                }
+
+                // ---- O^T = (Qbar S^T)^T + E^T P^T, written as O rows (rows past the end dropped)
+                const __amdgpu_buffer_rsrc_t ro = buf_rsrc(out + vcol + t0 * HDV, (unsigned)nval * rowb_v);
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    ka[b] = *(const V4 *)(Kt + Panel<In, 16>::swz_index(16 * ct + n, 16 * b + 4 * g, PC, K::SWZ));
-                Sacc[ct] = mma_tiles<K::KC, In, NB>(Sacc[ct] * gl, ka, Eb);
+                for (int I = 0; I < (map ? 0 : NB); ++I) {
+                    V4 pb[NB];
+#pragma unroll
+                    for (int J = 0; J < NB; ++J)
+                        pb[J] = (J <= I) ? *(const V4 *)(sP + tile_index(NB, I, J) * 16 * PT + n * PT + 4 * g) : V4{};
+                    f32x4 o = O1[I] + mma_tiles<K::KC, In, NB>(zero4(), Eb, pb);   // O[16I + n][16cb + 4g + i]
+                    if (prep) o = o * sc[K::SC_QI + 16 * I + n];                   // / |q|
+                    buf_store(to_op<In>(o), ro, voff_o, 16 * I * rowb_v);
+                }
+                // ---- S^T <- Diag(e^{G_last}) S^T + Ktil^T E (Ktil and the scales of this chunk are
+                //      double-buffered, so this needs no barrier)
+                const In *Kt = bufKt(ch);
+#pragma unroll
+                for (int ct = 0; ct < NDK; ++ct) {
+                    const f32x4 gl = *(const f32x4 *)(sc + K::SC_GL + 16 * ct + 4 * g);
+                    V4 ka[NB];
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        ka[b] = *(const V4 *)(Kt + Panel<In, 16>::swz_index(16 * ct + n, 16 * b + 4 * g, PC, K::SWZ));
+                    Sacc[ct] = mma_tiles<K::KC, In, NB>(Sacc[ct] * gl, ka, Eb);
+                }
             }
             __syncthreads();
 
-            // ---- the next chunk's tiles
+            // ---- the next chunk's tiles (the hard-block mask is read first, so
+            //      its latency hides behind them)
+            const int hm = ch + 1 < nch ? hard_mask(ch + 1) : 0;
             if (ch + 1 < nch) y_tiles(ch + 1);
+            if (ch + 1 < nch) hard_phase(ch + 1, hm);
             __syncthreads();
         }
         if (sfrow) {

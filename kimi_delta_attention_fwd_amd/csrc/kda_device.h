@@ -145,6 +145,21 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Lane i of each 16-lane row receives x of lane i - D (row_shr) or i + D
+// (row_shl) of the same row; lanes with no such source receive `fill`.
+template <int D>
+__device__ __forceinline__ float row_shr(float x, float fill) {
+    static_assert(D >= 1 && D <= 15, "row shift");
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill), __builtin_bit_cast(int, x),
+                                                                 0x110 + D, 0xF, 0xF, false));
+}
+template <int D>
+__device__ __forceinline__ float row_shl(float x, float fill) {
+    static_assert(D >= 1 && D <= 15, "row shift");
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill), __builtin_bit_cast(int, x),
+                                                                 0x100 + D, 0xF, 0xF, false));
+}
+
 // log(alpha) = -softplus(g) = -(max(g, 0) + log(1 + e^{-|g|})), through the
 // hardware base-2 exponential and logarithm (for e^{-|g|} below ~6e-8 the
 // sum rounds to 1 and log(alpha) to -max(g, 0), an error below 6e-8).

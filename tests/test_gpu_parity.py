@@ -69,13 +69,53 @@ def sampled(p, pairs):
                           f64(torch.stack([p.beta[b, :, h] for b, h in pairs]).unsqueeze(2)), S0=f64(S0))
 
 
+def _ratio(num, den):
+    """num / den elementwise, 0 where both are 0 (a slice that is exactly zero
+    in the reference and in the result)."""
+    return np.where(num == 0, 0.0, num / np.maximum(den, 1e-300))
+
+
+def worst_per_head(gpu, ref, axes):
+    """Largest normwise relative error over the (sequence, head) slices of a
+    4-d array, each slice normalised by its own max |ref|."""
+    d, a = np.abs(gpu - ref), np.abs(ref)
+    return float(np.max(_ratio(d.max(axis=axes), a.max(axis=axes))))
+
+
+def worst_per_chunk(gpu, ref, width=64):
+    """Same for the width-token windows of every (sequence, head) of an output
+    laid out [B, T, H, dv], each window normalised by its own max |ref|."""
+    B, T, H, V = gpu.shape
+    nc = -(-T // width)
+    pad = ((0, 0), (0, nc * width - T), (0, 0), (0, 0))
+    d = np.pad(np.abs(gpu - ref), pad).reshape(B, nc, width, H, V)
+    a = np.pad(np.abs(ref), pad).reshape(B, nc, width, H, V)
+    return float(np.max(_ratio(d.max(axis=(2, 4)), a.max(axis=(2, 4)))))
+
+
+WORST = {}   # name -> (per-head out, per-chunk out, per-head state): the worst cases seen
+
+
 def assert_close(name, out, sf, o_ref, s_ref, tol):
+    """Normwise relative error of the whole output and final state, and also the
+    worst (sequence, head) slice and the worst 64-token window of each
+    (sequence, head), each normalised by its own max |ref|: an error confined to
+    one head or one chunk of small outputs cannot hide under the tensor's
+    largest values."""
+    assert np.all(np.isfinite(out)) and (sf is None or np.all(np.isfinite(sf)))
     e_o = rel(out, o_ref)
     e_s = rel(sf, s_ref) if s_ref is not None else 0.0
-    note(f"  {name}: out rel err {e_o:.3e}, S_final rel err {e_s:.3e} (bar {tol:g})")
-    assert np.all(np.isfinite(out)) and (sf is None or np.all(np.isfinite(sf)))
+    h_o = worst_per_head(out, o_ref, (1, 3)) if out.ndim == 4 else e_o
+    c_o = worst_per_chunk(out, o_ref) if out.ndim == 4 else e_o
+    h_s = worst_per_head(sf, s_ref, (2, 3)) if (s_ref is not None and sf.ndim == 4) else e_s
+    WORST[name] = (h_o, c_o, h_s)
+    note(f"  {name}: out rel err {e_o:.3e} (worst head {h_o:.3e}, worst 64-token chunk {c_o:.3e}), "
+         f"S_final rel err {e_s:.3e} (worst head {h_s:.3e}) (bar {tol:g})")
     assert e_o < tol, f"{name}: output error {e_o}"
     assert e_s < tol, f"{name}: state error {e_s}"
+    assert h_o < tol, f"{name}: output error {h_o} in one (sequence, head)"
+    assert c_o < tol, f"{name}: output error {c_o} in one 64-token chunk of one (sequence, head)"
+    assert h_s < tol, f"{name}: state error {h_s} in one (sequence, head)"
 
 
 # ---------------------------------------------------------------- small full-oracle cases
@@ -242,6 +282,155 @@ def test_chunk_some_operand_waves_on_block_references(dev, dtype, dk, C):
     out, sf = gpu_chunk(p, C)
     o_ref, s_ref = oracle_dense(p)
     assert_close(f"partial block references {dtype}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+
+
+# ---------------------------------------------------------------- strong and complete forgetting
+# The per-channel gate lets a key channel be kept while another is cleared
+# ("KDA derivation summary", sect. 5; alpha in (0, 1] with no lower bound in
+# "Kimi K3 notes 1: KDA", sect. 4).  These cases decay some channels by far
+# more than the fp32 range inside one 16-token block: runs at log_alpha = -30
+# and -40 per token, and hard clears at -1e4 (alpha = 0 in fp32 and in float64).
+DEEP = [("bf16", 128, 128, 64), ("bf16", 64, 64, 32), ("bf16", 32, 64, 16), ("bf16", 16, 32, 64),
+        ("f32", 64, 64, 64), ("f32", 128, 64, 32), ("f32", 32, 32, 16)]
+
+
+def deep_gates(la, kind):
+    """Deep decay written into log_alpha [B, T, H, dk] in place."""
+    B, T, H, dk = la.shape
+    if kind == "run30":      # a quarter of the channels of head 0, then every channel of the last head
+        la[:, 40:100, 0, : max(dk // 4, 4)] = -30.0
+        la[:, 150:170, H - 1] = -30.0
+    elif kind == "clear":    # a quarter of the channels cleared every 37 tokens, one token clears everything
+        la[:, ::37, :, ::4] = -1e4
+        la[:, 101, :, :] = -1e4
+    elif kind == "all40":    # every channel at -40 for a long run (every block too deep to factor)
+        la[:, 60:200] = -40.0
+    else:
+        raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["run30", "clear", "all40"])
+@pytest.mark.parametrize("dtype,dk,dv,C", DEEP)
+def test_chunk_deep_decay(dev, dtype, dk, dv, C, kind):
+    B, T, H = 2, 260, 2
+    note(f"case deep decay {kind}: B{B} T{T} H{H} dk{dk} dv{dv} {dtype} C{C}")
+    p = kda_synth.prefill(B, T, H, dk, dv, dtype=dtype, s0_sigma=0.1, seed=131, device=dev)
+    deep_gates(p.log_alpha, kind)
+    out, sf = gpu_chunk(p, C)
+    o_ref, s_ref = oracle_dense(p)
+    assert_close(f"deep {kind} {dtype} dk{dk} C{C}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+
+
+@pytest.mark.parametrize("bv", ["16", "32"])
+def test_chunk_deep_decay_narrow_value_blocks(dev, bv, monkeypatch):
+    """One or two state waves: the hard-block corrections of a chunk are shared
+    by fewer waves (one wave takes every block at BV = 16)."""
+    monkeypatch.setenv("KDA_CHUNK_BV", bv)
+    for dtype, dk, C in (("bf16", 128, 64), ("f32", 64, 64)):
+        note(f"case deep decay BV={bv}: B1 T260 H2 dk{dk} dv64 {dtype} C{C}")
+        p = kda_synth.prefill(1, 260, 2, dk, 64, dtype=dtype, s0_sigma=0.1, seed=133, device=dev)
+        deep_gates(p.log_alpha, "clear")
+        deep_gates(p.log_alpha, "run30")
+        out, sf = gpu_chunk(p, C)
+        o_ref, s_ref = oracle_dense(p)
+        assert_close(f"deep BV={bv} {dtype}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+
+
+def test_segmented_and_varlen_deep_decay(dev):
+    """Deep decay through the segment maps (the augmented state), the lead
+    segment and the second pass, and through packed sequences."""
+    for dtype, dk, C in (("bf16", 128, 64), ("f32", 64, 32)):
+        for nseg in (3, 5):
+            note(f"case segmented deep decay: B1 T600 H2 dk{dk} {dtype} C{C}, {nseg} segments")
+            p = kda_synth.prefill(1, 600, 2, dk, 64, dtype=dtype, s0_sigma=0.1, seed=135, device=dev)
+            deep_gates(p.log_alpha, "clear")
+            p.log_alpha[:, 300:420, 1, : dk // 4] = -30.0
+            out, sf = gpu_chunk(p, C, segments=nseg)
+            o_ref, s_ref = oracle_dense(p)
+            assert_close(f"segmented deep {dtype} nseg={nseg}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+        lengths = [130, 0, 77, 300]
+        note(f"case varlen deep decay: lengths {lengths} H2 dk{dk} {dtype} C{C}")
+        p = kda_synth.prefill_varlen(lengths, 2, dk, 64, dtype=dtype, s0_sigma=0.1, seed=137, device=dev)
+        deep_gates(p.log_alpha, "clear")
+        deep_gates(p.log_alpha, "all40")
+        for segments in (1, 3):
+            out, sf = kda.chunk_fwd_varlen(p.q, p.k, p.v, p.log_alpha, p.beta, p.cu_seqlens, S0=p.S0, C=C,
+                                           segments=segments)
+            torch.cuda.synchronize()
+            o_ref, s_ref = oracle.forward_varlen(f64(p.q), f64(p.k), f64(p.v), f64(p.log_alpha), f64(p.beta),
+                                                 np.array(p.cu_host), S0=f64(p.S0))
+            assert_close(f"varlen deep {dtype} segments={segments}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+
+
+@pytest.mark.parametrize("gate,write", [("channel", "add"), ("scalar", "delta")])
+def test_chunk_variants_deep_decay(dev, gate, write):
+    """The additive write (GLA: only P needs the correction) and the scalar gate
+    (every channel of a token clears together)."""
+    for dtype, C in (("bf16", 64), ("f32", 32)):
+        note(f"case variant deep decay gate={gate} write={write} B2 T260 H2 d64 {dtype} C{C}")
+        p = kda_synth.prefill(2, 260, 2, 64, 64, dtype=dtype, s0_sigma=0.1, seed=139, device=dev)
+        deep_gates(p.log_alpha, "clear")
+        deep_gates(p.log_alpha, "run30")
+        if gate == "scalar":
+            p.log_alpha[..., 1:] = p.log_alpha[..., :1]
+        la, la_full = variant_inputs(p, gate)
+        o_ref, s_ref = oracle_variant(p, la_full, write)
+        for segments in (1, 3):
+            out, sf = kda.chunk_fwd(p.q, p.k, p.v, la, p.beta, S0=p.S0, C=C, segments=segments, gate=gate,
+                                    write=write)
+            torch.cuda.synchronize()
+            assert_close(f"deep {gate}/{write} {dtype} segments={segments}", f64(out), f64(sf), o_ref, s_ref,
+                         TOL[dtype])
+
+
+def test_chunk_raw_inputs_deep_gates(dev):
+    """Raw gate pre-activations g = 40 (log_alpha = -40) and g = 1e4 (a clear):
+    the softplus inside the kernel, then the deep-decay path."""
+    for dtype, dk, C in (("bf16", 128, 64), ("f32", 64, 32)):
+        B, T, H, dv = 2, 260, 2, 64
+        p = kda_synth.prefill_raw(B, T, H, dk, dv, dtype=dtype, s0_sigma=0.1, seed=141, device=dev)
+        p.log_alpha[:, 40:120, :, : dk // 4] = 40.0
+        p.log_alpha[:, 150:160, 1] = 40.0
+        p.log_alpha[:, ::29, :, 1::4] = 1e4
+        for gate in ("channel", "scalar"):
+            note(f"case raw deep gates {gate}: B{B} T{T} H{H} dk{dk} {dtype} C{C}")
+            o_ref, s_ref = oracle_raw(p, gate)
+            for segments in (1, 3):
+                out, sf = kda.chunk_fwd(p.q, p.k, p.v, raw_gate_arg(p, gate), p.beta, S0=p.S0, C=C,
+                                        segments=segments, gate=gate, raw=True)
+                torch.cuda.synchronize()
+                assert_close(f"raw deep {gate} {dtype} segments={segments}", f64(out), f64(sf), o_ref, s_ref,
+                             TOL[dtype])
+
+
+def test_decode_equals_chunk_prefill_deep_decay(dev):
+    """The two schedules of the one recurrence on a stream with deep decay and
+    hard clears: decode steps, the multi-token decode and one chunk prefill
+    agree with each other and with the oracle."""
+    N, H, dk, dv, steps = 8, 4, 128, 128, 150
+    note(f"case decode vs chunk prefill, deep decay: N{N} H{H} d128 bf16, {steps} tokens")
+    d = kda_synth.decode(N, H, dk, dv, steps, seed=143, device=dev, step_block=50)
+    tm = lambda t: t.transpose(0, 1).contiguous()
+    la = tm(d.log_alpha)                   # [N, T, H, dk]
+    deep_gates(la, "clear")
+    la[:, 60:90, 0] = -30.0
+    la[:, 100:140, 2, :32] = -40.0
+    d.log_alpha.copy_(la.transpose(0, 1))
+    S = d.S0.clone()
+    outs = [kda.recurrent_step(d.q[t], d.k[t], d.v[t], d.log_alpha[t], d.beta[t], S) for t in range(steps)]
+    dec = torch.stack(outs, dim=1)
+    S_multi = d.S0.clone()
+    multi = kda.recurrent_fwd(tm(d.q), tm(d.k), tm(d.v), la, tm(d.beta), S_multi)
+    pre, sf = kda.chunk_fwd(tm(d.q), tm(d.k), tm(d.v), la, tm(d.beta), S0=d.S0, C=64, segments=1)
+    torch.cuda.synchronize()
+    assert torch.equal(multi, dec) and torch.equal(S_multi, S), "multi-token decode differs from single steps"
+    e_o, e_s = rel(f64(dec), f64(pre)), rel(f64(S), f64(sf))
+    note(f"  decode vs prefill: out rel diff {e_o:.3e}, state rel diff {e_s:.3e}")
+    assert e_o < TOL["bf16"] and e_s < TOL["bf16"]
+    o_ref, s_ref = oracle.forward(f64(tm(d.q)), f64(tm(d.k)), f64(tm(d.v)), f64(la), f64(tm(d.beta)),
+                                  S0=f64(d.S0))
+    assert_close("decode deep", f64(dec), f64(S), o_ref, s_ref, TOL["bf16"])
+    assert_close("prefill deep", f64(pre), f64(sf), o_ref, s_ref, TOL["bf16"])
 
 
 def test_chunk_guard_bands_untouched(dev):
