@@ -309,11 +309,51 @@ def kda_version() -> int:
 # --- convenience wrappers: sizes from shapes, outputs allocated with torch ---------------------
 def _mode(q):
     import torch
+    if not isinstance(q, torch.Tensor):
+        raise TypeError(f"q must be a torch.Tensor, got {type(q).__name__}")
     if q.dtype == torch.bfloat16:
         return False
     if q.dtype == torch.float32:
         return True
     raise TypeError(f"q, k, v must be bfloat16 or float32, got {q.dtype}")
+
+
+def _validate(q, named, shapes, dtypes):
+    """Checks the convenience wrappers make before any C call (the C ABI sees
+    only pointers): every tensor is a torch tensor of the expected shape and
+    dtype, contiguous (the kernels assume the dense token-major layout), and on
+    the same GPU as q.  Raises TypeError or ValueError; does no arithmetic."""
+    import torch
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+        if name in dtypes and t.dtype != dtypes[name]:
+            raise TypeError(f"{name} must be {dtypes[name]}, got {t.dtype}")
+        if name in shapes and tuple(t.shape) != tuple(shapes[name]):
+            raise ValueError(f"{name} must have shape {tuple(shapes[name])}, got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (got strides {t.stride()}); call .contiguous() first")
+    for name, t in named.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise TypeError(f"{name} must be on a GPU (device 'cuda'), got {t.device}")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}: all tensors must be on one GPU")
+
+
+def _gate_spec(gate, raw, q, lead_shape, dk):
+    """Expected shape and dtype of the gate argument: fp32 log_alpha, or with
+    raw=True the pre-activations g in q's dtype; [.., dk] per channel, [..]
+    scalar, None for gate="none"."""
+    import torch
+    if gate not in GATES:
+        raise ValueError(f"gate must be one of {sorted(GATES)}, got {gate!r}")
+    dtype = q.dtype if raw else torch.float32
+    shape = tuple(lead_shape) + ((dk,) if gate == "channel" else ())
+    return shape, dtype
 
 
 def _workspace(nseq, H, dk, dv, nseg, device):
@@ -334,8 +374,18 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, C=64, output_final_state=True, 
     """
     import torch
     f32 = _mode(q)
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError(f"q and v must be [B, T, H, d], got {tuple(q.shape)} and {tuple(v.shape)}")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
+    if write not in WRITES:
+        raise ValueError(f"write must be one of {sorted(WRITES)}, got {write!r}")
+    g_shape, g_dtype = _gate_spec(gate, raw, q, (B, T, H), dk)
+    if gate != "none" and log_alpha is None:
+        raise ValueError(f"log_alpha is required with gate={gate!r}")
+    _validate(q, dict(q=q, k=k, v=v, log_alpha=log_alpha if gate != "none" else None, beta=beta, S0=S0),
+              dict(k=(B, T, H, dk), v=(B, T, H, dv), log_alpha=g_shape, beta=(B, T, H), S0=(B, H, dv, dk)),
+              dict(k=q.dtype, v=q.dtype, log_alpha=g_dtype, beta=torch.float32, S0=torch.float32))
     out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     sf = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device) if output_final_state else None
     nseg = kda_chunk_auto_segments(B, T, H, dk, dv, C, f32) if segments == "auto" else int(segments)
@@ -362,9 +412,18 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, C=64, output
     """
     import torch
     f32 = _mode(q)
+    if q.dim() != 4 or q.shape[0] != 1 or v.dim() != 4:
+        raise ValueError(f"q and v must be packed [1, T_total, H, d], got {tuple(q.shape)} and {tuple(v.shape)}")
     _, T_total, H, dk = q.shape
     dv = v.shape[-1]
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1:
+        raise ValueError("cu_seqlens must be a 1-d int32 tensor of N + 1 offsets")
     N = cu_seqlens.shape[0] - 1
+    _validate(q, dict(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, S0=S0, cu_seqlens=cu_seqlens),
+              dict(k=(1, T_total, H, dk), v=(1, T_total, H, dv), log_alpha=(1, T_total, H, dk), beta=(1, T_total, H),
+                   S0=(N, H, dv, dk)),
+              dict(k=q.dtype, v=q.dtype, log_alpha=torch.float32, beta=torch.float32, S0=torch.float32,
+                   cu_seqlens=torch.int32))
     out = torch.empty((1, T_total, H, dv), dtype=q.dtype, device=q.device)
     sf = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device) if output_final_state else None
     nseg = int(segments)
@@ -382,8 +441,16 @@ def recurrent_step(q, k, v, log_alpha, beta, S, out=None, stream=None):
     """One decode step on [N, H, d] tensors; S [N, H, dv, dk] fp32 is updated in place."""
     import torch
     f32 = _mode(q)
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError(f"q and v must be [N, H, d], got {tuple(q.shape)} and {tuple(v.shape)}")
     N, H, dk = q.shape
     dv = v.shape[-1]
+    _validate(q, dict(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, S=S, out=out),
+              dict(k=(N, H, dk), v=(N, H, dv), log_alpha=(N, H, dk), beta=(N, H), S=(N, H, dv, dk), out=(N, H, dv)),
+              dict(k=q.dtype, v=q.dtype, log_alpha=torch.float32, beta=torch.float32, S=torch.float32,
+                   out=q.dtype))
+    if S is None:
+        raise ValueError("S (the state, updated in place) is required")
     if out is None:
         out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     fn = kda_recurrent_step_f32 if f32 else kda_recurrent_step
@@ -400,8 +467,21 @@ def recurrent_fwd(q, k, v, log_alpha, beta, S, out=None, stream=None, gate="chan
     tensors is faster (same result up to rounding)."""
     import torch
     f32 = _mode(q)
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError(f"q and v must be [N, T, H, d], got {tuple(q.shape)} and {tuple(v.shape)}")
     N, T, H, dk = q.shape
     dv = v.shape[-1]
+    if write not in WRITES:
+        raise ValueError(f"write must be one of {sorted(WRITES)}, got {write!r}")
+    g_shape, g_dtype = _gate_spec(gate, raw, q, (N, T, H), dk)
+    if gate != "none" and log_alpha is None:
+        raise ValueError(f"log_alpha is required with gate={gate!r}")
+    _validate(q, dict(q=q, k=k, v=v, log_alpha=log_alpha if gate != "none" else None, beta=beta, S=S, out=out),
+              dict(k=(N, T, H, dk), v=(N, T, H, dv), log_alpha=g_shape, beta=(N, T, H), S=(N, H, dv, dk),
+                   out=(N, T, H, dv)),
+              dict(k=q.dtype, v=q.dtype, log_alpha=g_dtype, beta=torch.float32, S=torch.float32, out=q.dtype))
+    if S is None:
+        raise ValueError("S (the state, updated in place) is required")
     if out is None:
         out = torch.empty((N, T, H, dv), dtype=q.dtype, device=q.device)
     var = variant(gate, write, raw)

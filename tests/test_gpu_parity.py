@@ -96,6 +96,31 @@ def worst_per_chunk(gpu, ref, width=64):
 WORST = {}   # name -> (per-head out, per-chunk out, per-head state): the worst cases seen
 
 
+def assert_close_device(name, out, sf, o_ref, s_ref, tol, width=64):
+    """assert_close's metrics for two device results too large to copy to the
+    host as float64 (out [B, T, H, dv] with T a multiple of width, states
+    [B, H, dv, dk]); computed in fp32 on the GPU, exact for bf16 values."""
+    def metrics(x, y, head_axes):
+        d, a = (x.float() - y.float()).abs(), y.float().abs()
+        e = (d.amax() / a.amax().clamp_min(1e-30)).item()
+        ratio = lambda num, den: torch.where(num == 0, torch.zeros_like(num), num / den.clamp_min(1e-30))
+        h = ratio(d.amax(dim=head_axes), a.amax(dim=head_axes)).amax().item()
+        return d, a, e, h
+    assert torch.isfinite(out).all() and torch.isfinite(sf).all()
+    d, a, e_o, h_o = metrics(out, o_ref, (1, 3))
+    B, T, H, V = out.shape
+    dc, ac = d.view(B, T // width, width, H, V).amax(dim=(2, 4)), a.view(B, T // width, width, H, V).amax(dim=(2, 4))
+    c_o = torch.where(dc == 0, torch.zeros_like(dc), dc / ac.clamp_min(1e-30)).amax().item()
+    del d, a, dc, ac
+    _, _, e_s, h_s = metrics(sf, s_ref, (2, 3))
+    WORST[name] = (h_o, c_o, h_s)
+    note(f"  {name}: out rel err {e_o:.3e} (worst head {h_o:.3e}, worst {width}-token chunk {c_o:.3e}), "
+         f"S_final rel err {e_s:.3e} (worst head {h_s:.3e}) (bar {tol:g})")
+    for what, v in (("output", e_o), ("state", e_s), ("output of one (sequence, head)", h_o),
+                    ("output of one chunk", c_o), ("state of one (sequence, head)", h_s)):
+        assert v < tol, f"{name}: {what} error {v}"
+
+
 def assert_close(name, out, sf, o_ref, s_ref, tol):
     """Normwise relative error of the whole output and final state, and also the
     worst (sequence, head) slice and the worst 64-token window of each
@@ -969,25 +994,43 @@ def test_decode_config_sweep(dev, dtype, dk, dv, T, N):
 
 
 def test_decode_workload_sampled(dev):
+    """The decode workload at full size (256 sequences x 32 heads, d = 128, 1024
+    one-token steps): 16 sampled heads against the oracle at every step, and
+    the whole stream against the other schedule of the same recurrence, one
+    chunk prefill (C = 64, as the mid prefill) of the 1024 tokens laid out
+    [N, T, H, d] from the same initial states: every output and every final
+    state, plus the prefill's sampled heads against the oracle."""
     w = kda_synth.WORKLOADS["decode"]
+    N, H, dk, dv, steps = w["N"], w["H"], w["dk"], w["dv"], w["steps"]
     note("case decode workload: 256 seq x H32 d128 bf16, 1024 steps (16 sampled heads, every step)")
-    d = kda_synth.decode(w["N"], w["H"], w["dk"], w["dv"], w["steps"], device=dev)
+    d = kda_synth.decode(N, H, dk, dv, steps, device=dev)
     S = d.S0.clone()
     heads = [(n, h) for n, h in zip(range(3, 256, 16), range(0, 32, 2))]
-    out_s = torch.empty((len(heads), w["steps"], w["dv"]), dtype=torch.bfloat16, device=dev)
-    out = torch.empty((w["N"], w["H"], w["dv"]), dtype=torch.bfloat16, device=dev)
+    out_all = torch.empty((steps, N, H, dv), dtype=torch.bfloat16, device=dev)
     ni = torch.tensor([n for n, _ in heads], device=dev)
     hi = torch.tensor([h for _, h in heads], device=dev)
-    for t in range(w["steps"]):
-        kda.recurrent_step(d.q[t], d.k[t], d.v[t], d.log_alpha[t], d.beta[t], S, out=out)
-        out_s[:, t] = out[ni, hi]
+    for t in range(steps):
+        kda.recurrent_step(d.q[t], d.k[t], d.v[t], d.log_alpha[t], d.beta[t], S, out=out_all[t])
     torch.cuda.synchronize()
     assert torch.isfinite(S).all()
+    out_s = out_all[:, ni, hi].transpose(0, 1)                         # [n, steps, dv]
     pick = lambda t: t[:, ni, hi].transpose(0, 1).unsqueeze(2)      # [n, steps, 1, d]
     o_ref, s_ref = oracle.forward(f64(pick(d.q)), f64(pick(d.k)), f64(pick(d.v)), f64(pick(d.log_alpha)),
                                   f64(d.beta[:, ni, hi].transpose(0, 1).unsqueeze(2)),
                                   S0=f64(d.S0[ni, hi].unsqueeze(1)))
-    assert_close("decode sampled", f64(out_s)[:, :, None], f64(S[ni, hi]).reshape(len(heads), 1, w["dv"], w["dk"]),
+    s_ref = s_ref.reshape(len(heads), 1, dv, dk)
+    assert_close("decode sampled", f64(out_s)[:, :, None], f64(S[ni, hi]).reshape(len(heads), 1, dv, dk),
+                 o_ref, s_ref, TOL["bf16"])
+
+    note("case decode workload vs chunk prefill of the same stream: N256 T1024 H32 d128 bf16 C64")
+    tm = lambda t: t.transpose(0, 1).contiguous()                   # [steps, N, ...] -> [N, steps, ...]
+    pre, sf = kda.chunk_fwd(tm(d.q), tm(d.k), tm(d.v), tm(d.log_alpha), tm(d.beta), S0=d.S0, C=64, segments=1)
+    torch.cuda.synchronize()
+    dec = tm(out_all)                                                 # [N, steps, H, dv]
+    del d
+    # the whole stream: both schedules, every output and state
+    assert_close_device("decode vs prefill (all heads)", pre, sf, dec, S, TOL["bf16"])
+    assert_close("prefill sampled", f64(pre[ni, :, hi])[:, :, None], f64(sf[ni, hi]).reshape(len(heads), 1, dv, dk),
                  o_ref, s_ref, TOL["bf16"])
 
 
