@@ -45,8 +45,11 @@
  * call has no side effect.  kda_last_error() gives a message for the calling
  * thread's last failed call.
  *
- * SUPPORTED SHAPES.  dk, dv in {16, 32, 64, 128}; C in {16, 32, 64} (bf16
- * entry points), C in {16, 32} plus C = 64 for dk <= 64 (fp32 entry points).
+ * SUPPORTED SHAPES.  dk, dv in {16, 32, 64, 128}; C in {16, 32, 64}.  C is the
+ * chunk length of the schedule and does not change the result beyond
+ * rounding; the fp32 entry points at dk = 128 run C = 64 as 32-token chunks
+ * (64-token fp32 operands of 128 channels do not fit a workgroup's 160 KiB of
+ * LDS).
  * B, T, H, N >= 0 (a batch with no tokens only writes S_final).  Pointers to
  * q, k, v, out, log_alpha, S0, S_final and S must be 16-byte aligned; beta
  * 4-byte aligned.

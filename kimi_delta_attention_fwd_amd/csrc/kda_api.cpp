@@ -98,6 +98,18 @@ int choose_bv(bool f32, int dk, int dv, int C, int maxbv = 64)
 
 constexpr int kMaxSegments = 1024;
 
+// Chunk length the kernels run for a requested C: C itself, or the largest
+// shorter one whose kernel fits the LDS (fp32 operands at dk = 128: 64-token
+// chunks would need about 280 KB, 173 KB even single-buffered, so those
+// requests run as 32-token chunks).  The chunk length is a schedule choice:
+// both give the recurrence's result, up to rounding.
+int run_chunk_len(bool f32, int dk, int C)
+{
+    for (int c = C; c >= 16; c /= 2)
+        if (kda::chunk_fits(f32, dk, 16, c)) return c;
+    return 0;
+}
+
 // Variant selector of the *_ex entry points: bits 0-1 the gate (0 per
 // channel, 1 one value per token and head, 2 none), bit 2 the additive write,
 // bit 3 raw inputs (q, k normalised in the kernel, gate pre-activations).
@@ -201,12 +213,14 @@ int seg_lead(long nheads, int dk, int dv, int bv, int nseg, int cus)
 int auto_segments(bool f32, int B, int T, int H, int dk, int dv, int C)
 {
     if (B <= 0 || T <= 0 || H <= 0 || !supported_d(dk) || !supported_d(dv) || !supported_c(C)) return 1;
+    const int Cr = run_chunk_len(f32, dk, C);
+    if (Cr == 0) return 1;
     const int cus = device_cus();
-    const long nch = (T + C - 1) / C, nheads = (long)B * H;
+    const long nch = (T + Cr - 1) / Cr, nheads = (long)B * H;
     double best = 0.0;
     int best_s = 1;
     for (int s = 1; s <= 64 && s <= nch; ++s) {
-        const int bv = choose_bv(f32, dk, dv, C, s > 1 ? dk : 64);
+        const int bv = choose_bv(f32, dk, dv, Cr, s > 1 ? dk : 64);
         if (bv == 0) continue;
         const long nvA = dv / bv, nvB = (dv + dk) / bv;
         double cost;
@@ -314,7 +328,8 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
                 return fail(KDA_ERR_ALIASING, "workspace overlaps %s", b.name);
     }
 
-    const int BV = choose_bv(f32, dk, dv, C, nseg > 1 ? dk : 64);
+    const int Crun = run_chunk_len(f32, dk, C);
+    const int BV = Crun > 0 ? choose_bv(f32, dk, dv, Crun, nseg > 1 ? dk : 64) : 0;
     if (BV == 0)
         return fail(KDA_ERR_UNSUPPORTED, "no %s kernel fits LDS for dk=%d, dv=%d, C=%d",
                     f32 ? "fp32" : "bf16", dk, dv, C);
@@ -341,7 +356,7 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
     a.H = H;
     a.dk = dk;
     a.dv = dv;
-    a.C = C;
+    a.C = Crun;
     a.BV = BV;
     a.nsegs = nseg;
     a.gate = gate;

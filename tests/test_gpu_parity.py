@@ -232,18 +232,35 @@ SWEEP = [(dtype, dk, dv, C, H) for dtype in ("bf16", "f32")
 def test_chunk_config_sweep(dev, dtype, dk, dv, C, H):
     """The single-pass kernel over input type x (dk, dv) x C x head count on a
     ragged T = 130 (8 heads group a head's value blocks on one XCD, 2 do
-    not); the one combination that does not fit the LDS is rejected up front."""
+    not).  fp32 at dk = 128 with C = 64 runs as 32-token chunks (its 64-token
+    operands do not fit the LDS); it is held to the same bar."""
     note(f"case sweep {dtype} dk{dk} dv{dv} C{C} H{H} T130")
     p = kda_synth.prefill(1, 130, H, dk, dv, dtype=dtype, s0_sigma=0.1, seed=5, device=dev)
-    if dtype == "f32" and dk == 128 and C == 64:
-        with pytest.raises(kda.KdaError) as err:
-            kda.chunk_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S0=p.S0, C=C, segments=1)
-        assert err.value.status == 3
-        return
     out, sf = kda.chunk_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S0=p.S0, C=C, segments=1)
     torch.cuda.synchronize()
     o_ref, s_ref = oracle_dense(p)
     assert_close(f"sweep {dtype} dk{dk} dv{dv} C{C} H{H}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+
+
+def test_chunk_fp32_dk128_c64_all_schedules(dev):
+    """fp32 inputs at dk = 128 with C = 64 (run as 32-token chunks) through the
+    single pass, the segmented schedule and packed sequences, against the
+    oracle at the fp32 bar, and bit for bit against an explicit C = 32 call."""
+    note("case fp32 dk128 C64: B2 T300 H2 dk128 dv128, single pass / 3 segments / varlen")
+    p = kda_synth.prefill(2, 300, 2, 128, 128, dtype="f32", s0_sigma=0.1, seed=6, device=dev)
+    o_ref, s_ref = oracle_dense(p)
+    for segments in (1, 3):
+        out, sf = gpu_chunk(p, 64, segments=segments)
+        assert_close(f"fp32 dk128 C64 segments={segments}", f64(out), f64(sf), o_ref, s_ref, TOL["f32"])
+        o32, s32 = gpu_chunk(p, 32, segments=segments)
+        assert torch.equal(out, o32) and torch.equal(sf, s32)
+    lengths = [130, 0, 77, 200]
+    pv = kda_synth.prefill_varlen(lengths, 2, 128, 64, dtype="f32", s0_sigma=0.1, seed=7, device=dev)
+    out, sf = kda.chunk_fwd_varlen(pv.q, pv.k, pv.v, pv.log_alpha, pv.beta, pv.cu_seqlens, S0=pv.S0, C=64)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.forward_varlen(f64(pv.q), f64(pv.k), f64(pv.v), f64(pv.log_alpha), f64(pv.beta),
+                                         np.array(pv.cu_host), S0=f64(pv.S0))
+    assert_close("fp32 dk128 C64 varlen", f64(out), f64(sf), o_ref, s_ref, TOL["f32"])
 
 
 def test_chunk_decay_at_precondition_edge(dev):
