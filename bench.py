@@ -410,8 +410,15 @@ def host_cpu_model() -> str:
 def cpu_baseline(p, kda_synth, target_s=10.0, max_passes=8):
     """Float64 oracle on the whole mid workload (every sequence, head and token),
     repeated until about `target_s` seconds of CPU work have been timed."""
+    import tempfile
     import oracle
     B, T, H, _ = p.q.shape
+    build = "generic x86-64, -O2"
+    try:   # compiled for this host's CPU, as a CPU implementation would be deployed
+        oracle.use_library(oracle.build_native(tempfile.mkdtemp(prefix="kda_oracle_")))
+        build = "-O3 -march=native on this host"
+    except Exception as e:   # no compiler: the generic build of the same source
+        print(f"note: native oracle build failed ({e}); timing the generic build", file=sys.stderr)
     args = [kda_synth.to_f64(x) for x in (p.q, p.k, p.v, p.log_alpha, p.beta)]
     threads = min(oracle.max_threads(), B * H)   # the oracle's OpenMP loop runs over (sequence, head)
     passes, dt = 0, 0.0
@@ -425,7 +432,7 @@ def cpu_baseline(p, kda_synth, target_s=10.0, max_passes=8):
                 host_cpu=host_cpu_model(), host_threads=os.cpu_count(),
                 sample=f"the whole mid workload (B={B}, T={T}, H={H}, dk=dv=128, zero initial state) "
                        f"through the float64 token-by-token recurrence, {passes} pass(es) in {dt:.1f} s, "
-                       f"OpenMP over the {B * H} (sequence, head) pairs")
+                       f"OpenMP over the {B * H} (sequence, head) pairs; oracle built {build}")
 
 
 def main():

@@ -34,7 +34,9 @@ __all__ = [
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_PKG, "libkda.so")
+# KDA_LIBRARY names another build of the library to load (for instance one
+# whose host code carries the address and undefined-behaviour sanitizers).
+_LIB_PATH = os.environ.get("KDA_LIBRARY") or os.path.join(_PKG, "libkda.so")
 _lib = None
 
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL_POINTER", 2: "KDA_ERR_BAD_SHAPE", 3: "KDA_ERR_UNSUPPORTED",

@@ -26,6 +26,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
 _LIB = os.path.join(_HERE, "libkda_oracle.so")
+# KDA_ORACLE_LIBRARY names a prebuilt copy to load instead (for instance one
+# built with the address and undefined-behaviour sanitizers); it is not rebuilt.
+_LIB_OVERRIDE = os.environ.get("KDA_ORACLE_LIBRARY")
 
 WRITE_DELTA = 0
 WRITE_ADD = 1
@@ -66,9 +69,30 @@ def _bind(lib):
 def _load():
     global _lib
     if _lib is None:
-        build()
-        _lib = _bind(ctypes.CDLL(_LIB))
+        if _LIB_OVERRIDE:
+            _lib = _bind(ctypes.CDLL(_LIB_OVERRIDE))
+        else:
+            build()
+            _lib = _bind(ctypes.CDLL(_LIB))
     return _lib
+
+
+def build_native(out_dir: str) -> str:
+    """Compile kda_oracle.c for the CPU it runs on (-O3 -march=native, OpenMP)
+    into out_dir and return the library's path.  Used for the timed CPU
+    baseline on the host that runs the GPU; the same source as build()."""
+    os.makedirs(out_dir, exist_ok=True)
+    path = os.path.join(out_dir, "libkda_oracle_native.so")
+    cmd = ["gcc", "-O3", "-march=native", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-Wall", "-Wextra", "-o", path, _SRC, "-lm"]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return path
+
+
+def use_library(path: str) -> None:
+    """Load the oracle from another build of kda_oracle.c (build_native)."""
+    global _lib
+    _lib = _bind(ctypes.CDLL(path))
 
 
 def _f64(a):
