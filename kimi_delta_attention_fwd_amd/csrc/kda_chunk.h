@@ -1317,7 +1317,12 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 #pragma unroll
                         for (int J = 0; J < b; ++J) {
                             const f32x4 a = *(const f32x4 *)(sA + tile_index(NB, b, J) * 16 * PT + n * PT + 4 * g);
-                            y = mma_fp32a<In>(y, a, Eb[J]);
+                            if constexpr (K::F32) {
+                                y = mma_fp32a<In>(y, a, Eb[J]);
+                            } else {   // bf16 A (no lo part)
+                                const V4 aa[1] = {to_op<In>(a)}, bb[1] = {Eb[J]};
+                                y = mma_tiles<16, In, 1>(y, aa, bb);
+                            }
                         }
                         const f32x4 d = *(const f32x4 *)(sA + b * 16 * PT + n * PT + 4 * g);
                         const f32x4 e = mma_fp32ab<In>(d, R[b] - y);
