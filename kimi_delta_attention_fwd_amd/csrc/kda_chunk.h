@@ -332,7 +332,10 @@ __device__ __forceinline__ void diag_inverse_bf16(float *At, int PT, int n, int 
     const f32x4 M1t = id - U1 + U2 - U3;              // ((I - L)(I + L^2))^T
     const f32x4 M2t = M1t + mm(L4, M1t);              // ... (I + L^4)
     const f32x4 Dt = M2t + mm(L8, M2t);               // ... (I + L^8)
-    *(f32x4 *)(At + n * PT + 4 * g) = Dt;
+    // stored pre-split for the bf16 solve: hi then lo bf16 parts in the lane's 16 bytes
+    const bf16x4 hi = to_op<bf16>(Dt), lo = to_op<bf16>(Dt - to_f32<bf16>(hi));
+    const f32x2 h2 = __builtin_bit_cast(f32x2, hi), l2 = __builtin_bit_cast(f32x2, lo);
+    *(f32x4 *)(At + n * PT + 4 * g) = f32x4{h2[0], h2[1], l2[0], l2[1]};
 }
 
 // fp32 kernels: column n of D by forward substitution over the rows of the
@@ -1325,7 +1328,16 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                             }
                         }
                         const f32x4 d = *(const f32x4 *)(sA + b * 16 * PT + n * PT + 4 * g);
-                        const f32x4 e = mma_fp32ab<In>(d, R[b] - y);
+                        f32x4 e;
+                        if constexpr (K::F32) {
+                            e = mma_fp32ab<In>(d, R[b] - y);
+                        } else {   // D stored pre-split: hi then lo bf16 parts in the tile's 16 bytes
+                            const V4 dh = __builtin_bit_cast(V4, f32x2{d[0], d[1]}), dl = __builtin_bit_cast(V4, f32x2{d[2], d[3]});
+                            const f32x4 x = R[b] - y;
+                            const V4 xh = to_op<In>(x), xl = to_op<In>(x - to_f32<In>(xh));
+                            const V4 a3[3] = {dh, dh, dl}, x3[3] = {xh, xl, xh};
+                            e = mma_tiles<16, In, 3>(zero4(), a3, x3);
+                        }
                         Eb[b] = to_op<In>(e);
                     }
                 }
