@@ -678,11 +678,12 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     // diagonal).  Tiles are computed transposed, d[i] = X[16I + n][16J + 4g + i],
     // so each lane stores four consecutive columns of one row.
     auto tile_job = [&](long ch, int p, bool doA, bool doP, f32x4 *lt = nullptr) __attribute__((always_inline)) {
+        // (I, J) of tile p without a loop: off-diagonal tile o = p - NB has row
+        // block I = the o-th entry of 1, 2, 2, 3, 3, 3 (four bits each)
         int I = p, J = p;
         if (p >= NB) {
             const int o = p - NB;
-            I = 1;
-            while ((I + 1) * I / 2 <= o) ++I;
+            I = (int)((0x333221u >> (4 * o)) & 15u);
             J = o - I * (I - 1) / 2;
         }
         const float *scc = bufSc(ch);
@@ -1165,6 +1166,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     } else {
         // =============== state waves: value rows 16 cb .. 16 cb + 15 of the block
         const int cb = wave;
+        __builtin_assume(cb >= 0 && cb < K::NBV);
         const int row = vb * BV + 16 * cb + n;     // this lane's state row (of the augmented state in MAP mode)
         const bool vreal = !map || vb * BV < dv;   // real value rows (virtual ones see v = 0)
         // bf16: lane (n, g) loads row 16 (2 u + g/2) + n, columns 8 (g&1) .. +7;
