@@ -407,7 +407,7 @@ def host_cpu_model() -> str:
     return ""
 
 
-def cpu_baseline(p, kda_synth, target_s=10.0, max_passes=8):
+def cpu_baseline(p, kda_synth, target_s=10.0, max_passes=24):
     """Float64 oracle on the whole mid workload (every sequence, head and token),
     repeated until about `target_s` seconds of CPU work have been timed."""
     import tempfile
