@@ -241,7 +241,7 @@ __device__ __forceinline__ bool all_flags(const float *fl)
     return __builtin_amdgcn_readfirstlane((int)m) != 0;
 }
 
-template <typename In, int DK, int BV, int C>
+template <typename In, int DK, int BV, int C, bool PAIRED = true>
 struct ChunkCfg {
     typedef In OpT;                                  // MFMA operand type
     static constexpr bool F32 = sizeof(In) == 4;
@@ -254,7 +254,18 @@ struct ChunkCfg {
     static constexpr int KD = F32 ? 4 : (DK % 32 == 0 ? 32 : 16);   // MFMA step of d_k contractions
     static constexpr int KC = F32 ? 4 : (C % 32 == 0 ? 32 : 16);    // MFMA step of token contractions
     static constexpr int PADE = 16 / (int)sizeof(In);
-    static constexpr int PK = DK + 4;                // rows of [token, d_k] operands
+    // Paired operand order.  A 16x16x32 product takes, in lane (n, g), the
+    // contraction indices 32s + 4g + e and 32s + 16 + 4g + e (e = 0..3) of two
+    // 16-wide tiles.  Stored at pair_pos() of their index, these eight sit side
+    // by side and the lane loads them with one 16-byte LDS read instead of two
+    // 8-byte ones.  PAIRK: the d_k axis of Kr, Qr and Kd, whose rows are then
+    // 16-byte aligned and 4 banks apart.
+    static constexpr bool PAIRK = PAIRED && KD == 32;
+    static constexpr int PK = DK + (PAIRK ? 8 : 4);  // rows of [token, d_k] operands
+    // position of index c in the paired order (4-aligned groups of four stay together)
+    static __device__ __forceinline__ int pair_pos(int c) {
+        return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3);
+    }
     static constexpr int PC = C + PADE;              // rows of Ktil^T (16-byte aligned, chunk-swizzled)
     static constexpr int SWZ = C * (int)sizeof(In) / 16 - 1;
     static constexpr int PT = 20;                    // rows of an A (fp32) or P tile
@@ -576,7 +587,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     // and the delta write (the usual projection outputs), folded in
     const int gate = VAR == 1 ? gate_arg : 0, add = VAR == 1 ? add_arg : 0;
     const int prep = VAR == 2 ? 1 : (VAR == 1 ? prep_arg : 0);
-    typedef ChunkCfg<In, DK, BV, C> K;
+    // the raw-input kernel keeps the unpaired layouts (about 1.5% slower with them)
+    typedef ChunkCfg<In, DK, BV, C, VAR != 2> K;
     typedef typename V4T<In>::type V4;
     constexpr int NB = K::NB, NDK = K::NDK, PK = K::PK, PC = K::PC, PT = K::PT, RS = K::RS;
 
@@ -673,6 +685,28 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     const int HDK = H * DK, HDV = H * dv;
     const long hrow = tok0 * H + h;                 // token rows are H*d elements apart
 
+    // Ktil^T in the paired order along the tokens (its contraction with E in
+    // the state update); not in the map pass, where it timed slower
+    constexpr bool PAIRT = !K::F32 && K::KC == 32 && VAR != 2 && !MAP;
+    // LDS column of channel c of a [token, d_k] operand
+    auto kcol = [&](int c) { return K::PAIRK ? K::pair_pos(c) : c; };
+    // Fragments of one row of a [token, d_k] operand: x[t] = channels
+    // 16 t + 4 g .. 16 t + 4 g + 3
+    auto load_krow = [&](V4 (&x)[NDK], const In *row) __attribute__((always_inline)) {
+        if constexpr (K::PAIRK) {
+            typedef In V8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+            for (int s2 = 0; s2 < NDK / 2; ++s2) {
+                const V8 w = *(const V8 *)(row + 32 * s2 + 8 * g);
+                x[2 * s2] = __builtin_shufflevector(w, w, 0, 1, 2, 3);
+                x[2 * s2 + 1] = __builtin_shufflevector(w, w, 4, 5, 6, 7);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NDK; ++t) x[t] = *(const V4 *)(row + 16 * t + 4 * g);
+        }
+    };
+
     // One lower-triangle tile pair (I, J) of chunk ch: the A tile (beta-scaled,
     // strictly lower on the diagonal) and / or the P tile (lower incl. the
     // diagonal).  Tiles are computed transposed, d[i] = X[16I + n][16J + 4g + i],
@@ -690,8 +724,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         const float *fl = scc + K::SC_FLAG;
         const bool allfast = all_flags<K::NXW>(fl);
         V4 cf[NDK];
-#pragma unroll
-        for (int t = 0; t < NDK; ++t) cf[t] = *(const V4 *)(sKd + (16 * J + n) * PK + 16 * t + 4 * g);
+        load_krow(cf, sKd + (16 * J + n) * PK);
         if (!allfast) {   // the pair's column scale: Kc_J s_IJ = k e^{rho_I - G}
             const float *wr = sW + p * DK + 4 * g;
 #pragma unroll
@@ -703,8 +736,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         if (doA) {
             const In *Kr = bufKr(ch);
             V4 rk[NDK];
-#pragma unroll
-            for (int t = 0; t < NDK; ++t) rk[t] = *(const V4 *)(Kr + (16 * I + n) * PK + 16 * t + 4 * g);
+            load_krow(rk, Kr + (16 * I + n) * PK);
             const f32x4 da = mma_tiles<K::KD, In, NDK>(zero4(), cf, rk);
             const float b = prep ? beta_hat<K>(scc, 16 * I + n) : scc[K::SC_BETA + 16 * I + n];
             f32x4 va;
@@ -730,8 +762,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         if (doP) {
             const In *Qr = bufQr(ch);
             V4 rq[NDK];
-#pragma unroll
-            for (int t = 0; t < NDK; ++t) rq[t] = *(const V4 *)(Qr + (16 * I + n) * PK + 16 * t + 4 * g);
+            load_krow(rq, Qr + (16 * I + n) * PK);
             const f32x4 dp = mma_tiles<K::KD, In, NDK>(zero4(), cf, rq);
             f32x4 vp;
 #pragma unroll
@@ -1012,8 +1043,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                     }
                     if (act) {
                         const int r = r0 + i;
-                        store4(Kr + r * PK + c0, vkr);
-                        if (!map) store4(Qr + r * PK + c0, vqr);
+                        store4(Kr + r * PK + kcol(c0), vkr);
+                        if (!map) store4(Qr + r * PK + kcol(c0), vqr);
                     }
                 }
                 if (prep) {   // per token over the channel group's lanes, stored by its first lane
@@ -1057,7 +1088,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                             vkd[j] = ktf * gli[j];                     // k e^{-G}
                             sf[j] *= al[i][j];
                         }
-                        if (act) store4(sKd + (r0 + i) * PK + c0, vkd);
+                        if (act) store4(sKd + (r0 + i) * PK + kcol(c0), vkd);
                     }
                 } else {
                     float sb[4];
@@ -1075,12 +1106,31 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                             sf[j] *= al[i][j];
                             sb[j] *= al[i][j];
                         }
-                        if (act) store4(sKd + (r0 + i) * PK + c0, vkd);
+                        if (act) store4(sKd + (r0 + i) * PK + kcol(c0), vkd);
                     }
                 }
                 if (act) {
+                    if constexpr (PAIRT) {   // tokens in the paired order: pieces of up to four
+                        constexpr int W = RS < 4 ? RS : 4;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) store_row_swz<In, RS>(Kt, c0 + j, r0, PC, K::SWZ, kt[j]);
+                        for (int j = 0; j < 4; ++j)
+#pragma unroll
+                            for (int i0 = 0; i0 < RS; i0 += W) {
+                                In *dst = Kt + Panel<In, 16>::swz_index(c0 + j, K::pair_pos(r0 + i0), PC, K::SWZ);
+                                if constexpr (W == 1) {
+                                    *dst = kt[j][i0];
+                                } else {
+                                    typedef In VW __attribute__((ext_vector_type(W)));
+                                    VW x;
+#pragma unroll
+                                    for (int i = 0; i < W; ++i) x[i] = kt[j][i0 + i];
+                                    *(VW *)dst = x;
+                                }
+                            }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) store_row_swz<In, RS>(Kt, c0 + j, r0, PC, K::SWZ, kt[j]);
+                    }
                 }
             }
             if (seg == 0) *(f32x4 *)(sc + K::SC_GL + c0) = f32x4{fexp(glast[0]), fexp(glast[1]), fexp(glast[2]), fexp(glast[3])};
@@ -1271,11 +1321,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 V4 ss[NDK];
                 auto rows = [&](int I) __attribute__((always_inline)) {
                     V4 ak[NDK], bq[NDK];
-#pragma unroll
-                    for (int ct = 0; ct < NDK; ++ct) {
-                        if (!add) ak[ct] = *(const V4 *)(Kr + (16 * I + n) * PK + 16 * ct + 4 * g);
-                        if (!map) bq[ct] = *(const V4 *)(Qr + (16 * I + n) * PK + 16 * ct + 4 * g);
-                    }
+                    if (!add) load_krow(ak, Kr + (16 * I + n) * PK);
+                    if (!map) load_krow(bq, Qr + (16 * I + n) * PK);
                     R[I] = add ? zero4() : mma_tiles<K::KD, In, NDK>(zero4(), ak, ss);    // [16I + 4g + i][n]
                     if (!map) O1[I] = mma_tiles<K::KD, In, NDK>(zero4(), ss, bq);   // [v = 4g + i][16I + n]
                 };
@@ -1363,9 +1410,19 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 for (int ct = 0; ct < NDK; ++ct) {
                     const f32x4 gl = *(const f32x4 *)(sc + K::SC_GL + 16 * ct + 4 * g);
                     V4 ka[NB];
+                    if constexpr (PAIRT) {   // tokens 16 b + 4 g .. + 3 of blocks 2 s2, 2 s2 + 1 in one read
+                        typedef In V8 __attribute__((ext_vector_type(8)));
 #pragma unroll
-                    for (int b = 0; b < NB; ++b)
-                        ka[b] = *(const V4 *)(Kt + Panel<In, 16>::swz_index(16 * ct + n, 16 * b + 4 * g, PC, K::SWZ));
+                        for (int s2 = 0; s2 < NB / 2; ++s2) {
+                            const V8 w = *(const V8 *)(Kt + Panel<In, 16>::swz_index(16 * ct + n, 32 * s2 + 8 * g, PC, K::SWZ));
+                            ka[2 * s2] = __builtin_shufflevector(w, w, 0, 1, 2, 3);
+                            ka[2 * s2 + 1] = __builtin_shufflevector(w, w, 4, 5, 6, 7);
+                        }
+                    } else {
+#pragma unroll
+                        for (int b = 0; b < NB; ++b)
+                            ka[b] = *(const V4 *)(Kt + Panel<In, 16>::swz_index(16 * ct + n, 16 * b + 4 * g, PC, K::SWZ));
+                    }
                     Sacc[ct] = mma_tiles<K::KC, In, NB>(Sacc[ct] * gl, ka, Eb);
                 }
             }
