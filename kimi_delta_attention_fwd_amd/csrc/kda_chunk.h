@@ -688,6 +688,11 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     // Ktil^T in the paired order along the tokens (its contraction with E in
     // the state update); not in the map pass, where it timed slower
     constexpr bool PAIRT = !K::F32 && K::KC == 32 && VAR != 2 && !MAP;
+    // The off-diagonal A tiles enter the bf16 solve as one bf16 part.  The
+    // raw-input kernel rounds them when it stores them (half the LDS bytes;
+    // 1.4% faster there, 1% slower on varlen in the plain kernel, which
+    // rounds them in the solve instead: the same bits either way).
+    constexpr bool ABF = !K::F32 && VAR == 2;
     // LDS column of channel c of a [token, d_k] operand
     auto kcol = [&](int c) { return K::PAIRK ? K::pair_pos(c) : c; };
     // Fragments of one row of a [token, d_k] operand: x[t] = channels
@@ -742,7 +747,11 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             f32x4 va;
 #pragma unroll
             for (int i = 0; i < 4; ++i) va[i] = (I > J || 4 * g + i < n) ? da[i] * b : 0.f;
-            *(f32x4 *)(sA + p * 16 * PT + n * PT + 4 * g) = va;
+            if (ABF && I > J) {
+                *(V4 *)(sA + p * 16 * PT + n * PT + 4 * g) = to_op<In>(va);
+            } else {
+                *(f32x4 *)(sA + p * 16 * PT + n * PT + 4 * g) = va;
+            }
             if (lt) {
                 // diagonal tile: also L itself in accumulator layout,
                 // lt[0][i] = L[4g + i][n] (and lt[1] = L^T, the tile just stored)
@@ -864,6 +873,31 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             for (int i = 0; i < RS; ++i) kr[i] = buf_load<In4>(rk, voff_in, i * rowb_in);
         };
 
+        // The plain kernel scans a chunk's log-decays ahead, at the end of the
+        // previous chunk's stage A (its loads are in by then), so the scan's
+        // lane shuffles are off the start of the stage.
+        constexpr bool PSCAN = VAR == 0;
+        float nx_inc[4], nx_gl[4];
+        auto scan_g = [&](float (&inc)[4], float (&glast)[4]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float acc = 0.f;
+#pragma unroll
+                for (int i = 0; i < RS; ++i) acc += gr[i][j];
+                inc[j] = acc;
+            }
+            // inclusive scan of the segment sums over the lanes of one channel group
+#pragma unroll
+            for (int d = 1; d < K::NSEG; d <<= 1)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float y = __shfl_up(inc[j], d * K::NCG, 64);
+                    if (seg >= d) inc[j] += y;
+                }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) glast[j] = __shfl(inc[j], (K::NSEG - 1) * K::NCG + cg, 64);   // G_last
+        };
+
         // ---- stage A: cumulative decay, references, scaled operands
         auto stage_a = [&](long ch) __attribute__((always_inline)) {
             const long t0 = ch * C;
@@ -882,29 +916,27 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                     for (int j = 0; j < 4; ++j) gr[i][j] = (gate == 2 || r0 + i >= nval) ? 0.f : neg_softplus(gv[j]);
                 }
             }
-            float tot[4], inc[4], exc[4];
+            float tot[4], inc[4], exc[4], glast[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float acc = 0.f;
 #pragma unroll
                 for (int i = 0; i < RS; ++i) acc += gr[i][j];
                 tot[j] = acc;
-                inc[j] = acc;
             }
-            // inclusive scan of the segment sums over the lanes of one channel group
-#pragma unroll
-            for (int d = 1; d < K::NSEG; d <<= 1)
+            if constexpr (PSCAN) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float y = __shfl_up(inc[j], d * K::NCG, 64);
-                    if (seg >= d) inc[j] += y;
+                    inc[j] = nx_inc[j];
+                    glast[j] = nx_gl[j];
                 }
-            float glast[4];
+            } else {
+                scan_g(inc, glast);
+            }
             bool fastc[4], lane_fast = true;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 exc[j] = inc[j] - tot[j];                                       // G before my first token
-                glast[j] = __shfl(inc[j], (K::NSEG - 1) * K::NCG + cg, 64);      // G_last
                 fastc[j] = glast[j] >= -K::FAST_NATS;
                 lane_fast = lane_fast && fastc[j];
             }
@@ -1146,6 +1178,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 sc[K::SC_HARD + xw] = __builtin_bit_cast(float, hard);
             }
             if (xw == 0 && lane < C) sc[K::SC_BETA + lane] = (lane < nval) ? betar : 0.f;
+            if (PSCAN && ch + 1 < nch) scan_g(nx_inc, nx_gl);
         };
 
         // ---- stage B: the diagonal A tiles and their block inverses (with P
@@ -1196,6 +1229,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             prefetch_g(0);
             prefetch_q(0);
             prefetch_k(0);
+            if (PSCAN) scan_g(nx_inc, nx_gl);
         }
         // Stage A sets the pace of the first segment, where each operand wave
         // shares its SIMD with a state wave that has time to spare: the operand
@@ -1368,11 +1402,11 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                         f32x4 y = zero4();
 #pragma unroll
                         for (int J = 0; J < b; ++J) {
-                            const f32x4 a = *(const f32x4 *)(sA + tile_index(NB, b, J) * 16 * PT + n * PT + 4 * g);
+                            const float *at = sA + tile_index(NB, b, J) * 16 * PT + n * PT + 4 * g;
                             if constexpr (K::F32) {
-                                y = mma_fp32a<In>(y, a, Eb[J]);
+                                y = mma_fp32a<In>(y, *(const f32x4 *)at, Eb[J]);
                             } else {   // bf16 A (no lo part)
-                                const V4 aa[1] = {to_op<In>(a)}, bb[1] = {Eb[J]};
+                                const V4 aa[1] = {ABF ? *(const V4 *)at : to_op<In>(*(const f32x4 *)at)}, bb[1] = {Eb[J]};
                                 y = mma_tiles<16, In, 1>(y, aa, bb);
                             }
                         }
