@@ -75,6 +75,8 @@
 #include "kda_device.h"
 #include "kda_launch.h"
 
+#include <type_traits>
+
 namespace kda {
 
 template <typename T> struct V4T { typedef T type __attribute__((ext_vector_type(4))); };
@@ -590,6 +592,10 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     // the raw-input kernel keeps the unpaired layouts (about 1.5% slower with them)
     typedef ChunkCfg<In, DK, BV, C, VAR != 2> K;
     typedef typename V4T<In>::type V4;
+    // Chunk indices and lengths are 32-bit (fewer scalar registers, which the
+    // kernel otherwise spills into vector lanes); the raw-input kernel timed
+    // faster with 64-bit ones
+    typedef typename std::conditional<VAR == 2, long, int>::type CI;
     constexpr int NB = K::NB, NDK = K::NDK, PK = K::PK, PC = K::PC, PT = K::PT, RS = K::RS;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[K::LDS];
@@ -597,10 +603,10 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     float *const sW = (float *)(smem + K::O_W);
     float *const sA = (float *)(smem + K::O_A);
     In *const sP = (In *)(smem + K::O_P);
-    auto bufKr = [&](long ch) { return (In *)(smem + K::O_KR + (ch & 1) * K::SZ_R); };
-    auto bufQr = [&](long ch) { return (In *)(smem + K::O_QR + (ch & 1) * K::SZ_R); };
-    auto bufKt = [&](long ch) { return (In *)(smem + K::O_KT + (ch & 1) * K::SZ_KT); };
-    auto bufSc = [&](long ch) { return (float *)(smem + K::O_SC + (ch & 1) * K::SZ_SC); };
+    auto bufKr = [&](CI ch) { return (In *)(smem + K::O_KR + (ch & 1) * K::SZ_R); };
+    auto bufQr = [&](CI ch) { return (In *)(smem + K::O_QR + (ch & 1) * K::SZ_R); };
+    auto bufKt = [&](CI ch) { return (In *)(smem + K::O_KT + (ch & 1) * K::SZ_KT); };
+    auto bufSc = [&](CI ch) { return (float *)(smem + K::O_SC + (ch & 1) * K::SZ_SC); };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) index
@@ -651,12 +657,13 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     }
     const bool map = MAP && !lead_full;              // augmented state, no outputs
     const int seq = head / H, h = head % H;
-    long tok0, len;
+    long tok0;
+    CI len;   // tokens of this unit (at most T)
     if (cu_seqlens) {   // T is the stream length here; offsets clamped to [0, T] keep every access inside it
         const long a0 = min(max((long)cu_seqlens[seq], 0L), (long)T);
         const long a1 = min(max((long)cu_seqlens[seq + 1], a0), (long)T);
         tok0 = a0;
-        len = a1 - a0;
+        len = (CI)(a1 - a0);
     } else {
         tok0 = (long)seq * T;
         len = T;
@@ -679,9 +686,9 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             c1 = min(c0 + L, n);
         }
         tok0 += c0 * C;
-        len = max(0L, min(len - c0 * C, (c1 - c0) * C));
+        len = (CI)max(0L, min((long)len - c0 * C, (c1 - c0) * C));
     }
-    const long nch = (len + C - 1) / C;
+    const CI nch = (len + C - 1) / C;
     const int HDK = H * DK, HDV = H * dv;
     const long hrow = tok0 * H + h;                 // token rows are H*d elements apart
 
@@ -716,7 +723,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     // strictly lower on the diagonal) and / or the P tile (lower incl. the
     // diagonal).  Tiles are computed transposed, d[i] = X[16I + n][16J + 4g + i],
     // so each lane stores four consecutive columns of one row.
-    auto tile_job = [&](long ch, int p, bool doA, bool doP, f32x4 *lt = nullptr) __attribute__((always_inline)) {
+    auto tile_job = [&](CI ch, int p, bool doA, bool doP, f32x4 *lt = nullptr) __attribute__((always_inline)) {
         // (I, J) of tile p without a loop: off-diagonal tile o = p - NB has row
         // block I = the o-th entry of 1, 2, 2, 3, 3, 3 (four bits each)
         int I = p, J = p;
@@ -782,7 +789,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 
     // Blocks of chunk ch with a key channel too deep to factor (bit I: block I),
     // from the operand waves' masks; workgroup-uniform after the first barrier.
-    auto hard_mask = [&](long ch) __attribute__((always_inline)) {
+    auto hard_mask = [&](CI ch) __attribute__((always_inline)) {
         static_assert(K::NXW == 4 && K::SC_HARD % 4 == 0, "the four masks are one 16-byte LDS read");
         const f32x4 m4 = *(const f32x4 *)(bufSc(ch) + K::SC_HARD);
         int m = 0;
@@ -795,8 +802,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         diag_inverse_bf16(sA + p * 16 * PT, PT, n, g, lt0, lt1);
     };
     auto inv_f32 = [&](int p) __attribute__((always_inline)) { diag_inverse_f32(sA + p * 16 * PT, PT, n, lane); };
-    auto hard_block = [&](long ch, int I) {
-        hard_block_fn<In, DK, C>(k, q, log_alpha, beta, hrow, ch * C, len, H, gate, add, prep, map, sW, sA, sP,
+    auto hard_block = [&](CI ch, int I) {
+        hard_block_fn<In, DK, C>(k, q, log_alpha, beta, hrow, (long)ch * C, (long)len, H, gate, add, prep, map, sW, sA, sP,
                                  bufSc(ch), I);
     };
 
@@ -821,7 +828,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         float betar = 0.f;
         const int rowb_in = HDK * (int)sizeof(In), rowb_f = HDK * 4;
         const int voff_in = r0 * rowb_in + c0 * (int)sizeof(In), voff_f = r0 * rowb_f + c0 * 4;
-        auto chunk_valid = [&](long t0) { return (unsigned)((len - t0 < C) ? len - t0 : C); };
+        auto chunk_valid = [&](long t0) { const CI r = len - (CI)t0; return (unsigned)(r < C ? r : C); };
         auto prefetch_g = [&](long t0) __attribute__((always_inline)) {
             if (prep) {        // g in the input type, its bits kept in gr until stage A
                 const In *gp = (const In *)log_alpha;
@@ -899,9 +906,9 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         };
 
         // ---- stage A: cumulative decay, references, scaled operands
-        auto stage_a = [&](long ch) __attribute__((always_inline)) {
-            const long t0 = ch * C;
-            const int nval = (int)((len - t0 < C) ? len - t0 : C);
+        auto stage_a = [&](CI ch) __attribute__((always_inline)) {
+            const long t0 = (long)ch * C;
+            const int nval = (int)(len - ch * C < C ? len - ch * C : C);
             if (prep) {   // log_alpha = -softplus(g); no gate: 0
 #pragma unroll
                 for (int i = 0; i < RS; ++i) {
@@ -1184,7 +1191,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         // ---- stage B: the diagonal A tiles and their block inverses (with P
         //      when there is a single state wave, which then also leaves the
         //      off-diagonal A tiles here)
-        auto stage_b = [&](long ch, int hard) __attribute__((always_inline)) {
+        auto stage_b = [&](CI ch, int hard) __attribute__((always_inline)) {
             if (prep && xw == 0 && lane < C) {
                 // per-token factors for the state waves' next chunk: beta / |k|^2,
                 // |k| and 1 / |q| (zero vectors give 0)
@@ -1234,7 +1241,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         // Stage A sets the pace of the first segment, where each operand wave
         // shares its SIMD with a state wave that has time to spare: the operand
         // waves issue first there (wave priority, this workgroup only).
-        for (long ch = -1; ch < nch; ++ch) {
+        for (CI ch = -1; ch < nch; ++ch) {
             __builtin_amdgcn_s_setprio(3);
             if (ch + 1 < nch) {
                 stage_a(ch + 1);
@@ -1296,7 +1303,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         typedef In VL __attribute__((ext_vector_type(K::F32 ? 4 : 8)));
         VL vr[NVL];
         auto prefetch_v = [&](long t0) __attribute__((always_inline)) {
-            const unsigned nv = vreal ? (unsigned)((len - t0 < C) ? len - t0 : C) : 0u;
+            const CI rv_ = len - (CI)t0;
+            const unsigned nv = vreal ? (unsigned)(rv_ < C ? rv_ : C) : 0u;
             const __amdgpu_buffer_rsrc_t rv = buf_rsrc(v + (vreal ? vcol + t0 * HDV : 0), nv * rowb_v);
 #pragma unroll
             for (int u = 0; u < NVL; ++u) vr[u] = buf_load<VL>(rv, voff_v, (K::F32 ? 16 : 32) * u * rowb_v);
@@ -1320,7 +1328,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         constexpr int NJOB_MAP = K::NBV >= 2 ? K::NOFF : 0, NJOB_FULL = K::NBV >= 2 ? K::NPAIR : K::NOFF;
         const int njob = map ? NJOB_MAP : NJOB_FULL;
         constexpr int NROUND = (NJOB_FULL + K::NBV - 1) / K::NBV;   // NJOB_MAP <= NJOB_FULL
-        auto y_tiles = [&](long ch) __attribute__((always_inline)) {
+        auto y_tiles = [&](CI ch) __attribute__((always_inline)) {
 #pragma unroll
             for (int r = 0; r < NROUND; ++r) {
                 const int s = r * K::NBV + ((r & 1) ? K::NBV - 1 - cb : cb);
@@ -1332,7 +1340,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         };
         // Chunks with hard blocks take one more barrier after their tiles; then
         // the state waves correct those blocks' diagonal tiles.
-        auto hard_phase = [&](long ch, int hm) __attribute__((always_inline)) {
+        auto hard_phase = [&](CI ch, int hm) __attribute__((always_inline)) {
             if (hm) {
                 __syncthreads();
                 for (int I = cb; I < NB; I += K::NBV)
@@ -1342,10 +1350,10 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         if (nch > 0) prefetch_v(0);
 
         V4 Eb[NB];   // corrected errors of the chunk, operand type: E[16b + 4g + i][n]
-        for (long ch = -1; ch < nch; ++ch) {   // step -1: only the tiles of chunk 0
+        for (CI ch = -1; ch < nch; ++ch) {   // step -1: only the tiles of chunk 0
             if (ch >= 0) {
-                const long t0 = ch * C;
-                const int nval = (int)((len - t0 < C) ? len - t0 : C);
+                const long t0 = (long)ch * C;
+                const int nval = (int)(len - ch * C < C ? len - ch * C : C);
                 const In *Kr = bufKr(ch), *Qr = bufQr(ch);
                 const float *sc = bufSc(ch);
                 const float *fl = sc + K::SC_FLAG;
