@@ -27,11 +27,11 @@ LIB = os.path.join(PKG, "libkda.so")
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are disabled in all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# The chunk kernels are scheduled with LLVM's memory-clause strategy: with the
-# same results bit for bit, it ran the B=4 H=32 T=8192 prefill 1.2% and the
-# segmented T=65536 one 1.5% faster than the default (occupancy) strategy
-# (max-ILP was 9% slower).
-CHUNK_FLAGS = ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]
+# Extra flags of the chunk kernels.  LLVM's default scheduling strategy: on the
+# current kernels the memory-clause strategy (which once ran them 1.2-1.5%
+# faster) is 0.6-1.6% slower on every prefill workload, with the same results
+# bit for bit; max-ILP and iterative-minreg are slower still.
+CHUNK_FLAGS = []
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
 
