@@ -58,7 +58,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 KERNEL_SOURCES = ["kimi_delta_attention_fwd_amd/csrc/kda_chunk.h",
                   "kimi_delta_attention_fwd_amd/csrc/kda_device.h",
-                  "kimi_delta_attention_fwd_amd/csrc/kda_decode.h"]
+                  "kimi_delta_attention_fwd_amd/csrc/kda_decode.h",
+                  "kimi_delta_attention_fwd_amd/build.py"]   # (its compiler flags shape the kernels too)
 
 
 def kernel_source_hash() -> str:
