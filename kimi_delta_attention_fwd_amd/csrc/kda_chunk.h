@@ -700,6 +700,11 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     // 1.4% faster there, 1% slower on varlen in the plain kernel, which
     // rounds them in the solve instead: the same bits either way).
     constexpr bool ABF = !K::F32 && VAR == 2;
+    // The operand waves form the diagonal P tiles along with the diagonal A
+    // tiles (always with a single state wave; with more, except in the
+    // raw-input kernel, where that timed 1.4% slower: there the state waves
+    // take them with their off-diagonal pairs)
+    constexpr bool DPOP = K::NBV == 1 || VAR != 2;
     // LDS column of channel c of a [token, d_k] operand
     auto kcol = [&](int c) { return K::PAIRK ? K::pair_pos(c) : c; };
     // Fragments of one row of a [token, d_k] operand: x[t] = channels
@@ -1188,8 +1193,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             if (PSCAN && ch + 1 < nch) scan_g(nx_inc, nx_gl);
         };
 
-        // ---- stage B: the diagonal A tiles and their block inverses (with P
-        //      when there is a single state wave, which then also leaves the
+        // ---- stage B: the diagonal A tiles and their block inverses, with the
+        //      diagonal P tiles (DPOP; a single state wave also leaves the
         //      off-diagonal A tiles here)
         auto stage_b = [&](CI ch, int hard) __attribute__((always_inline)) {
             if (prep && xw == 0 && lane < C) {
@@ -1206,8 +1211,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 sc[K::SC_KN + lane] = __builtin_sqrtf(sk);
                 sc[K::SC_QI + lane] = sq > 0.f ? __builtin_amdgcn_rsqf(sq) : 0.f;
             }
-            if (add) {   // no A: only the diagonal P tiles of a single state wave
-                if (K::NBV == 1 && !map) {
+            if (add) {   // no A: only the diagonal P tiles
+                if (DPOP && !map) {
                     for (int p = xw; p < NB; p += K::NXW) tile_job(ch, p, false, true);
                 }
                 return;
@@ -1217,10 +1222,10 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             for (int p = xw; p < (K::NBV == 1 ? K::NPAIR : NB); p += K::NXW) {
                 if (p < NB && !K::F32) {
                     f32x4 lt[2];
-                    tile_job(ch, p, true, K::NBV == 1 && !map, lt);
+                    tile_job(ch, p, true, DPOP && !map, lt);
                     if (!((hard >> p) & 1)) inv_bf16(p, lt[0], lt[1]);
                 } else if (p < NB) {
-                    tile_job(ch, p, true, K::NBV == 1 && !map);
+                    tile_job(ch, p, true, DPOP && !map);
                     if (!((hard >> p) & 1)) inv_f32(p);
                 } else {
                     tile_job(ch, p, true, false);
@@ -1321,11 +1326,11 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             }
         }
         // Tiles the state waves form for a chunk, in their second segment: with
-        // two or more state waves the off-diagonal pairs (A and P) and then the
-        // diagonal P tiles, else the off-diagonal P tiles (MAP mode: no P tiles).
-        // Jobs are dealt in snake order so the heavier pairs spread evenly over
-        // the waves.
-        constexpr int NJOB_MAP = K::NBV >= 2 ? K::NOFF : 0, NJOB_FULL = K::NBV >= 2 ? K::NPAIR : K::NOFF;
+        // two or more state waves the off-diagonal pairs (A and P, and then the
+        // diagonal P tiles when the operand waves leave them), else the
+        // off-diagonal P tiles (MAP mode: no P tiles).  Jobs are dealt in snake
+        // order so the heavier pairs spread evenly over the waves.
+        constexpr int NJOB_MAP = K::NBV >= 2 ? K::NOFF : 0, NJOB_FULL = (K::NBV >= 2 && !DPOP) ? K::NPAIR : K::NOFF;
         const int njob = map ? NJOB_MAP : NJOB_FULL;
         constexpr int NROUND = (NJOB_FULL + K::NBV - 1) / K::NBV;   // NJOB_MAP <= NJOB_FULL
         auto y_tiles = [&](CI ch) __attribute__((always_inline)) {
