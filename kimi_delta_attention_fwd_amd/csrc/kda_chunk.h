@@ -592,9 +592,9 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     // the raw-input kernel keeps the unpaired layouts (about 1.5% slower with them)
     typedef ChunkCfg<In, DK, BV, C, VAR != 2> K;
     typedef typename V4T<In>::type V4;
-    // Chunk indices and lengths are 32-bit (fewer scalar registers, which the
-    // kernel otherwise spills into vector lanes); the raw-input kernel timed
-    // faster with 64-bit ones
+    // Chunk indices and lengths are 32-bit (cheaper scalar arithmetic, and
+    // fewer scalar registers for the kernel to spill into vector lanes); the
+    // raw-input kernel timed faster with 64-bit ones
     typedef typename std::conditional<VAR == 2, long, int>::type CI;
     constexpr int NB = K::NB, NDK = K::NDK, PK = K::PK, PC = K::PC, PT = K::PT, RS = K::RS;
 
