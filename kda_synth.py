@@ -152,15 +152,18 @@ def varlen_lengths(n=8, lo=2048, hi=16384, seed=3):
     return [int(x) for x in torch.randint(lo, hi + 1, (n,), generator=g)]
 
 
-def workload(name: str, device="cuda", seed=None) -> Prefill:
+def workload(name: str, device="cuda", seed=None, dtype=None) -> Prefill:
+    """A named prefill workload; `dtype` overrides its input type (the same
+    recipe and shapes in fp32, say)."""
     w = WORKLOADS[name]
     seed = SEEDS[name] if seed is None else seed
+    dt = w["dtype"] if dtype is None else dtype
     if name == "varlen":
         lengths = varlen_lengths(w["N"], w["len_lo"], w["len_hi"], seed=seed)
-        return prefill_varlen(lengths, w["H"], w["dk"], w["dv"], dtype=w["dtype"], g_mu=w["g_mu"],
+        return prefill_varlen(lengths, w["H"], w["dk"], w["dv"], dtype=dt, g_mu=w["g_mu"],
                               g_sigma=w["g_sigma"], beta=w["beta"], s0_sigma=w["s0_sigma"], seed=seed,
                               device=device)
-    return prefill(w["B"], w["T"], w["H"], w["dk"], w["dv"], dtype=w["dtype"], g_mu=w["g_mu"],
+    return prefill(w["B"], w["T"], w["H"], w["dk"], w["dv"], dtype=dt, g_mu=w["g_mu"],
                    g_sigma=w["g_sigma"], beta=w["beta"], s0_sigma=w["s0_sigma"], seed=seed, device=device)
 
 

@@ -968,6 +968,48 @@ def test_long_workload_sampled(dev):
         del out, sf
 
 
+def test_workloads_fp32_inputs_sampled(dev):
+    """The fp32-input mode at the full prefill sizes: the mid, long and varlen
+    workloads with the same recipe in fp32 (dk = 128 with C = 64 runs as
+    32-token chunks), each schedule the library picks, sampled heads against
+    the oracle at the fp32 bar."""
+    w = kda_synth.WORKLOADS["mid"]
+    note("case mid workload in fp32: B4 H32 T8192 d128 C64 (4 sampled heads)")
+    p = kda_synth.workload("mid", device=dev, dtype="f32")
+    out, sf = gpu_chunk(p, w["C"])
+    pairs = [(0, 5), (1, 30), (2, 17), (3, 0)]
+    o_ref, s_ref = sampled(p, pairs)
+    o_gpu = np.stack([f64(out[b, :, h]) for b, h in pairs])[:, :, None]
+    s_gpu = np.stack([f64(sf[b, h]) for b, h in pairs])[:, None]
+    assert_close("mid fp32 sampled", o_gpu, s_gpu, o_ref, s_ref, TOL["f32"])
+    del p, out, sf
+
+    w = kda_synth.WORKLOADS["long"]
+    note("case long workload in fp32: B1 H16 T65536 d128 C64, S0 in (2 sampled heads), segments=auto")
+    p = kda_synth.workload("long", device=dev, dtype="f32")
+    out, sf = gpu_chunk(p, w["C"], segments="auto")
+    pairs = [(0, 4), (0, 13)]
+    o_ref, s_ref = sampled(p, pairs)
+    o_gpu = np.stack([f64(out[b, :, h]) for b, h in pairs])[:, :, None]
+    s_gpu = np.stack([f64(sf[b, h]) for b, h in pairs])[:, None]
+    assert_close("long fp32 sampled", o_gpu, s_gpu, o_ref, s_ref, TOL["f32"])
+    del p, out, sf
+
+    w = kda_synth.WORKLOADS["varlen"]
+    note("case varlen workload in fp32: 8 sequences U[2048,16384] x H16 d128 C64 (one head per sequence)")
+    p = kda_synth.workload("varlen", device=dev, dtype="f32")
+    out, sf = kda.chunk_fwd_varlen(p.q, p.k, p.v, p.log_alpha, p.beta, p.cu_seqlens, S0=p.S0, C=w["C"])
+    torch.cuda.synchronize()
+    for n in range(len(p.cu_host) - 1):
+        a, b = p.cu_host[n], p.cu_host[n + 1]
+        h = (3 * n + 1) % w["H"]
+        sl = lambda t: t[:, a:b, h:h + 1]
+        o_ref, s_ref = oracle.forward(f64(sl(p.q)), f64(sl(p.k)), f64(sl(p.v)), f64(sl(p.log_alpha)),
+                                      f64(p.beta[:, a:b, h:h + 1]), S0=f64(p.S0[n:n + 1, h:h + 1]))
+        assert_close(f"varlen fp32 sequence {n} ({b - a} tokens) head {h}", f64(sl(out)),
+                     f64(sf[n:n + 1, h:h + 1]), o_ref, s_ref, TOL["f32"])
+
+
 # ---------------------------------------------------------------- decode step
 @pytest.mark.parametrize("N,H,dk,dv,dtype", [(3, 2, 64, 32, "bf16"), (2, 3, 128, 128, "bf16"),
                                              (4, 1, 16, 128, "f32"), (2, 2, 32, 64, "f32"),
