@@ -1052,20 +1052,21 @@ def test_decode_config_sweep(dev, dtype, dk, dv, T, N):
     assert_close(f"decode sweep {dtype} dk{dk} dv{dv} T{T} N{N}", f64(out), f64(S), o_ref, s_ref, TOL[dtype])
 
 
-def test_decode_workload_sampled(dev):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_workload_sampled(dev, dtype):
     """The decode workload at full size (256 sequences x 32 heads, d = 128, 1024
-    one-token steps): 16 sampled heads against the oracle at every step, and
+    one-token steps), in its bf16 inputs and in fp32 with the same recipe: 16 sampled heads against the oracle at every step, and
     the whole stream against the other schedule of the same recurrence, one
     chunk prefill (C = 64, as the mid prefill) of the 1024 tokens laid out
     [N, T, H, d] from the same initial states: every output and every final
     state, plus the prefill's sampled heads against the oracle."""
     w = kda_synth.WORKLOADS["decode"]
     N, H, dk, dv, steps = w["N"], w["H"], w["dk"], w["dv"], w["steps"]
-    note("case decode workload: 256 seq x H32 d128 bf16, 1024 steps (16 sampled heads, every step)")
-    d = kda_synth.decode(N, H, dk, dv, steps, device=dev)
+    note(f"case decode workload: 256 seq x H32 d128 {dtype}, 1024 steps (16 sampled heads, every step)")
+    d = kda_synth.decode(N, H, dk, dv, steps, dtype=dtype, device=dev)
     S = d.S0.clone()
     heads = [(n, h) for n, h in zip(range(3, 256, 16), range(0, 32, 2))]
-    out_all = torch.empty((steps, N, H, dv), dtype=torch.bfloat16, device=dev)
+    out_all = torch.empty((steps, N, H, dv), dtype=kda_synth.DTYPES[dtype], device=dev)
     ni = torch.tensor([n for n, _ in heads], device=dev)
     hi = torch.tensor([h for _, h in heads], device=dev)
     for t in range(steps):
@@ -1078,19 +1079,19 @@ def test_decode_workload_sampled(dev):
                                   f64(d.beta[:, ni, hi].transpose(0, 1).unsqueeze(2)),
                                   S0=f64(d.S0[ni, hi].unsqueeze(1)))
     s_ref = s_ref.reshape(len(heads), 1, dv, dk)
-    assert_close("decode sampled", f64(out_s)[:, :, None], f64(S[ni, hi]).reshape(len(heads), 1, dv, dk),
-                 o_ref, s_ref, TOL["bf16"])
+    assert_close(f"decode sampled {dtype}", f64(out_s)[:, :, None], f64(S[ni, hi]).reshape(len(heads), 1, dv, dk),
+                 o_ref, s_ref, TOL[dtype])
 
-    note("case decode workload vs chunk prefill of the same stream: N256 T1024 H32 d128 bf16 C64")
+    note(f"case decode workload vs chunk prefill of the same stream: N256 T1024 H32 d128 {dtype} C64")
     tm = lambda t: t.transpose(0, 1).contiguous()                   # [steps, N, ...] -> [N, steps, ...]
     pre, sf = kda.chunk_fwd(tm(d.q), tm(d.k), tm(d.v), tm(d.log_alpha), tm(d.beta), S0=d.S0, C=64, segments=1)
     torch.cuda.synchronize()
     dec = tm(out_all)                                                 # [N, steps, H, dv]
     del d
     # the whole stream: both schedules, every output and state
-    assert_close_device("decode vs prefill (all heads)", pre, sf, dec, S, TOL["bf16"])
-    assert_close("prefill sampled", f64(pre[ni, :, hi])[:, :, None], f64(sf[ni, hi]).reshape(len(heads), 1, dv, dk),
-                 o_ref, s_ref, TOL["bf16"])
+    assert_close_device(f"decode vs prefill (all heads) {dtype}", pre, sf, dec, S, TOL[dtype])
+    assert_close(f"prefill sampled {dtype}", f64(pre[ni, :, hi])[:, :, None], f64(sf[ni, hi]).reshape(len(heads), 1, dv, dk),
+                 o_ref, s_ref, TOL[dtype])
 
 
 def test_decode_equals_chunk_prefill_on_same_stream(dev):
