@@ -908,18 +908,21 @@ def test_mid_workload_sampled(dev):
     assert_close("mid sampled", o_gpu, s_gpu, o_ref, s_ref, TOL["bf16"])
 
 
-def test_prep_workload_sampled(dev):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prep_workload_sampled(dev, dtype):
     """The fused input preparation at the sizes the bench times it on: the mid
-    sizes with raw q, k and bf16 gate pre-activations (one launch of the
-    raw-input kernel), sampled heads against the oracle on the raw inputs."""
+    sizes with raw q, k and gate pre-activations in the input type (bf16, and
+    fp32 with the same recipe; one launch of the raw-input kernel), sampled
+    heads against the oracle on the raw inputs."""
     w = kda_synth.WORKLOADS["mid"]
     B, T, H, dk, dv, C = w["B"], w["T"], w["H"], w["dk"], w["dv"], w["C"]
-    note("case fused preparation at mid sizes: B4 H32 T8192 d128, raw q, k, bf16 g (4 sampled heads)")
-    p = kda_synth.prefill_raw(B, T, H, dk, dv, dtype="bf16", g_mu=w["g_mu"], g_sigma=w["g_sigma"],
+    note(f"case fused preparation at mid sizes: B4 H32 T8192 d128, raw q, k, {dtype} g (4 sampled heads)")
+    p = kda_synth.prefill_raw(B, T, H, dk, dv, dtype=dtype, g_mu=w["g_mu"], g_sigma=w["g_sigma"],
                               seed=kda_synth.SEEDS["mid"], device=dev)
-    out = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((B, T, H, dv), dtype=kda_synth.DTYPES[dtype], device=dev)
     sf = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
-    kda.kda_chunk_fwd_ex(p.q, p.k, p.v, p.log_alpha, p.beta, None, out, sf, B, T, H, dk, dv, C,
+    chunk_ex = kda.kda_chunk_fwd_ex if dtype == "bf16" else kda.kda_chunk_fwd_ex_f32
+    chunk_ex(p.q, p.k, p.v, p.log_alpha, p.beta, None, out, sf, B, T, H, dk, dv, C,
                          kda.variant(raw=True), 1, None, 0)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all() and torch.isfinite(sf).all()
@@ -929,17 +932,18 @@ def test_prep_workload_sampled(dev):
     o_ref, s_ref = oracle.forward(qn, kn, f64(pick(p.v)), la, f64(torch.stack([p.beta[b, :, h] for b, h in pairs]).unsqueeze(2)))
     o_gpu = np.stack([f64(out[b, :, h]) for b, h in pairs])[:, :, None]
     s_gpu = np.stack([f64(sf[b, h]) for b, h in pairs])[:, None]
-    assert_close("prep sampled", o_gpu, s_gpu, o_ref, s_ref, TOL["bf16"])
+    assert_close(f"prep sampled {dtype}", o_gpu, s_gpu, o_ref, s_ref, TOL[dtype])
 
 
-def test_decode_multi_workload_sampled(dev):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_multi_workload_sampled(dev, dtype):
     """The multi-token launch the bench times: the decode workload's sizes
-    (256 sequences x 32 heads, d = 128) with 4 tokens per launch, sampled heads
-    against the oracle."""
+    (256 sequences x 32 heads, d = 128) with 4 tokens per launch, in bf16 and
+    fp32 inputs, sampled heads against the oracle."""
     w = kda_synth.WORKLOADS["decode"]
     N, H, dk, dv, T = w["N"], w["H"], w["dk"], w["dv"], 4
-    note("case multi-token decode at decode sizes: N256 H32 d128, T4 (12 sampled heads)")
-    p = kda_synth.prefill(N, T, H, dk, dv, dtype="bf16", g_mu=w["g_mu"], g_sigma=w["g_sigma"],
+    note(f"case multi-token decode at decode sizes: N256 H32 d128 {dtype}, T4 (12 sampled heads)")
+    p = kda_synth.prefill(N, T, H, dk, dv, dtype=dtype, g_mu=w["g_mu"], g_sigma=w["g_sigma"],
                           beta=w["beta"], s0_sigma=w["s0_sigma"], seed=kda_synth.SEEDS["decode"], device=dev)
     S = p.S0.clone()
     out = kda.recurrent_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S)
@@ -948,7 +952,7 @@ def test_decode_multi_workload_sampled(dev):
     o_ref, s_ref = sampled(p, pairs)
     o_gpu = np.stack([f64(out[n, :, h]) for n, h in pairs])[:, :, None]
     s_gpu = np.stack([f64(S[n, h]) for n, h in pairs])[:, None]
-    assert_close("multi-token decode sampled", o_gpu, s_gpu, o_ref, s_ref, TOL["bf16"])
+    assert_close(f"multi-token decode sampled {dtype}", o_gpu, s_gpu, o_ref, s_ref, TOL[dtype])
 
 
 def test_long_workload_sampled(dev):
