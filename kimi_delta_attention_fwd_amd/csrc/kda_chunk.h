@@ -337,14 +337,15 @@ __device__ __forceinline__ void diag_inverse_bf16(float *At, int PT, int n, int 
     };
     const f32x4 L1 = lt0, U1 = lt1;
     const f32x4 U2 = mm(L1, U1), L2 = mm(U1, L1);
-    const f32x4 U3 = mm(L1, U2), L4 = mm(U2, L2), U4 = mm(L2, U2);
-    const f32x4 L8 = mm(U4, L4);
+    const f32x4 L4 = mm(U2, L2);
     f32x4 id;
 #pragma unroll
     for (int i = 0; i < 4; ++i) id[i] = (4 * g + i == n) ? 1.f : 0.f;
-    const f32x4 M1t = id - U1 + U2 - U3;              // ((I - L)(I + L^2))^T
+    const f32x4 X = id - U1;                          // (I - L)^T
+    const f32x4 M1t = X + mm(L2, X);                  // ((I - L)(I + L^2))^T
     const f32x4 M2t = M1t + mm(L4, M1t);              // ... (I + L^4)
-    const f32x4 Dt = M2t + mm(L8, M2t);               // ... (I + L^8)
+    const f32x4 W = mm(L4, M2t);                      // (L^4)^T M2t: L^8 as two L^4 factors
+    const f32x4 Dt = M2t + mm(L4, W);                 // ... (I + L^8)
     // stored pre-split for the bf16 solve: hi then lo bf16 parts in the lane's 16 bytes
     const bf16x4 hi = to_op<bf16>(Dt), lo = to_op<bf16>(Dt - to_f32<bf16>(hi));
     const f32x2 h2 = __builtin_bit_cast(f32x2, hi), l2 = __builtin_bit_cast(f32x2, lo);
