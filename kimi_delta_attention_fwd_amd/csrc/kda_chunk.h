@@ -329,7 +329,8 @@ struct ChunkCfg {
 // one fp32 MFMA product of two accumulator tiles gives acc(X^T Y).  (The powers
 // of L can grow like binomial coefficients before they cancel, about 1e-4
 // relative at worst: fine for the bf16 kernels.)
-__device__ __forceinline__ void diag_inverse_bf16(float *At, int PT, int n, int g, f32x4 lt0, f32x4 lt1)
+__device__ __forceinline__ void diag_inverse_bf16(float *At, int PT, int n, int g, f32x4 lt0, f32x4 lt1,
+                                                  bool keep_l = false)
 {
     auto mm = [](f32x4 x, f32x4 y) {   // acc(X^T Y)
         const f32x4 a[1] = {x}, b[1] = {y};
@@ -349,7 +350,13 @@ __device__ __forceinline__ void diag_inverse_bf16(float *At, int PT, int n, int 
     // stored pre-split for the bf16 solve: hi then lo bf16 parts in the lane's 16 bytes
     const bf16x4 hi = to_op<bf16>(Dt), lo = to_op<bf16>(Dt - to_f32<bf16>(hi));
     const f32x2 h2 = __builtin_bit_cast(f32x2, hi), l2 = __builtin_bit_cast(f32x2, lo);
-    *(f32x4 *)(At + n * PT + 4 * g) = f32x4{h2[0], h2[1], l2[0], l2[1]};
+    // keep_l (wave-uniform): store L itself (lt1, what the tile already holds)
+    // instead, with no branch, so the products above share one basic block with
+    // the code before them
+    f32x4 st = f32x4{h2[0], h2[1], l2[0], l2[1]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st[i] = keep_l ? lt1[i] : st[i];
+    *(f32x4 *)(At + n * PT + 4 * g) = st;
 }
 
 // fp32 kernels: column n of D by forward substitution over the rows of the
@@ -804,8 +811,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         return __builtin_amdgcn_readfirstlane(m);
     };
 
-    auto inv_bf16 = [&](int p, f32x4 lt0, f32x4 lt1) __attribute__((always_inline)) {
-        diag_inverse_bf16(sA + p * 16 * PT, PT, n, g, lt0, lt1);
+    auto inv_bf16 = [&](int p, f32x4 lt0, f32x4 lt1, bool keep_l) __attribute__((always_inline)) {
+        diag_inverse_bf16(sA + p * 16 * PT, PT, n, g, lt0, lt1, keep_l);
     };
     auto inv_f32 = [&](int p) __attribute__((always_inline)) { diag_inverse_f32(sA + p * 16 * PT, PT, n, lane); };
     auto hard_block = [&](CI ch, int I) {
@@ -1220,17 +1227,23 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             }
             // a diagonal tile of a hard block keeps L here: the hard-block
             // correction completes it and inverts it after the next barrier
-            for (int p = xw; p < (K::NBV == 1 ? K::NPAIR : NB); p += K::NXW) {
+            auto job = [&](int p) __attribute__((always_inline)) {
                 if (p < NB && !K::F32) {
                     f32x4 lt[2];
                     tile_job(ch, p, true, DPOP && !map, lt);
-                    if (!((hard >> p) & 1)) inv_bf16(p, lt[0], lt[1]);
+                    inv_bf16(p, lt[0], lt[1], (hard >> p) & 1);
                 } else if (p < NB) {
                     tile_job(ch, p, true, DPOP && !map);
                     if (!((hard >> p) & 1)) inv_f32(p);
                 } else {
                     tile_job(ch, p, true, false);
                 }
+            };
+            constexpr int NJB = K::NBV == 1 ? K::NPAIR : NB;
+            if constexpr (NJB <= K::NXW) {   // at most one job per wave: straight-line code
+                if (xw < NJB) job(xw);
+            } else {
+                for (int p = xw; p < NJB; p += K::NXW) job(p);
             }
         };
 
