@@ -1344,16 +1344,26 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         // diagonal P tiles when the operand waves leave them), else the
         // off-diagonal P tiles (MAP mode: no P tiles).  Jobs are dealt in snake
         // order so the heavier pairs spread evenly over the waves.
+        // When the operand waves keep the diagonal tiles (and there is no map),
+        // each off-diagonal pair is dealt as two jobs, its A tile and its P tile,
+        // so that the waves' shares differ by at most one tile.
+        constexpr bool SPLITJ = K::NBV >= 2 && DPOP && !MAP;
+        const bool split = SPLITJ && !add;
         constexpr int NJOB_MAP = K::NBV >= 2 ? K::NOFF : 0, NJOB_FULL = (K::NBV >= 2 && !DPOP) ? K::NPAIR : K::NOFF;
-        const int njob = map ? NJOB_MAP : NJOB_FULL;
-        constexpr int NROUND = (NJOB_FULL + K::NBV - 1) / K::NBV;   // NJOB_MAP <= NJOB_FULL
+        const int njob = split ? 2 * K::NOFF : (map ? NJOB_MAP : NJOB_FULL);
+        constexpr int NJOB_MAX = SPLITJ ? 2 * K::NOFF : NJOB_FULL;   // NJOB_MAP <= NJOB_FULL
+        constexpr int NROUND = (NJOB_MAX + K::NBV - 1) / K::NBV;
         auto y_tiles = [&](CI ch) __attribute__((always_inline)) {
 #pragma unroll
             for (int r = 0; r < NROUND; ++r) {
                 const int s = r * K::NBV + ((r & 1) ? K::NBV - 1 - cb : cb);
                 if (s < njob) {
-                    const int p = s < K::NOFF ? NB + s : s - K::NOFF;
-                    tile_job(ch, p, K::NBV >= 2 && p >= NB && !add, !map);
+                    if (split) {
+                        tile_job(ch, NB + (s >> 1), (s & 1) == 0, (s & 1) != 0);
+                    } else {
+                        const int p = s < K::NOFF ? NB + s : s - K::NOFF;
+                        tile_job(ch, p, K::NBV >= 2 && p >= NB && !add, !map);
+                    }
                 }
             }
         };
