@@ -1470,7 +1470,18 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 #pragma unroll
                     for (int J = 0; J < NB; ++J)
                         pb[J] = (J <= I) ? *(const V4 *)(sP + tile_index(NB, I, J) * 16 * PT + n * PT + 4 * g) : V4{};
-                    f32x4 o = O1[I] + mma_tiles<K::KC, In, NB>(zero4(), Eb, pb);   // O[16I + n][16cb + 4g + i]
+                    f32x4 po = zero4();
+                    if constexpr (!MAP && K::KC == 32) {   // pairs of tiles past the diagonal are zero: skipped
+#pragma unroll
+                        for (int s2 = 0; s2 < NB / 2; ++s2)
+                            if (2 * s2 <= I) {
+                                const V4 e2[2] = {Eb[2 * s2], Eb[2 * s2 + 1]}, p2[2] = {pb[2 * s2], pb[2 * s2 + 1]};
+                                po = mma_tiles<32, In, 2>(po, e2, p2);
+                            }
+                    } else {
+                        po = mma_tiles<K::KC, In, NB>(zero4(), Eb, pb);
+                    }
+                    f32x4 o = O1[I] + po;   // O[16I + n][16cb + 4g + i]
                     if (prep) o = o * sc[K::SC_QI + 16 * I + n];                   // / |q|
                     buf_store(to_op<In>(o), ro, voff_o, 16 * I * rowb_v);
                 }
