@@ -1388,18 +1388,42 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 const float *fl = sc + K::SC_FLAG;
                 const bool allfast = all_flags<K::NXW>(fl);
                 // ---- R = beta (V - Kbar S^T) and (Qbar S^T)^T, per 16-token block I
+                // VFOLD: V enters accumulator layout first and R accumulates onto it
+                // with the state negated (R = V - Kbar S^T with no subtraction; O1
+                // then holds -(Qbar S^T)^T).  Only where the V product and the row
+                // products share one MFMA shape; the plain kernel only (0.6% faster
+                // there, 2% slower with raw inputs).
+                constexpr bool VFOLD = (K::F32 || K::KD == 32) && VAR == 0;
                 f32x4 R[NB], O1[NB];
                 V4 ss[NDK];
+                if constexpr (VFOLD) {
+#pragma unroll
+                    for (int I = 0; I < NB; ++I) {
+                        f32x4 vt;                                       // V[16I + 4g + i][n]
+                        if constexpr (K::F32) {
+                            const V4 va[1] = {vr[I]}, vi[1] = {ident[0]};
+                            vt = mma_tiles<4, In, 1>(zero4(), va, vi);
+                        } else {
+                            vt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[I / 2], ident[I & 1], zero4(), 0, 0, 0);
+                        }
+                        if (prep) vt = vt * *(const f32x4 *)(sc + K::SC_KN + 16 * I + 4 * g);   // |k| v
+                        R[I] = vt;
+                    }
+                }
                 auto rows = [&](int I) __attribute__((always_inline)) {
                     V4 ak[NDK], bq[NDK];
                     if (!add) load_krow(ak, Kr + (16 * I + n) * PK);
                     if (!map) load_krow(bq, Qr + (16 * I + n) * PK);
-                    R[I] = add ? zero4() : mma_tiles<K::KD, In, NDK>(zero4(), ak, ss);    // [16I + 4g + i][n]
+                    if constexpr (VFOLD) {
+                        if (!add) R[I] = mma_tiles<K::KD, In, NDK>(R[I], ak, ss);    // V - Kbar S^T
+                    } else {
+                        R[I] = add ? zero4() : mma_tiles<K::KD, In, NDK>(zero4(), ak, ss);    // [16I + 4g + i][n]
+                    }
                     if (!map) O1[I] = mma_tiles<K::KD, In, NDK>(zero4(), ss, bq);   // [v = 4g + i][16I + n]
                 };
                 if (allfast) {
 #pragma unroll
-                    for (int ct = 0; ct < NDK; ++ct) ss[ct] = to_op<In>(Sacc[ct]);
+                    for (int ct = 0; ct < NDK; ++ct) ss[ct] = to_op<In>(VFOLD ? -Sacc[ct] : Sacc[ct]);
 #pragma unroll
                     for (int I = 0; I < NB; ++I) rows(I);
                 } else {
@@ -1408,7 +1432,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 #pragma unroll
                         for (int ct = 0; ct < NDK; ++ct) {
                             const f32x4 er = *(const f32x4 *)(sc + I * DK + 16 * ct + 4 * g);
-                            ss[ct] = to_op<In>(Sacc[ct] * er);        // S Diag(e^{rho_I}), transposed
+                            ss[ct] = to_op<In>(Sacc[ct] * (VFOLD ? -er : er));   // S Diag(e^{rho_I}), transposed
                         }
                         rows(I);
                     }
@@ -1416,6 +1440,11 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 #pragma unroll
                 for (int I = 0; I < NB; ++I) {
                     const f32x4 b4 = *(const f32x4 *)(sc + (prep ? K::SC_BH : K::SC_BETA) + 16 * I + 4 * g);
+                    if constexpr (VFOLD) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) R[I][i] *= b4[i];
+                        continue;
+                    }
                     f32x4 vt;                                           // V[16I + 4g + i][n]
                     if constexpr (K::F32) {
                         const V4 va[1] = {vr[I]}, vi[1] = {ident[0]};
@@ -1481,7 +1510,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                     } else {
                         po = mma_tiles<K::KC, In, NB>(zero4(), Eb, pb);
                     }
-                    f32x4 o = O1[I] + po;   // O[16I + n][16cb + 4g + i]
+                    f32x4 o = VFOLD ? po - O1[I] : O1[I] + po;   // O[16I + n][16cb + 4g + i]
                     if (prep) o = o * sc[K::SC_QI + 16 * I + n];                   // / |q|
                     buf_store(to_op<In>(o), ro, voff_o, 16 * I * rowb_v);
                 }
