@@ -264,6 +264,22 @@ kda_status_t kda_chunk_fwd_varlen_segmented_f32(const float *q, const float *k, 
  *                            the separate normalisation and softplus passes.
  * variant = gate | write | input; anything else is KDA_ERR_BAD_SHAPE.  The
  * plain entry points are variant 0 (KDA_GATE_CHANNEL | KDA_WRITE_DELTA).
+ *
+ * SCHEDULE (chunk *_ex entry points only; the decode ones reject it).
+ *   KDA_SCHED_MAP_OUTPUTS  with nseg > 1: the segmented schedule without a
+ *   second pass.  Every output is affine in the incoming state too: with the
+ *   extra state rows of a map started at the identity, o_t = o0_t + S_p m_t,
+ *   where o0_t is the real rows' output from S_start = 0 and m_t (dk values)
+ *   the extra rows' own output (their readout S_t q_t).  So the map launch
+ *   maps every segment after the first and also writes o0 into out and m into
+ *   the workspace, beside segment 0's whole pass; the composition carries the
+ *   incoming states on through S_final; and an epilogue adds S_p m_t to every
+ *   output of segment p.  The state in the epilogue's products is rounded to
+ *   bf16 in the bf16 entry points (as in the chunk kernel's own products with
+ *   it), and a bf16 output is rounded twice (o0, then the sum).  The
+ *   workspace also holds m, T_total * H * dk values of the input type:
+ *   kda_chunk_segmented_workspace_bytes_ex() gives its size.  Same results as
+ *   the two-pass schedule up to rounding.
  */
 enum {
     KDA_GATE_CHANNEL = 0,
@@ -271,12 +287,15 @@ enum {
     KDA_GATE_NONE = 2,
     KDA_WRITE_DELTA = 0,
     KDA_WRITE_ADD = 4,
-    KDA_INPUT_RAW = 8
+    KDA_INPUT_RAW = 8,
+    KDA_SCHED_MAP_OUTPUTS = 16
 };
 
 /* Chunk prefill with a variant and an optional segment-parallel schedule
- * (nseg, workspace as in kda_chunk_fwd_segmented; nseg = 1 needs no
- * workspace).  Dense and packed layouts, bf16 and fp32 inputs. */
+ * (nseg, workspace as in kda_chunk_fwd_segmented, or with
+ * KDA_SCHED_MAP_OUTPUTS in variant the schedule without a second pass and its
+ * larger workspace; nseg = 1 needs no workspace).  Dense and packed layouts,
+ * bf16 and fp32 inputs. */
 kda_status_t kda_chunk_fwd_ex(const void *q, const void *k, const void *v,
                               const float *log_alpha, const float *beta,
                               const float *S0, void *out, float *S_final,
@@ -312,6 +331,18 @@ kda_status_t kda_chunk_fwd_varlen_ex_f32(const float *q, const float *k, const f
 size_t kda_chunk_segmented_workspace_bytes(int nseq, int H, int dk, int dv, int nseg);
 
 /*
+ * Workspace bytes of the *_ex chunk entry points for nseq sequences of
+ * T_total tokens in all (B * T for the dense layout) and H heads, for the
+ * schedule `variant` selects (fp32_inputs: 1 for the _f32 entry points).
+ * Without KDA_SCHED_MAP_OUTPUTS, kda_chunk_segmented_workspace_bytes(); with
+ * it: 4 * nseq * H * nseg * (dv + dk) dk rounded up to 256, plus
+ * 4 * nseq * H * nseg * dv * dk rounded up to 256, plus T_total * H * dk
+ * values of the input type.  0 for nseg = 1 or invalid arguments.
+ */
+size_t kda_chunk_segmented_workspace_bytes_ex(int nseq, int T_total, int H, int dk, int dv, int nseg,
+                                              int variant, int fp32_inputs);
+
+/*
  * Segment count for a dense batch (fp32_inputs: 0 for the bf16 entry points,
  * 1 for the fp32 ones), from a model of the run time: 1 when the plain pass
  * already fills the GPU, more when few (sequence, head) pairs walk many
@@ -319,6 +350,22 @@ size_t kda_chunk_segmented_workspace_bytes(int nseq, int H, int dk, int dv, int 
  * that fails); never fails, returns at least 1.
  */
 int kda_chunk_auto_segments(int B, int T, int H, int dk, int dv, int C, int fp32_inputs);
+
+/*
+ * kda_chunk_auto_segments for the schedule `variant` selects: with
+ * KDA_SCHED_MAP_OUTPUTS the run-time model of the schedule without a second
+ * pass (its map chunks costing about a full chunk, plus the epilogue's
+ * streaming of m and out), else kda_chunk_auto_segments().
+ */
+int kda_chunk_auto_segments_ex(int B, int T, int H, int dk, int dv, int C, int fp32_inputs, int variant);
+
+/*
+ * The schedule the two run-time models above favour for a dense batch:
+ * KDA_SCHED_MAP_OUTPUTS when both pick more than one segment and the one
+ * without a second pass comes out cheaper, else 0 (the two-pass schedule, or
+ * the single pass when kda_chunk_auto_segments() returns 1).
+ */
+int kda_chunk_auto_schedule(int B, int T, int H, int dk, int dv, int C, int fp32_inputs);
 
 /*
  * One decode step ("KDA derivation summary" page, sect. 6, fused recurrent

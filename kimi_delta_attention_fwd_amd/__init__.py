@@ -96,6 +96,12 @@ def load():
     lib.kda_chunk_segmented_workspace_bytes.restype = Z
     lib.kda_chunk_auto_segments.argtypes = [I] * 7
     lib.kda_chunk_auto_segments.restype = I
+    lib.kda_chunk_segmented_workspace_bytes_ex.argtypes = [I] * 8
+    lib.kda_chunk_segmented_workspace_bytes_ex.restype = Z
+    lib.kda_chunk_auto_segments_ex.argtypes = [I] * 8
+    lib.kda_chunk_auto_segments_ex.restype = I
+    lib.kda_chunk_auto_schedule.argtypes = [I] * 7
+    lib.kda_chunk_auto_schedule.restype = I
     lib.kda_stream_copy.argtypes = [P, P, Z, P]
     lib.kda_stream_copy.restype = I
     lib.kda_check_cu_seqlens_host.argtypes = [P, I, I]
@@ -208,6 +214,19 @@ def kda_chunk_auto_segments(B, T, H, dk, dv, C, fp32_inputs) -> int:
     return load().kda_chunk_auto_segments(B, T, H, dk, dv, C, 1 if fp32_inputs else 0)
 
 
+def kda_chunk_segmented_workspace_bytes_ex(nseq, T_total, H, dk, dv, nseg, variant, fp32_inputs) -> int:
+    return load().kda_chunk_segmented_workspace_bytes_ex(nseq, T_total, H, dk, dv, nseg, variant,
+                                                         1 if fp32_inputs else 0)
+
+
+def kda_chunk_auto_segments_ex(B, T, H, dk, dv, C, fp32_inputs, variant) -> int:
+    return load().kda_chunk_auto_segments_ex(B, T, H, dk, dv, C, 1 if fp32_inputs else 0, variant)
+
+
+def kda_chunk_auto_schedule(B, T, H, dk, dv, C, fp32_inputs) -> int:
+    return load().kda_chunk_auto_schedule(B, T, H, dk, dv, C, 1 if fp32_inputs else 0)
+
+
 def kda_recurrent_step(q, k, v, log_alpha, beta, S, out, N, H, dk, dv, stream=None):
     _check("kda_recurrent_step", load().kda_recurrent_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(out), N, H, dk, dv,
@@ -234,13 +253,19 @@ def kda_recurrent_fwd_f32(q, k, v, log_alpha, beta, S, out, N, T, H, dk, dv, str
 
 GATES = {"channel": 0, "scalar": 1, "none": 2}
 WRITES = {"delta": 0, "add": 4}
+SCHED_MAP_OUTPUTS = 16
+SCHEDULES = ("two-pass", "one-pass")
 
 
-def variant(gate="channel", write="delta", raw=False) -> int:
+def variant(gate="channel", write="delta", raw=False, schedule="two-pass") -> int:
     """Variant selector of the *_ex entry points: gate "channel" (KDA, GLA),
     "scalar" (one decay per token and head) or "none"; write "delta" or "add";
-    raw=True for un-normalised q, k and gate pre-activations g (fused prep)."""
-    return GATES[gate] | WRITES[write] | (8 if raw else 0)
+    raw=True for un-normalised q, k and gate pre-activations g (fused prep);
+    schedule "one-pass" for the segmented schedule without a second pass
+    (KDA_SCHED_MAP_OUTPUTS; chunk entry points only)."""
+    if schedule not in SCHEDULES:
+        raise ValueError(f"schedule must be one of {SCHEDULES}, got {schedule!r}")
+    return GATES[gate] | WRITES[write] | (8 if raw else 0) | (SCHED_MAP_OUTPUTS if schedule == "one-pass" else 0)
 
 
 def kda_chunk_fwd_ex(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, dk, dv, C, variant, nseg=1,
@@ -358,18 +383,30 @@ def _gate_spec(gate, raw, q, lead_shape, dk):
     return shape, dtype
 
 
-def _workspace(nseq, H, dk, dv, nseg, device):
+def _workspace(nseq, H, dk, dv, nseg, device, T_total=0, var=0, f32=False):
     import torch
-    nbytes = kda_chunk_segmented_workspace_bytes(nseq, H, dk, dv, nseg)
+    nbytes = kda_chunk_segmented_workspace_bytes_ex(nseq, T_total, H, dk, dv, nseg, var, f32)
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device), nbytes
 
 
+def _schedule(schedule, nseq, T, H, dk, dv, C, f32):
+    """The schedule's variant bit: "auto" asks the library's run-time models."""
+    if schedule == "auto":
+        return kda_chunk_auto_schedule(nseq, T, H, dk, dv, C, f32)
+    if schedule not in SCHEDULES:
+        raise ValueError(f"schedule must be 'auto' or one of {SCHEDULES}, got {schedule!r}")
+    return SCHED_MAP_OUTPUTS if schedule == "one-pass" else 0
+
+
 def chunk_fwd(q, k, v, log_alpha, beta, S0=None, C=64, output_final_state=True, stream=None, segments="auto",
-              gate="channel", write="delta", raw=False):
+              gate="channel", write="delta", raw=False, schedule="auto"):
     """Chunk prefill of a dense batch.  Returns ``(out, S_final or None)``.
 
     ``segments``: 1 for the single pass, n > 1 for the segment-parallel
     schedule with n segments per sequence, "auto" for the library's choice.
+    ``schedule`` (segments > 1): "two-pass", "one-pass" (no second pass, a
+    larger workspace) or "auto": with segments="auto" the library's run-time
+    models pick the schedule and its segment count, else "two-pass".
     ``gate`` / ``write`` / ``raw`` select a variant (see :func:`variant`); with
     gate="scalar" log_alpha is [B, T, H], with gate="none" it may be None;
     with raw=True it holds the pre-activations g in q's dtype.
@@ -390,10 +427,15 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, C=64, output_final_state=True, 
               dict(k=q.dtype, v=q.dtype, log_alpha=g_dtype, beta=torch.float32, S0=torch.float32))
     out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     sf = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device) if output_final_state else None
-    nseg = kda_chunk_auto_segments(B, T, H, dk, dv, C, f32) if segments == "auto" else int(segments)
-    var = variant(gate, write, raw)
+    if segments == "auto":
+        sched = _schedule(schedule, B, T, H, dk, dv, C, f32)
+        nseg = kda_chunk_auto_segments_ex(B, T, H, dk, dv, C, f32, sched)
+    else:
+        sched = _schedule("two-pass" if schedule == "auto" else schedule, B, T, H, dk, dv, C, f32)
+        nseg = int(segments)
+    var = variant(gate, write, raw) | (sched if nseg > 1 else 0)
     if var != 0:
-        ws, nbytes = _workspace(B, H, dk, dv, nseg, q.device) if nseg > 1 else (None, 0)
+        ws, nbytes = _workspace(B, H, dk, dv, nseg, q.device, B * T, var, f32) if nseg > 1 else (None, 0)
         fn = kda_chunk_fwd_ex_f32 if f32 else kda_chunk_fwd_ex
         fn(q, k, v, log_alpha, beta, S0, out, sf, B, T, H, dk, dv, C, var, nseg, ws, nbytes, stream)
     elif nseg == 1:
@@ -407,10 +449,11 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, C=64, output_final_state=True, 
 
 
 def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, C=64, output_final_state=True, stream=None,
-                     segments=1):
+                     segments=1, schedule="two-pass"):
     """Chunk prefill of N packed sequences ([1, T_total, H, d] tensors, device cu_seqlens [N+1]).
 
-    ``segments`` > 1 cuts every sequence into that many segments run in parallel.
+    ``segments`` > 1 cuts every sequence into that many segments run in
+    parallel, with ``schedule`` "two-pass" or "one-pass".
     """
     import torch
     f32 = _mode(q)
@@ -429,9 +472,15 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, C=64, output
     out = torch.empty((1, T_total, H, dv), dtype=q.dtype, device=q.device)
     sf = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device) if output_final_state else None
     nseg = int(segments)
+    sched = _schedule(schedule, 1, 1, H, dk, dv, C, f32)
     if nseg == 1:
         fn = kda_chunk_fwd_varlen_f32 if f32 else kda_chunk_fwd_varlen
         fn(q, k, v, log_alpha, beta, S0, out, sf, cu_seqlens, N, T_total, H, dk, dv, C, stream)
+    elif sched:
+        ws, nbytes = _workspace(N, H, dk, dv, nseg, q.device, T_total, sched, f32)
+        fn = kda_chunk_fwd_varlen_ex_f32 if f32 else kda_chunk_fwd_varlen_ex
+        fn(q, k, v, log_alpha, beta, S0, out, sf, cu_seqlens, N, T_total, H, dk, dv, C, sched, nseg, ws, nbytes,
+           stream)
     else:
         ws, nbytes = _workspace(N, H, dk, dv, nseg, q.device)
         fn = kda_chunk_fwd_varlen_segmented_f32 if f32 else kda_chunk_fwd_varlen_segmented

@@ -115,6 +115,10 @@ int run_chunk_len(bool f32, int dk, int C)
 // bit 3 raw inputs (q, k normalised in the kernel, gate pre-activations).
 bool valid_variant(int variant) { return (variant & ~15) == 0 && (variant & 3) != 3; }
 
+// Bit 4 of the chunk entry points' variant: the segmented schedule without a
+// second pass (KDA_SCHED_MAP_OUTPUTS).
+constexpr int kSchedMapOut = 16;
+
 // Bytes and alignment of the gate argument: fp32 log_alpha, or with raw
 // inputs g in the input type (es bytes per element).
 uint64_t gate_bytes(int variant, uint64_t ntok_heads, int dk, uint64_t es)
@@ -146,6 +150,25 @@ uint64_t seg_workspace_bytes(uint64_t nheads, int dk, int dv, int nseg)
 {
     if (nseg <= 1) return 0;
     return seg_map_bytes(nheads, dk, dv, nseg) + nheads * (uint64_t)nseg * (uint64_t)dv * (uint64_t)dk * 4u;
+}
+
+// Workspace of the schedule without a second pass: a map for every segment
+// (slot 0 unused), the incoming states, then the virtual rows' outputs
+// [ntok, H, dk] in the input type (es bytes).
+uint64_t mout_map_bytes(uint64_t nheads, int dk, int dv, int nseg)
+{
+    return align256(nheads * (uint64_t)nseg * (uint64_t)(dv + dk) * (uint64_t)dk * 4u);
+}
+
+uint64_t mout_start_bytes(uint64_t nheads, int dk, int dv, int nseg)
+{
+    return align256(nheads * (uint64_t)nseg * (uint64_t)dv * (uint64_t)dk * 4u);
+}
+
+uint64_t mout_workspace_bytes(uint64_t nheads, uint64_t ntok_heads, int dk, int dv, int nseg, uint64_t es)
+{
+    if (nseg <= 1) return 0;
+    return mout_map_bytes(nheads, dk, dv, nseg) + mout_start_bytes(nheads, dk, dv, nseg) + ntok_heads * dk * es;
 }
 
 // Compute units of the current device, queried once per device (256, the
@@ -199,6 +222,22 @@ int seg_lead(long nheads, int dk, int dv, int bv, int nseg, int cus)
     return rounds > 100 ? 1000 : (int)(8.5 * (double)rounds + 0.5);
 }
 
+// Lead segment of the schedule without a second pass: the map launch holds
+// segment 0's pass beside the maps of segments 1 .. nseg - 1, whose chunks
+// (with their outputs) cost about what a full one does, so segment 0 gets one
+// chunk per map chunk and round of workgroups.
+int seg_lead_mout(long nheads, int dk, int dv, int bv, int nseg, int cus)
+{
+    if (nseg < 2) return 0;
+    if (const char *env = std::getenv("KDA_SEG_LEAD")) {
+        const int v = std::atoi(env);
+        if (v >= 1 && v <= 1000) return v;
+    }
+    const long nA = nheads * (dv / bv);
+    const long rounds = map_launch_rounds(nheads * (long)(nseg - 1) * ((dv + dk) / bv) + nA, nA, cus);
+    return rounds > 100 ? 1000 : (int)(10 * rounds);
+}
+
 // Segment count for a dense batch from a model of the run time in chunk steps.
 // A pass of g workgroups that each walk L chunks takes ceil(g / CUs) (L + 1)
 // steps (one workgroup per compute unit; the extra step is the prologue: the
@@ -210,15 +249,21 @@ int seg_lead(long nheads, int dk, int dv, int bv, int nseg, int cus)
 // extra launches about one step; rounds as in map_launch_rounds.  Fitted to
 // measured runs: 1 segment for B=4 H=32 T=8192, 9 for B=1 H=16 T=65536
 // (d = 128), 9 for B=2 H=4 T=1024 (d = 64).
-int auto_segments(bool f32, int B, int T, int H, int dk, int dv, int C)
+//
+// Schedule without a second pass (mout): the map launch takes max(L0 + 1,
+// rounds (L + 1)) steps (its map chunks, which also form the outputs, cost
+// about a full chunk), the composition as above, and the epilogue streams m
+// and out once: about one step per 13 MB (fitted to B=1 H=16 T=65536 d=128,
+// 8 segments: 1.22 ms, and 7 and 9 segments within 5%).
+double auto_cost(bool f32, int B, int T, int H, int dk, int dv, int C, bool mout, int &best_s)
 {
-    if (B <= 0 || T <= 0 || H <= 0 || !supported_d(dk) || !supported_d(dv) || !supported_c(C)) return 1;
+    best_s = 1;
+    if (B <= 0 || T <= 0 || H <= 0 || !supported_d(dk) || !supported_d(dv) || !supported_c(C)) return 0.0;
     const int Cr = run_chunk_len(f32, dk, C);
-    if (Cr == 0) return 1;
+    if (Cr == 0) return 0.0;
     const int cus = device_cus();
     const long nch = (T + Cr - 1) / Cr, nheads = (long)B * H;
     double best = 0.0;
-    int best_s = 1;
     for (int s = 1; s <= 64 && s <= nch; ++s) {
         const int bv = choose_bv(f32, dk, dv, Cr, s > 1 ? dk : 64);
         if (bv == 0) continue;
@@ -226,6 +271,14 @@ int auto_segments(bool f32, int B, int T, int H, int dk, int dv, int C)
         double cost;
         if (s == 1) {
             cost = (double)((nheads * nvA + cus - 1) / cus) * (double)(nch + 1);
+        } else if (mout) {
+            const int lead = seg_lead_mout(nheads, dk, dv, bv, s, cus);
+            const long L = (10 * nch + 10 * (s - 1) + lead - 1) / (10 * (s - 1) + lead);
+            const long L0 = nch - (s - 1) * L > 0 ? nch - (s - 1) * L : 0;
+            const long g1 = nheads * ((s - 1) * nvB + nvA);
+            const double map = (double)map_launch_rounds(g1, nheads * nvA, cus) * (double)(L + 1);
+            const double epi = (double)B * (double)T * (double)H * (double)(dk + 2 * dv) * (f32 ? 4.0 : 2.0) / 13e6;
+            cost = (map > (double)(L0 + 1) ? map : (double)(L0 + 1)) + 0.6 * std::pow(dk / 64.0, 1.5) * s + epi + 1.0;
         } else {
             const int lead = seg_lead(nheads, dk, dv, bv, s, cus);
             const long L = (10 * nch + 10 * (s - 1) + lead - 1) / (10 * (s - 1) + lead);
@@ -240,7 +293,14 @@ int auto_segments(bool f32, int B, int T, int H, int dk, int dv, int C)
             best_s = s;
         }
     }
-    return best_s;
+    return best;
+}
+
+int auto_segments(bool f32, int B, int T, int H, int dk, int dv, int C, bool mout = false)
+{
+    int s = 1;
+    auto_cost(f32, B, T, H, dk, dv, C, mout, s);
+    return s;
 }
 
 hipError_t dispatch_chunk(bool f32, const kda::ChunkArgs &a)
@@ -264,7 +324,10 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
                           uint64_t workspace_bytes = 0, int variant = 0,
                           const kda::StaticScratch *scratch = nullptr)
 {
-    if (!valid_variant(variant)) return fail(KDA_ERR_BAD_SHAPE, "invalid variant %d", variant);
+    const bool mout = (variant & kSchedMapOut) != 0;
+    variant &= ~kSchedMapOut;
+    if (!valid_variant(variant)) return fail(KDA_ERR_BAD_SHAPE, "invalid variant %d", variant | (mout ? kSchedMapOut : 0));
+    if (mout && scratch) return fail(KDA_ERR_UNSUPPORTED, "the allocation-free entry point has no one-pass schedule");
     const int gate = variant & 3;
     if (nseg < 1 || nseg > kMaxSegments)
         return fail(KDA_ERR_BAD_SHAPE, "segment count must be in [1, %d] (got %d)", kMaxSegments, nseg);
@@ -306,7 +369,8 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
                                      Buf{S_final, S_final ? ns * 4 : 0, "S_final"},
                                      Buf{S0, S0 ? ns * 4 : 0, "S0"});
     if (st != KDA_OK) return st;
-    const uint64_t wsb = seg_workspace_bytes(nheads, dk, dv, nseg);
+    const uint64_t wsb = mout ? mout_workspace_bytes(nheads, ntok * H, dk, dv, nseg, f32 ? 4 : 2)
+                              : seg_workspace_bytes(nheads, dk, dv, nseg);
     if (nseg > 1 && scratch) {
         // the library's own fixed-size array: it aliases nothing the caller owns
         if (wsb > scratch->bytes)
@@ -362,9 +426,19 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
     a.gate = gate;
     a.add = (variant >> 2) & 1;
     a.prep = (variant >> 3) & 1;
-    a.lead = nseg > 1 ? seg_lead((long)nheads, dk, dv, BV, nseg, device_cus()) : 0;
-    a.seg_map = nseg > 1 ? (float *)workspace : nullptr;
-    a.seg_start = nseg > 1 ? (float *)((char *)workspace + seg_map_bytes(nheads, dk, dv, nseg)) : nullptr;
+    a.mout = (mout && nseg > 1) ? 1 : 0;
+    a.cus = device_cus();
+    a.mws = nullptr;
+    if (a.mout) {
+        a.lead = seg_lead_mout((long)nheads, dk, dv, BV, nseg, device_cus());
+        a.seg_map = (float *)workspace;
+        a.seg_start = (float *)((char *)workspace + mout_map_bytes(nheads, dk, dv, nseg));
+        a.mws = (char *)workspace + mout_map_bytes(nheads, dk, dv, nseg) + mout_start_bytes(nheads, dk, dv, nseg);
+    } else {
+        a.lead = nseg > 1 ? seg_lead((long)nheads, dk, dv, BV, nseg, device_cus()) : 0;
+        a.seg_map = nseg > 1 ? (float *)workspace : nullptr;
+        a.seg_start = nseg > 1 ? (float *)((char *)workspace + seg_map_bytes(nheads, dk, dv, nseg)) : nullptr;
+    }
     a.stream = (hipStream_t)stream;
     const hipError_t e = dispatch_chunk(f32, a);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "chunk kernel launch failed: %s", hipGetErrorString(e));
@@ -573,6 +647,31 @@ size_t kda_chunk_segmented_workspace_bytes(int nseq, int H, int dk, int dv, int 
 int kda_chunk_auto_segments(int B, int T, int H, int dk, int dv, int C, int fp32_inputs)
 {
     return auto_segments(fp32_inputs != 0, B, T, H, dk, dv, C);
+}
+
+int kda_chunk_auto_segments_ex(int B, int T, int H, int dk, int dv, int C, int fp32_inputs, int variant)
+{
+    return auto_segments(fp32_inputs != 0, B, T, H, dk, dv, C, (variant & kSchedMapOut) != 0);
+}
+
+int kda_chunk_auto_schedule(int B, int T, int H, int dk, int dv, int C, int fp32_inputs)
+{
+    int s2 = 1, s1 = 1;
+    const double two = auto_cost(fp32_inputs != 0, B, T, H, dk, dv, C, false, s2);
+    const double one = auto_cost(fp32_inputs != 0, B, T, H, dk, dv, C, true, s1);
+    return (s1 > 1 && s2 > 1 && one < two) ? kSchedMapOut : 0;
+}
+
+size_t kda_chunk_segmented_workspace_bytes_ex(int nseq, int T_total, int H, int dk, int dv, int nseg, int variant,
+                                              int fp32_inputs)
+{
+    if (nseq <= 0 || T_total < 0 || H <= 0 || !supported_d(dk) || !supported_d(dv) || nseg < 1 ||
+        nseg > kMaxSegments || !valid_variant(variant & ~kSchedMapOut))
+        return 0;
+    const uint64_t nheads = (uint64_t)nseq * (uint64_t)H;
+    if (variant & kSchedMapOut)
+        return (size_t)mout_workspace_bytes(nheads, (uint64_t)T_total * (uint64_t)H, dk, dv, nseg, fp32_inputs ? 4 : 2);
+    return (size_t)seg_workspace_bytes(nheads, dk, dv, nseg);
 }
 
 kda_status_t kda_recurrent_step(const void *q, const void *k, const void *v, const float *log_alpha,

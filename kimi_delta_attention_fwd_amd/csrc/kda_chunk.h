@@ -559,6 +559,24 @@ __device__ __noinline__ void hard_block_fn(const In *__restrict__ k, const In *_
     }
 }
 
+// Segment bounds of the chunk schedule, shared by the chunk kernel and the
+// output epilogue: chunks [c0, c1) of a sequence of n chunks for segment seg
+// of nsegs (lead > 0: segments 1 .. nsegs - 1 take L = ceil(10 n / (10
+// (nsegs - 1) + lead)) each from the end, segment 0 the rest; else equal).
+__device__ __forceinline__ void seg_bounds(long n, int nsegs, int lead, int seg, long &c0, long &c1)
+{
+    if (lead > 0) {
+        const long L = (10 * n + 10 * (nsegs - 1) + lead - 1) / (10 * (nsegs - 1) + lead);
+        const long l0 = max(0L, n - (nsegs - 1) * L);
+        c0 = seg == 0 ? 0 : min(l0 + (seg - 1) * L, n);
+        c1 = seg == 0 ? l0 : min(c0 + L, n);
+    } else {
+        const long L = (n + nsegs - 1) / nsegs;
+        c0 = min((long)seg * L, n);
+        c1 = min(c0 + L, n);
+    }
+}
+
 // Variants (uniform arguments, read only when VAR): gate 0 = per-channel log_alpha [.., H, DK],
 // 1 = one log_alpha per token and head [.., H] shared by all key channels,
 // 2 = no decay (log_alpha not read); add = 1 replaces the delta write by the
@@ -590,7 +608,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                  const float *S0, In *__restrict__ out, float *S_final,
                  const int *__restrict__ cu_seqlens, int T, int H, int dv, int xcd_map,
                  int nsegs, float *seg_start, float *seg_map, int gate_arg, int add_arg, int prep_arg,
-                 int lead)
+                 int lead, In *__restrict__ mws, int mout_arg)
 {
     // VAR = 0: the plain recurrence, the variant arguments folded away; 1: any
     // variant, read from the arguments; 2: raw inputs with the per-channel gate
@@ -643,8 +661,13 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     };
     int head, seg, vb;
     bool lead_full = false;                          // the lead segment's whole pass in the map launch
+    // mout: the map launch of the schedule without a second pass maps every
+    // segment after the first and writes their outputs from a zero incoming
+    // state (real rows, into out) and those of the virtual rows (into mws)
+    const bool mout = MAP && mout_arg != 0 && lead > 0;
+    const int nmap = mout ? nsegs - 1 : nsegs - 2;   // mapped segments per sequence beside the lead one
     if (MAP && lead > 0) {
-        const int nA = (int)(gridDim.x / (nvA + (nsegs - 2) * nvB)) * nvA;
+        const int nA = (int)(gridDim.x / (nvA + nmap * nvB)) * nvA;
         int unit;
         if ((int)blockIdx.x < nA) {
             place(blockIdx.x, nvA, xcd_map & 1, unit, vb);
@@ -653,8 +676,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             lead_full = true;
         } else {
             place(blockIdx.x - nA, nvB, xcd_map & 2, unit, vb);
-            head = unit / (nsegs - 2);
-            seg = 1 + unit % (nsegs - 2);
+            head = unit / nmap;
+            seg = 1 + unit % nmap;
         }
     } else {
         const int nsu = (MAP || lead > 0) ? nsegs - 1 : nsegs;   // segments per sequence in this grid
@@ -663,7 +686,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         head = unit / nsu;
         seg = unit % nsu + ((!MAP && lead > 0) ? 1 : 0);
     }
-    const bool map = MAP && !lead_full;              // augmented state, no outputs
+    const bool map = MAP && !lead_full;              // augmented state
+    const bool noout = map && !mout;                 // ... and no outputs (q not read)
     const int seq = head / H, h = head % H;
     long tok0;
     CI len;   // tokens of this unit (at most T)
@@ -681,18 +705,8 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         // nsegs) each.  Lead: segments 1 .. nsegs - 1 take L = ceil(10 n /
         // (10 (nsegs - 1) + lead)) each from the end, segment 0 the rest (about
         // lead / 10 L; none when the sequence is short).
-        const long n = (len + C - 1) / C;
         long c0, c1;
-        if (lead > 0) {
-            const long L = (10 * n + 10 * (nsegs - 1) + lead - 1) / (10 * (nsegs - 1) + lead);
-            const long l0 = max(0L, n - (nsegs - 1) * L);
-            c0 = seg == 0 ? 0 : min(l0 + (seg - 1) * L, n);
-            c1 = seg == 0 ? l0 : min(c0 + L, n);
-        } else {
-            const long L = (n + nsegs - 1) / nsegs;
-            c0 = min((long)seg * L, n);
-            c1 = min(c0 + L, n);
-        }
+        seg_bounds((len + C - 1) / C, nsegs, lead, seg, c0, c1);
         tok0 += c0 * C;
         len = (CI)max(0L, min((long)len - c0 * C, (c1 - c0) * C));
     }
@@ -816,7 +830,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     };
     auto inv_f32 = [&](int p) __attribute__((always_inline)) { diag_inverse_f32(sA + p * 16 * PT, PT, n, lane); };
     auto hard_block = [&](CI ch, int I) {
-        hard_block_fn<In, DK, C>(k, q, log_alpha, beta, hrow, (long)ch * C, (long)len, H, gate, add, prep, map, sW, sA, sP,
+        hard_block_fn<In, DK, C>(k, q, log_alpha, beta, hrow, (long)ch * C, (long)len, H, gate, add, prep, noout, sW, sA, sP,
                                  bufSc(ch), I);
     };
 
@@ -880,7 +894,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             }
         };
         auto prefetch_q = [&](long t0) __attribute__((always_inline)) {
-            if (map) return;
+            if (noout) return;
             const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + (hrow + t0 * H) * DK, chunk_valid(t0) * rowb_in);
 #pragma unroll
             for (int i = 0; i < RS; ++i) qr[i] = buf_load<In4>(rq, voff_in, i * rowb_in);
@@ -1087,16 +1101,16 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                         pp[j] *= al[i][j];
                         const float kf = tof(kr[i][j]);
                         vkr[j] = kf * pp[j];                       // k e^{G - ref}
-                        if (!map) vqr[j] = tof(qr[i][j]) * pp[j];   // q e^{G - ref}
+                        if (!noout) vqr[j] = tof(qr[i][j]) * pp[j];   // q e^{G - ref}
                         if (prep) {
                             sk[i] += kf * kf;
-                            if (!map) sq[i] += tof(qr[i][j]) * tof(qr[i][j]);
+                            if (!noout) sq[i] += tof(qr[i][j]) * tof(qr[i][j]);
                         }
                     }
                     if (act) {
                         const int r = r0 + i;
                         store4(Kr + r * PK + kcol(c0), vkr);
-                        if (!map) store4(Qr + r * PK + kcol(c0), vqr);
+                        if (!noout) store4(Qr + r * PK + kcol(c0), vqr);
                     }
                 }
                 if (prep) {   // per token over the channel group's lanes, stored by its first lane
@@ -1220,7 +1234,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 sc[K::SC_QI + lane] = sq > 0.f ? __builtin_amdgcn_rsqf(sq) : 0.f;
             }
             if (add) {   // no A: only the diagonal P tiles
-                if (DPOP && !map) {
+                if (DPOP && !noout) {
                     for (int p = xw; p < NB; p += K::NXW) tile_job(ch, p, false, true);
                 }
                 return;
@@ -1230,10 +1244,10 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
             auto job = [&](int p) __attribute__((always_inline)) {
                 if (p < NB && !K::F32) {
                     f32x4 lt[2];
-                    tile_job(ch, p, true, DPOP && !map, lt);
+                    tile_job(ch, p, true, DPOP && !noout, lt);
                     inv_bf16(p, lt[0], lt[1], (hard >> p) & 1);
                 } else if (p < NB) {
-                    tile_job(ch, p, true, DPOP && !map);
+                    tile_job(ch, p, true, DPOP && !noout);
                     if (!((hard >> p) & 1)) inv_f32(p);
                 } else {
                     tile_job(ch, p, true, false);
@@ -1283,8 +1297,12 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         // fp32: row 16 u + n, columns 4g .. 4g+3 (u = load index)
         const int rowb_v = HDV * (int)sizeof(In);
         const int voff_v = (K::F32 ? n : (16 * (g >> 1) + n)) * rowb_v + (K::F32 ? 4 * g : 8 * (g & 1)) * (int)sizeof(In);
-        const int voff_o = n * rowb_v + 4 * g * (int)sizeof(In);   // output row 16 I + n, columns 4g .. 4g+3
         const long vcol = hrow * dv + vb * BV + 16 * cb;
+        // outputs: out (real rows), or mws [tokens, H, DK] for the virtual rows of a map with outputs
+        In *const obase = vreal ? out + vcol : mws + hrow * DK + (vb * BV - dv) + 16 * cb;
+        const int opitch = vreal ? HDV : HDK;
+        const int rowb_o = opitch * (int)sizeof(In);
+        const int voff_o = n * rowb_o + 4 * g * (int)sizeof(In);   // output row 16 I + n, columns 4g .. 4g+3
 
         // State, transposed, in accumulator layout: Sacc[ct][i] = S[16 cb + n][16 ct + 4g + i].
         // Where it comes from and goes to: S0 / S_final for a whole sequence;
@@ -1295,7 +1313,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         const float *s0row = nullptr;
         float *sfrow = nullptr;
         if (map) {
-            sfrow = seg_map + (((long)head * (nsegs - 1) + seg) * (dv + DK) + row) * DK;
+            sfrow = seg_map + (((long)head * (mout ? nsegs : nsegs - 1) + seg) * (dv + DK) + row) * DK;
         } else if (MAP) {
             if (S0) s0row = S0 + ((long)head * dv + row) * DK;
             sfrow = seg_start + (((long)head * nsegs + 1) * dv + row) * DK;
@@ -1350,7 +1368,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         constexpr bool SPLITJ = K::NBV >= 2 && DPOP && !MAP;
         const bool split = SPLITJ && !add;
         constexpr int NJOB_MAP = K::NBV >= 2 ? K::NOFF : 0, NJOB_FULL = (K::NBV >= 2 && !DPOP) ? K::NPAIR : K::NOFF;
-        const int njob = split ? 2 * K::NOFF : (map ? NJOB_MAP : NJOB_FULL);
+        const int njob = split ? 2 * K::NOFF : (noout ? NJOB_MAP : NJOB_FULL);
         constexpr int NJOB_MAX = SPLITJ ? 2 * K::NOFF : NJOB_FULL;   // NJOB_MAP <= NJOB_FULL
         constexpr int NROUND = (NJOB_MAX + K::NBV - 1) / K::NBV;
         auto y_tiles = [&](CI ch) __attribute__((always_inline)) {
@@ -1362,7 +1380,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                         tile_job(ch, NB + (s >> 1), (s & 1) == 0, (s & 1) != 0);
                     } else {
                         const int p = s < K::NOFF ? NB + s : s - K::NOFF;
-                        tile_job(ch, p, K::NBV >= 2 && p >= NB && !add, !map);
+                        tile_job(ch, p, K::NBV >= 2 && p >= NB && !add, !noout);
                     }
                 }
             }
@@ -1413,13 +1431,13 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 auto rows = [&](int I) __attribute__((always_inline)) {
                     V4 ak[NDK], bq[NDK];
                     if (!add) load_krow(ak, Kr + (16 * I + n) * PK);
-                    if (!map) load_krow(bq, Qr + (16 * I + n) * PK);
+                    if (!noout) load_krow(bq, Qr + (16 * I + n) * PK);
                     if constexpr (VFOLD) {
                         if (!add) R[I] = mma_tiles<K::KD, In, NDK>(R[I], ak, ss);    // V - Kbar S^T
                     } else {
                         R[I] = add ? zero4() : mma_tiles<K::KD, In, NDK>(zero4(), ak, ss);    // [16I + 4g + i][n]
                     }
-                    if (!map) O1[I] = mma_tiles<K::KD, In, NDK>(zero4(), ss, bq);   // [v = 4g + i][16I + n]
+                    if (!noout) O1[I] = mma_tiles<K::KD, In, NDK>(zero4(), ss, bq);   // [v = 4g + i][16I + n]
                 };
                 if (allfast) {
 #pragma unroll
@@ -1492,9 +1510,9 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                 }
 
                 // ---- O^T = (Qbar S^T)^T + E^T P^T, written as O rows (rows past the end dropped)
-                const __amdgpu_buffer_rsrc_t ro = buf_rsrc(out + vcol + t0 * HDV, (unsigned)nval * rowb_v);
+                const __amdgpu_buffer_rsrc_t ro = buf_rsrc(obase + t0 * opitch, (unsigned)nval * rowb_o);
 #pragma unroll
-                for (int I = 0; I < (map ? 0 : NB); ++I) {
+                for (int I = 0; I < (noout ? 0 : NB); ++I) {
                     V4 pb[NB];
 #pragma unroll
                     for (int J = 0; J < NB; ++J)
@@ -1512,7 +1530,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
                     }
                     f32x4 o = VFOLD ? po - O1[I] : O1[I] + po;   // O[16I + n][16cb + 4g + i]
                     if (prep) o = o * sc[K::SC_QI + 16 * I + n];                   // / |q|
-                    buf_store(to_op<In>(o), ro, voff_o, 16 * I * rowb_v);
+                    buf_store(to_op<In>(o), ro, voff_o, 16 * I * rowb_o);
                 }
                 // ---- S^T <- Diag(e^{G_last}) S^T + Ktil^T E (Ktil and the scales of this chunk are
                 //      double-buffered, so this needs no barrier)
@@ -1560,9 +1578,14 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 // stages M_p in LDS (coalesced 16-byte loads, in two halves of DK/2 rows for
 // DK = 128 to stay within the LDS budget) next to the current rows.  fp32
 // throughout.
+//
+// mout (the schedule without a second pass): every segment p >= 1 has a map,
+// at slot p of nsegs per head, and the last one carries the state on to
+// S_final (skipped when S_final is NULL).
 template <int DK>
 __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const float *seg_map,
-                                                          float *seg_start, int dv, int nsegs, int p0)
+                                                          float *seg_start, int dv, int nsegs, int p0,
+                                                          int mout, float *S_final)
 {
     constexpr int CPT = DK / 16;                  // columns per thread
     constexpr int MR = DK > 64 ? DK / 2 : DK;     // rows of M staged at a time
@@ -1581,11 +1604,12 @@ __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const
         float *dst = seg_start + (((long)head * nsegs + p) * dv + row) * DK + c0;
 #pragma unroll
         for (int j = 0; j < CPT; ++j) dst[j] = acc[j];
-        if (p + 1 >= nsegs) break;
+        const bool last = p + 1 >= nsegs;
+        if (last && !(mout && S_final)) break;
         __syncthreads();   // the previous step's reads of srow are done
 #pragma unroll
         for (int j = 0; j < CPT; ++j) srow[r][c0 + j] = acc[j];
-        const float *mp = seg_map + ((long)head * (nsegs - 1) + p) * (dv + DK) * DK;
+        const float *mp = seg_map + ((long)head * (mout ? nsegs : nsegs - 1) + p) * (dv + DK) * DK;
 #pragma unroll
         for (int j = 0; j < CPT; ++j) acc[j] = mp[(long)row * DK + c0 + j];   // N_p
         const float *M = mp + (long)dv * DK;
@@ -1601,6 +1625,122 @@ __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const
                 for (int j = 0; j < CPT; ++j) acc[j] = fmaf(si, sm[i][c0 + j], acc[j]);
             }
         }
+        if (last) {   // mout: the final state
+            float *sf = S_final + ((long)head * dv + row) * DK + c0;
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) sf[j] = acc[j];
+            break;
+        }
+    }
+}
+
+// Output epilogue of the schedule without a second pass.  A segment p >= 1
+// was run from a zero incoming state, with DK virtual rows that start at the
+// identity; since every output is linear in the incoming state, the true
+// output of token t is o_t = o0_t + S_p m_t, where o0_t (in out) is the real
+// rows' output from zero and m_t (in mws, [tokens, H, DK]) the virtual rows'.
+// This adds S_p m_t, with S_p the composed incoming state of segment p, as
+// MFMA products D[v][t] = sum_c S_p[v][c] m_t[c] (bf16 inputs: S_p rounded
+// to bf16, as the chunk kernel rounds the state for its row products).  It streams m and out once
+// (HBM-bound): a workgroup takes 16 tokens per step, wave w a quarter of the
+// head's 16-row value tiles, and the next step's m and out are requested
+// before this step's products.
+// Workgroups: W per (sequence, head, segment), each taking every W-th step of
+// its segment.
+template <typename In, int DK>
+__global__ void __launch_bounds__(256) seg_out_kernel(const In *__restrict__ mws, const float *__restrict__ seg_start,
+                                                      In *__restrict__ out, const int *__restrict__ cu_seqlens,
+                                                      int T, int H, int dv, int C, int nsegs, int lead, int W)
+{
+    constexpr bool F32 = sizeof(In) == 4;
+    // k-chunk per lane and MFMA: 8 contiguous channels (bf16, 16x16x32), else
+    // 4 (bf16 16x16x16 at DK = 16, fp32 16x16x4 over the chunk's 4 elements)
+    constexpr bool K8 = !F32 && DK % 32 == 0;
+    constexpr int KW = K8 ? 8 : 4;               // channels per lane per step
+    constexpr int NKS = DK / (4 * KW);           // k steps
+    typedef In VK __attribute__((ext_vector_type(KW)));
+    constexpr int MT = 2;                        // value tiles per wave, at most
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
+    const int w = blockIdx.x % W, hs = blockIdx.x / W;
+    const int head = hs / (nsegs - 1), seg = 1 + hs % (nsegs - 1);
+    const int seq = head / H, h = head % H;
+    long tok0, len;
+    if (cu_seqlens) {
+        const long a0 = min(max((long)cu_seqlens[seq], 0L), (long)T);
+        const long a1 = min(max((long)cu_seqlens[seq + 1], a0), (long)T);
+        tok0 = a0;
+        len = a1 - a0;
+    } else {
+        tok0 = (long)seq * T;
+        len = T;
+    }
+    long c0, c1;
+    seg_bounds((len + C - 1) / C, nsegs, lead, seg, c0, c1);
+    const long s0 = tok0 + c0 * C, s1 = tok0 + min(c1 * C, len);
+    const int ndv = dv / 16, tpw = (ndv + 3) / 4;
+    const int t0 = wave * tpw, nt = min(ndv, t0 + tpw) - t0;   // this wave's value tiles [t0, t0 + nt)
+    if (s1 <= s0 || nt <= 0) return;
+    // S_p rows 16 tile + n, channels KW (4 s + g) .. + KW - 1 (A operand fragments)
+    const float *sp = seg_start + ((long)head * nsegs + seg) * dv * DK;
+    VK ah[MT][NKS];
+#pragma unroll
+    for (int u = 0; u < MT; ++u)
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            float x[KW];
+#pragma unroll
+            for (int e0 = 0; e0 < KW; e0 += 4) {
+                const f32x4 y = u < nt ? *(const f32x4 *)(sp + (16 * (t0 + u) + n) * DK + KW * (4 * s + g) + e0) : zero4();
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e0 + e] = y[e];
+            }
+#pragma unroll
+            for (int e = 0; e < KW; ++e) ah[u][s][e] = fromf<In>(x[e]);
+        }
+    const int HDK = H * DK, HDV = H * dv;
+    const int es = (int)sizeof(In);
+    // NBK blocks of 16 tokens per step, every load of the step issued before
+    // the first product
+    constexpr int NBK = 4;
+    const long stride = 16L * W;
+    for (long b0 = s0 + 16L * w; b0 < s1; b0 += NBK * stride) {
+        VK bm[NBK][NKS];
+        typename V4T<In>::type ov[NBK][MT];
+        __amdgpu_buffer_rsrc_t ro[NBK];
+#pragma unroll
+        for (int j = 0; j < NBK; ++j) {
+            const long bj = b0 + j * stride;
+            const unsigned nval = bj < s1 ? (unsigned)min(16L, s1 - bj) : 0u;   // 0: an empty descriptor
+            const long bb = bj < s1 ? bj : s0;
+            const __amdgpu_buffer_rsrc_t rm = buf_rsrc(mws + (bb * H + h) * DK, nval * HDK * (unsigned)es);
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) bm[j][s] = buf_load<VK>(rm, (n * HDK + KW * (4 * s + g)) * es, 0);
+            ro[j] = buf_rsrc(out + (bb * H + h) * dv, nval * HDV * (unsigned)es);
+#pragma unroll
+            for (int u = 0; u < MT; ++u)
+                if (u < nt) ov[j][u] = buf_load<typename V4T<In>::type>(ro[j], (n * HDV + 16 * (t0 + u) + 4 * g) * es, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < NBK; ++j)
+#pragma unroll
+            for (int u = 0; u < MT; ++u) {
+                if (u >= nt) break;
+                f32x4 acc = to_f32<In>(ov[j][u]);   // out[b0 + j stride + n][16 tile + 4 g + i]
+#pragma unroll
+                for (int s = 0; s < NKS; ++s) {
+                    if constexpr (K8) {
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u][s], bm[j][s], acc, 0, 0, 0);
+                    } else if constexpr (!F32) {
+                        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, ah[u][s]),
+                                                                        __builtin_bit_cast(i16x4, bm[j][s]), acc, 0, 0, 0);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ah[u][s][e], bm[j][s][e], acc, 0, 0, 0);
+                    }
+                }
+                buf_store(to_op<In>(acc), ro[j], (n * HDV + 16 * (t0 + u) + 4 * g) * es, 0);
+            }
     }
 }
 
@@ -1615,7 +1755,8 @@ hipError_t launch_chunk_grid_v(const ChunkArgs &a, long grid, int xcd_map)
     hipLaunchKernelGGL((chunk_fwd_kernel<In, DK, BV, C, MAP, VAR>), dim3((unsigned)grid), dim3(K::NT), 0,
                        a.stream, (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha, a.beta, a.S0,
                        (In *)a.out, a.S_final, a.cu_seqlens, a.T, a.H, a.dv, xcd_map, a.nsegs < 1 ? 1 : a.nsegs,
-                       a.seg_start, a.seg_map, a.gate, a.add, a.prep, a.nsegs > 1 ? a.lead : 0);
+                       a.seg_start, a.seg_map, a.gate, a.add, a.prep, a.nsegs > 1 ? a.lead : 0, (In *)a.mws,
+                       a.mout);
     return hipGetLastError();
 }
 
@@ -1647,6 +1788,27 @@ hipError_t launch_chunk_t(const ChunkArgs &a)
             const long nvB = (a.dv + DK) / BV;
             const bool lead = a.lead > 0;
             hipError_t e;
+            if (lead && a.mout) {
+                // no second pass: the map launch (segment 0's pass, and every later
+                // segment's map with its outputs from a zero state), the
+                // composition (through S_final), then the output epilogue
+                const long unitsB = nheads * (a.nsegs - 1);
+                e = launch_chunk_grid<In, DK, BV, C, true>(a, nheads * nvA + unitsB * nvB,
+                                                            (nheads % 8 == 0 ? 1 : 0) | (unitsB % 8 == 0 ? 2 : 0));
+                if (e != hipSuccess) return e;
+                const long ncomp = (long)a.nseq * a.H * (a.dv / 16);
+                hipLaunchKernelGGL((seg_compose_kernel<DK>), dim3((unsigned)ncomp), dim3(256), 0, a.stream, a.S0,
+                                   (const float *)a.seg_map, a.seg_start, a.dv, a.nsegs, 1, 1, a.S_final);
+                e = hipGetLastError();
+                if (e != hipSuccess) return e;
+                const long units = nheads * (a.nsegs - 1);
+                // about one resident round of workgroups (four per compute unit)
+                const long W = units >= 4L * a.cus ? 1 : (4L * a.cus) / units;
+                hipLaunchKernelGGL((seg_out_kernel<In, DK>), dim3((unsigned)(units * W)), dim3(256), 0, a.stream,
+                                   (const In *)a.mws, (const float *)a.seg_start, (In *)a.out, a.cu_seqlens, a.T,
+                                   a.H, a.dv, C, a.nsegs, a.lead, (int)W);
+                return hipGetLastError();
+            }
             if (lead) {
                 const long unitsB = nheads * (a.nsegs - 2);
                 e = launch_chunk_grid<In, DK, BV, C, true>(a, nheads * nvA + unitsB * nvB,
@@ -1659,7 +1821,7 @@ hipError_t launch_chunk_t(const ChunkArgs &a)
             const long ncomp = (long)a.nseq * a.H * (a.dv / 16);
             if (ncomp > 0) {
                 hipLaunchKernelGGL((seg_compose_kernel<DK>), dim3((unsigned)ncomp), dim3(256), 0, a.stream, a.S0,
-                                   (const float *)a.seg_map, a.seg_start, a.dv, a.nsegs, lead ? 1 : 0);
+                                   (const float *)a.seg_map, a.seg_start, a.dv, a.nsegs, lead ? 1 : 0, 0, nullptr);
                 e = hipGetLastError();
                 if (e != hipSuccess) return e;
             }

@@ -23,6 +23,11 @@ struct ChunkArgs {
     // variant: gate 0 per channel, 1 scalar per token and head, 2 none;
     // add 1 = additive write; prep 1 = raw q, k and gate pre-activations
     int gate, add, prep;
+    // mout (lead > 0): the schedule without a second pass; mws holds the
+    // virtual rows' outputs [tokens, H, dk] in the input type
+    void *mws;
+    int mout;
+    int cus;   // compute units of the device (launch sizing)
     hipStream_t stream;
 };
 

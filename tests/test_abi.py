@@ -266,8 +266,12 @@ def test_variant_validation(lib):
     def ex(variant, la=A + 192 * MB, nseg=1, ws=None, wsb=0):
         return lib.kda_chunk_fwd_ex(A, A + 64 * MB, A + 128 * MB, la, A + 256 * MB, None, A + 320 * MB,
                                     A + 384 * MB, 2, 100, 4, 64, 64, 64, variant, nseg, ws, wsb, None)
-    assert ex(3) == 2 and ex(16) == 2 and ex(-1) == 2 and ex(8 | 3) == 2
+    assert ex(3) == 2 and ex(32) == 2 and ex(-1) == 2 and ex(8 | 3) == 2 and ex(16 | 3) == 2
     assert "variant" in kda.kda_last_error()
+    # the schedule without a second pass: its own, larger workspace is checked
+    assert ex(16, nseg=2) == 1 and "workspace" in kda.kda_last_error()
+    need = kda.kda_chunk_segmented_workspace_bytes_ex(2, 200, 4, 64, 64, 2, 16, False)
+    assert ex(16, nseg=2, ws=A + 512 * MB, wsb=need - 1) == 2 and "workspace" in kda.kda_last_error()
     assert ex(0, la=None) == 1                  # the per-channel gate needs log_alpha
     assert ex(1, la=None) == 1                  # so does the scalar gate
     assert ex(1, la=A + 192 * MB + 4) != 4      # 4-byte alignment is enough for one gate per token
@@ -278,6 +282,28 @@ def test_variant_validation(lib):
         return lib.kda_recurrent_fwd_ex(A, A + MB, A + 2 * MB, la, A + 4 * MB, A + 8 * MB, A + 64 * MB,
                                         4, 0, 2, 128, 128, variant, None)
     assert rex(3) == 2 and rex(2, la=None) == 0
+    assert rex(16) == 2                         # no schedule bit for the decode entry points
+
+
+def test_one_pass_workspace_bytes(lib):
+    """Workspace of the schedule without a second pass: a map per segment
+    (nseg of them, (dv + dk) dk fp32 each), the incoming states, each rounded
+    up to 256 bytes, then T_total H dk values of the input type; the two-pass
+    schedule's size without the schedule bit; 0 for one segment or bad sizes."""
+    def r256(x):
+        return (x + 255) // 256 * 256
+    for nseq, T, H, dk, dv, nseg, f32 in ((1, 65536, 16, 128, 128, 8, False), (3, 1001, 2, 64, 32, 5, True),
+                                          (2, 7, 1, 16, 128, 2, False)):
+        es = 4 if f32 else 2
+        want = (r256(4 * nseq * H * nseg * (dv + dk) * dk) + r256(4 * nseq * H * nseg * dv * dk)
+                + T * H * dk * es)
+        assert kda.kda_chunk_segmented_workspace_bytes_ex(nseq, T, H, dk, dv, nseg, 16, f32) == want
+        assert kda.kda_chunk_segmented_workspace_bytes_ex(nseq, T, H, dk, dv, nseg, 0, f32) == \
+            kda.kda_chunk_segmented_workspace_bytes(nseq, H, dk, dv, nseg)
+    assert kda.kda_chunk_segmented_workspace_bytes_ex(1, 100, 2, 64, 64, 1, 16, False) == 0
+    assert kda.kda_chunk_segmented_workspace_bytes_ex(1, 100, 2, 48, 64, 4, 16, False) == 0
+    assert kda.kda_chunk_segmented_workspace_bytes_ex(1, 100, 2, 64, 64, 4, 32, False) == 0
+    assert kda.variant(schedule="one-pass") == 16 and kda.variant("none", "add", schedule="one-pass") == 22
 
 
 def test_raw_input_variant_validation(lib):

@@ -607,6 +607,90 @@ def test_segmented_is_deterministic(dev):
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
+# ---------------------------------------------------------------- segmented schedule without a second pass
+@pytest.mark.parametrize("B,T,H,dk,dv,C,dtype,nseg,with_s0", SEG_SHAPES)
+def test_one_pass_matches_oracle(dev, B, T, H, dk, dv, C, dtype, nseg, with_s0):
+    """The schedule without a second pass (map launch with every later
+    segment's outputs from a zero state, composition through S_final, output
+    epilogue) against the oracle, and against the two-pass schedule."""
+    note(f"case one-pass B{B} T{T} H{H} dk{dk} dv{dv} C{C} {dtype} segments={nseg} S0={with_s0}")
+    p = kda_synth.prefill(B, T, H, dk, dv, dtype=dtype, s0_sigma=0.1 if with_s0 else None,
+                          seed=2000 + T + dk + dv + nseg, device=dev)
+    out, sf = kda.chunk_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S0=p.S0, C=C, segments=nseg, schedule="one-pass")
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_dense(p)
+    assert_close("one-pass", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+    o2, s2 = gpu_chunk(p, C, segments=nseg)
+    assert_close("one-pass vs two-pass", f64(out), f64(sf), f64(o2), f64(s2), TOL[dtype])
+
+
+def test_one_pass_varlen_variants_and_deep_decay(dev):
+    """Packed sequences (empty and one-token ones included), every variant,
+    raw inputs and deep decay through the schedule without a second pass."""
+    lengths = [300, 64, 1, 0, 517, 129]
+    for dtype in ("bf16", "f32"):
+        note(f"case one-pass varlen lengths {lengths} H2 d64 {dtype} C32, 3 segments per sequence")
+        p = kda_synth.prefill_varlen(lengths, 2, 64, 64, dtype=dtype, s0_sigma=0.1, seed=45, device=dev)
+        out, sf = kda.chunk_fwd_varlen(p.q, p.k, p.v, p.log_alpha, p.beta, p.cu_seqlens, S0=p.S0, C=32,
+                                       segments=3, schedule="one-pass")
+        torch.cuda.synchronize()
+        o_ref, s_ref = oracle.forward_varlen(f64(p.q), f64(p.k), f64(p.v), f64(p.log_alpha), f64(p.beta),
+                                             np.array(p.cu_host), S0=f64(p.S0))
+        assert_close(f"one-pass varlen {dtype}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+    for gate, write in VARIANTS:
+        for dtype, C in (("bf16", 64), ("f32", 32)):
+            note(f"case one-pass variant {gate}/{write}: B1 T700 H2 d64 {dtype} C{C}, 4 segments")
+            p = kda_synth.prefill(1, 700, 2, 64, 64, dtype=dtype, s0_sigma=0.1, seed=61, device=dev)
+            la, la_full = variant_inputs(p, gate)
+            o_ref, s_ref = oracle.forward(f64(p.q), f64(p.k), f64(p.v), f64(la_full), f64(p.beta), S0=f64(p.S0),
+                                          write=write)
+            out, sf = kda.chunk_fwd(p.q, p.k, p.v, la, p.beta, S0=p.S0, C=C, segments=4, gate=gate, write=write,
+                                    schedule="one-pass")
+            torch.cuda.synchronize()
+            assert_close(f"one-pass {gate}/{write} {dtype}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+    for gate in ("channel", "scalar"):
+        note(f"case one-pass raw inputs gate={gate}: B1 T600 H2 d128 bf16 C64, 3 segments")
+        p = kda_synth.prefill_raw(1, 600, 2, 128, 128, dtype="bf16", s0_sigma=0.1, seed=63, device=dev)
+        o_ref, s_ref = oracle_raw(p, gate, "delta")
+        out, sf = kda.chunk_fwd(p.q, p.k, p.v, raw_gate_arg(p, gate), p.beta, S0=p.S0, C=64, segments=3,
+                                gate=gate, raw=True, schedule="one-pass")
+        torch.cuda.synchronize()
+        assert_close(f"one-pass raw {gate}", f64(out), f64(sf), o_ref, s_ref, TOL["bf16"])
+    for dtype, dk, C in (("bf16", 128, 64), ("f32", 64, 32)):
+        note(f"case one-pass deep decay: B1 T600 H2 dk{dk} {dtype} C{C}, 5 segments")
+        p = kda_synth.prefill(1, 600, 2, dk, 64, dtype=dtype, s0_sigma=0.1, seed=135, device=dev)
+        deep_gates(p.log_alpha, "clear")
+        p.log_alpha[:, 300:420, 1, : dk // 4] = -30.0
+        out, sf = kda.chunk_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S0=p.S0, C=C, segments=5, schedule="one-pass")
+        torch.cuda.synchronize()
+        o_ref, s_ref = oracle_dense(p)
+        assert_close(f"one-pass deep {dtype}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+
+
+def test_one_pass_in_place_no_final_state_and_determinism(dev):
+    note("case one-pass in place: S_final == S0, S_final not requested, two runs bitwise")
+    B, T, H, dk, dv, C, nseg = 1, 800, 2, 128, 128, 64, 3
+    p = kda_synth.prefill(B, T, H, dk, dv, dtype="bf16", s0_sigma=0.1, seed=43, device=dev)
+    o_ref, s_ref = oracle_dense(p)
+    var = kda.variant(schedule="one-pass")
+    nbytes = kda.kda_chunk_segmented_workspace_bytes_ex(B, B * T, H, dk, dv, nseg, var, False)
+    assert nbytes > kda.kda_chunk_segmented_workspace_bytes(B, H, dk, dv, nseg)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    S = p.S0.clone()
+    out = torch.empty_like(p.v)
+    kda.kda_chunk_fwd_ex(p.q, p.k, p.v, p.log_alpha, p.beta, S, out, S, B, T, H, dk, dv, C, var, nseg, ws, nbytes)
+    torch.cuda.synchronize()
+    assert_close("one-pass in-place", f64(out), f64(S), o_ref, s_ref, TOL["bf16"])
+    out2 = torch.empty_like(p.v)
+    kda.kda_chunk_fwd_ex(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out2, None, B, T, H, dk, dv, C, var, nseg, ws,
+                         nbytes)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out)
+    with pytest.raises(kda.KdaError):   # one byte short of the workspace it needs
+        kda.kda_chunk_fwd_ex(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out2, None, B, T, H, dk, dv, C, var, nseg,
+                             ws, nbytes - 1)
+
+
 # ---------------------------------------------------------------- variants (gate, write)
 VARIANTS = [("scalar", "delta"), ("none", "delta"), ("channel", "add"), ("scalar", "add"), ("none", "add")]
 
@@ -962,13 +1046,16 @@ def test_long_workload_sampled(dev):
     p = kda_synth.workload("long", device=dev)
     pairs = [(0, 0), (0, 9), (0, 15)]
     o_ref, s_ref = sampled(p, pairs)
-    for segments in ("auto", 1):
-        note(f"case long workload: B1 H16 T65536 d128 bf16 C64, S0 in (3 sampled heads), segments={segments}")
-        out, sf = gpu_chunk(p, w["C"], segments=segments)
+    for segments, schedule in (("auto", "auto"), ("auto", "two-pass"), (1, "auto")):
+        note(f"case long workload: B1 H16 T65536 d128 bf16 C64, S0 in (3 sampled heads), segments={segments} "
+             f"schedule={schedule}")
+        out, sf = kda.chunk_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, S0=p.S0, C=w["C"], segments=segments,
+                                schedule=schedule)
+        torch.cuda.synchronize()
         assert torch.isfinite(out.float()).all() and torch.isfinite(sf).all()
         o_gpu = np.stack([f64(out[b, :, h]) for b, h in pairs])[:, :, None]
         s_gpu = np.stack([f64(sf[b, h]) for b, h in pairs])[:, None]
-        assert_close(f"long sampled ({segments})", o_gpu, s_gpu, o_ref, s_ref, TOL["bf16"])
+        assert_close(f"long sampled ({segments}, {schedule})", o_gpu, s_gpu, o_ref, s_ref, TOL["bf16"])
         del out, sf
 
 
