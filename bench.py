@@ -283,27 +283,41 @@ def bench_long(args, torch, kda, kda_synth, stream, steps=3):
     sf = torch.empty((B, H, dv, dk), dtype=torch.float32, device="cuda")
     h = stream.cuda_stream
 
-    # segment-parallel schedule with the library's segment count (workspace
-    # allocated before the timed region), and the single pass for reference
-    nseg = kda.kda_chunk_auto_segments(B, T, H, dk, dv, C, 0)
-    wsb = kda.kda_chunk_segmented_workspace_bytes(B, H, dk, dv, nseg)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    # the library's schedule and segment count (kda_chunk_auto_schedule,
+    # kda_chunk_auto_segments_ex; workspace allocated before the timed region),
+    # the other segmented schedule, and the single pass, for reference
+    def seg_launcher(sched):
+        nseg = kda.kda_chunk_auto_segments_ex(B, T, H, dk, dv, C, 0, sched)
+        wsb = kda.kda_chunk_segmented_workspace_bytes_ex(B, B * T, H, dk, dv, nseg, sched, False)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
 
-    def launch():
-        kda.kda_chunk_fwd_segmented(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out, sf, B, T, H, dk, dv, C, nseg,
-                                    ws, wsb, h)
+        def launch():
+            kda.kda_chunk_fwd_ex(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out, sf, B, T, H, dk, dv, C, sched, nseg,
+                                 ws, wsb, h)
+        return nseg, ws, launch
 
     def launch_single():
         kda.kda_chunk_fwd(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out, sf, B, T, H, dk, dv, C, h)
 
+    sched = kda.kda_chunk_auto_schedule(B, T, H, dk, dv, C, 0)
+    nseg, ws, launch = seg_launcher(sched)
     wall, kms = time_launches(launch, stream, steps, 1, torch)
+    del ws
+    other = kda.SCHED_MAP_OUTPUTS - sched
+    nseg2, ws, launch2 = seg_launcher(other)
+    _, kms2 = time_launches(launch2, stream, steps, 1, torch)
+    del ws
     _, kms1 = time_launches(launch_single, stream, 2, 1, torch)
     nbytes = prefill_bytes(B * T * H, dk, dv, B * H, s0=True, sfinal=True)
-    del p, out, sf, ws
+    del p, out, sf
+    names = {0: "two-pass (map launch with the lead segment's whole pass, composition, second pass)",
+             kda.SCHED_MAP_OUTPUTS: "one-pass (map launch with the lead segment's whole pass and every later "
+                                    "segment's outputs from a zero state, composition, output epilogue)"}
     return dict(workload="long prefill: B=1 H=16 T=65536 dk=dv=128 bf16 C=64, S0 in, S_final out",
-                schedule=f"segment-parallel, {nseg} segments per sequence (map launch with the lead segment's whole pass, "
-                         f"composition, second pass)",
-                tokens_per_s=B * T * steps / wall, kernel_ms=kms, single_pass_kernel_ms=kms1,
+                schedule=f"segment-parallel, {nseg} segments per sequence, {names[sched]}",
+                tokens_per_s=B * T * steps / wall, kernel_ms=kms,
+                other_schedule=dict(schedule=names[other].split(" (")[0], segments=nseg2, kernel_ms=kms2),
+                single_pass_kernel_ms=kms1,
                 hbm_gbs=round(nbytes / (kms * 1e-3) / 1e9, 1),
                 hbm_frac=round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
 
@@ -376,19 +390,22 @@ def bench_small(args, torch, kda, kda_synth, stream, launches=200):
         res[name] = dict(workload=f"{name}: B={B} H={H} T={T} dk=dv={dk} {w['dtype']} C={C}",
                          kernel_us=round(kms * 1e3, 2), us_per_launch=round(wall * 1e6 / launches, 2),
                          tokens_per_s=round(B * T * launches / wall, 1))
-        # the library's own schedule choice (kda_chunk_auto_segments), through
-        # the segmented entry point with a workspace allocated once
-        nseg = kda.kda_chunk_auto_segments(B, T, H, dk, dv, C, w["dtype"] == "f32")
+        # the library's own schedule choice (kda_chunk_auto_schedule and
+        # kda_chunk_auto_segments_ex), with a workspace allocated once
+        f32 = w["dtype"] == "f32"
+        sched = kda.kda_chunk_auto_schedule(B, T, H, dk, dv, C, f32)
+        nseg = kda.kda_chunk_auto_segments_ex(B, T, H, dk, dv, C, f32, sched)
         if nseg > 1:
-            wsb = kda.kda_chunk_segmented_workspace_bytes(B, H, dk, dv, nseg)
+            wsb = kda.kda_chunk_segmented_workspace_bytes_ex(B, B * T, H, dk, dv, nseg, sched, f32)
             ws = torch.empty(wsb // 4 + 64, dtype=torch.float32, device="cuda")
-            seg = kda.kda_chunk_fwd_segmented_f32 if w["dtype"] == "f32" else kda.kda_chunk_fwd_segmented
+            seg = kda.kda_chunk_fwd_ex_f32 if f32 else kda.kda_chunk_fwd_ex
 
             def launch_seg():
-                seg(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out, sf, B, T, H, dk, dv, C, nseg, ws, wsb, h)
+                seg(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out, sf, B, T, H, dk, dv, C, sched, nseg, ws, wsb, h)
 
             wall, kms = time_launches(launch_seg, stream, launches, 20, torch)
-            res[name]["auto_schedule"] = dict(segments=nseg, kernel_us=round(kms * 1e3, 2),
+            res[name]["auto_schedule"] = dict(segments=nseg, schedule="one-pass" if sched else "two-pass",
+                                              kernel_us=round(kms * 1e3, 2),
                                               us_per_launch=round(wall * 1e6 / launches, 2),
                                               tokens_per_s=round(B * T * launches / wall, 1))
             del ws

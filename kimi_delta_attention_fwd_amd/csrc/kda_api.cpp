@@ -244,7 +244,7 @@ int seg_lead_mout(long nheads, int dk, int dv, int bv, int nseg, int cus)
 // first chunk's operands, the incoming state and the final store).  With s
 // segments the map launch takes max(L0 + 1, 0.85 rounds (L + 1)) (the
 // lead segment's whole pass beside the maps, a map chunk being about 0.85 of a
-// full one), the serial composition 0.6 (dk / 64)^1.5 steps per segment, the
+// full one), the serial composition 0.3 (dk / 64)^1.5 steps per segment, the
 // second pass ceil(g3 / CUs) (L + 1) over segments 1 .. s - 1, and the two
 // extra launches about one step; rounds as in map_launch_rounds.  Fitted to
 // measured runs: 1 segment for B=4 H=32 T=8192, 9 for B=1 H=16 T=65536
@@ -253,8 +253,8 @@ int seg_lead_mout(long nheads, int dk, int dv, int bv, int nseg, int cus)
 // Schedule without a second pass (mout): the map launch takes max(L0 + 1,
 // rounds (L + 1)) steps (its map chunks, which also form the outputs, cost
 // about a full chunk), the composition as above, and the epilogue streams m
-// and out once: about one step per 13 MB (fitted to B=1 H=16 T=65536 d=128,
-// 8 segments: 1.22 ms, and 7 and 9 segments within 5%).
+// and out once: about one step per 16 MB (fitted to B=1 H=16 T=65536 d=128,
+// 8 segments: 1.15 ms, and 7 and 9 segments within 5%).
 double auto_cost(bool f32, int B, int T, int H, int dk, int dv, int C, bool mout, int &best_s)
 {
     best_s = 1;
@@ -277,15 +277,15 @@ double auto_cost(bool f32, int B, int T, int H, int dk, int dv, int C, bool mout
             const long L0 = nch - (s - 1) * L > 0 ? nch - (s - 1) * L : 0;
             const long g1 = nheads * ((s - 1) * nvB + nvA);
             const double map = (double)map_launch_rounds(g1, nheads * nvA, cus) * (double)(L + 1);
-            const double epi = (double)B * (double)T * (double)H * (double)(dk + 2 * dv) * (f32 ? 4.0 : 2.0) / 13e6;
-            cost = (map > (double)(L0 + 1) ? map : (double)(L0 + 1)) + 0.6 * std::pow(dk / 64.0, 1.5) * s + epi + 1.0;
+            const double epi = (double)B * (double)T * (double)H * (double)(dk + 2 * dv) * (f32 ? 4.0 : 2.0) / 16e6;
+            cost = (map > (double)(L0 + 1) ? map : (double)(L0 + 1)) + 0.3 * std::pow(dk / 64.0, 1.5) * s + epi + 1.0;
         } else {
             const int lead = seg_lead(nheads, dk, dv, bv, s, cus);
             const long L = (10 * nch + 10 * (s - 1) + lead - 1) / (10 * (s - 1) + lead);
             const long L0 = nch - (s - 1) * L > 0 ? nch - (s - 1) * L : 0;
             const long g1 = nheads * ((s - 2) * nvB + nvA), g3 = nheads * (s - 1) * nvA;
             const double map = 0.85 * (double)map_launch_rounds(g1, nheads * nvA, cus) * (double)(L + 1);
-            cost = (map > (double)(L0 + 1) ? map : (double)(L0 + 1)) + 0.6 * std::pow(dk / 64.0, 1.5) * s +
+            cost = (map > (double)(L0 + 1) ? map : (double)(L0 + 1)) + 0.3 * std::pow(dk / 64.0, 1.5) * s +
                    (double)((g3 + cus - 1) / cus) * (double)(L + 1) + 1.0;
         }
         if (s == 1 || cost < best) {

@@ -1573,11 +1573,13 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 
 // Incoming states of the segments of every (sequence, head): slot 0 holds S0
 // (zero when absent), slot p + 1 = slot p M_p + N_p, row by row, with (M_p,
-// N_p) the map of segment p from the MAP pass.  One workgroup per 16 state rows
-// of a head; thread (r, cg) keeps columns cg DK/16 .. of row r.  Each step
-// stages M_p in LDS (coalesced 16-byte loads, in two halves of DK/2 rows for
-// DK = 128 to stay within the LDS budget) next to the current rows.  fp32
-// throughout.
+// N_p) the map of segment p from the MAP pass.  fp32 throughout, the products
+// as fp32 MFMAs: one workgroup per 16 state rows s of a head, and per step
+// D = M_p^T s^T + N_p^T, so that wave w's accumulator tiles (key-channel
+// tiles w, w + 4, ...) hold the new rows in exactly the layout the next
+// step's products read them in.  The rows go through LDS once per step (every
+// wave needs all of them); M_p is staged in LDS with coalesced 16-byte loads,
+// and the next map's loads are issued before this step's products.
 //
 // mout (the schedule without a second pass): every segment p >= 1 has a map,
 // at slot p of nsegs per head, and the last one carries the state on to
@@ -1587,49 +1589,91 @@ __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const
                                                           float *seg_start, int dv, int nsegs, int p0,
                                                           int mout, float *S_final)
 {
-    constexpr int CPT = DK / 16;                  // columns per thread
-    constexpr int MR = DK > 64 ? DK / 2 : DK;     // rows of M staged at a time
-    __shared__ __attribute__((aligned(16))) float srow[16][DK + 4];
-    __shared__ __attribute__((aligned(16))) float sm[MR][DK];
+    constexpr int NCT = DK / 16;                 // key-channel tiles
+    constexpr int TPW = (NCT + 3) / 4;           // tiles per wave, at most
+    constexpr int PM = DK + 4;                   // LDS row pitch (floats)
+    constexpr int NLD = DK * DK / (4 * 256);     // 16-byte loads of a map per thread (DK >= 32)
+    constexpr int NLDX = NLD > 0 ? NLD : 1;
+    __shared__ __attribute__((aligned(16))) float sM[DK * PM];
+    __shared__ __attribute__((aligned(16))) float sS[16 * PM];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
     const int nrb = dv / 16;
     const int head = blockIdx.x / nrb, rb = blockIdx.x % nrb;
-    const int tid = threadIdx.x, r = tid >> 4, c0 = (tid & 15) * CPT;
-    const int row = rb * 16 + r;
-    float acc[CPT];
+    const int mstride = mout ? nsegs : nsegs - 1;
+    // the incoming rows 16 rb .. 16 rb + 15 of slot p0
+    for (int e = 4 * tid; e < 16 * DK; e += 4 * 256) {
+        const int r = e / DK, c = e % DK;
+        const long row = (long)head * dv + 16 * rb + r;
+        f32x4 x = zero4();
+        if (p0 > 0) x = *(const f32x4 *)(seg_start + (((long)head * nsegs + p0) * dv + 16 * rb + r) * DK + c);
+        else if (S0) x = *(const f32x4 *)(S0 + row * DK + c);
+        *(f32x4 *)(sS + r * PM + c) = x;
+    }
+    // map loads: element 4 (tid + 256 j) of M, row-major [DK][DK]
+    f32x4 ml[NLDX];
+    auto load_map = [&](int p) __attribute__((always_inline)) {
+        const float *M = seg_map + ((long)head * mstride + p) * (dv + DK) * DK + (long)dv * DK;
+        if constexpr (NLD > 0) {
 #pragma unroll
-    for (int j = 0; j < CPT; ++j)
-        acc[j] = p0 > 0 ? seg_start[(((long)head * nsegs + p0) * dv + row) * DK + c0 + j]
-                        : (S0 ? S0[((long)head * dv + row) * DK + c0 + j] : 0.f);
+            for (int j = 0; j < NLD; ++j) ml[j] = *(const f32x4 *)(M + 4 * (tid + 256 * j));
+        } else {
+            if (4 * tid < DK * DK) ml[0] = *(const f32x4 *)(M + 4 * tid);
+        }
+    };
+    auto store_map = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < NLDX; ++j) {
+            const int e = 4 * (tid + 256 * j);
+            if (e < DK * DK) *(f32x4 *)(sM + (e / DK) * PM + e % DK) = ml[j];
+        }
+    };
+    const bool more = p0 + 1 < nsegs || (mout && S_final);
+    if (more) load_map(p0);
     for (int p = p0;; ++p) {
-        float *dst = seg_start + (((long)head * nsegs + p) * dv + row) * DK + c0;
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) dst[j] = acc[j];
+        __syncthreads();   // the rows of slot p are in sS
+        // slot p out
+        for (int e = 4 * tid; e < 16 * DK; e += 4 * 256) {
+            const int r = e / DK, c = e % DK;
+            *(f32x4 *)(seg_start + (((long)head * nsegs + p) * dv + 16 * rb + r) * DK + c) = *(const f32x4 *)(sS + r * PM + c);
+        }
         const bool last = p + 1 >= nsegs;
         if (last && !(mout && S_final)) break;
-        __syncthreads();   // the previous step's reads of srow are done
+        store_map();        // M_p (the threads' own loads)
+        const bool next = !last && (p + 2 < nsegs || (mout && S_final));
+        if (next) load_map(p + 1);   // in flight across this step
+        __syncthreads();
+        const float *Np = seg_map + ((long)head * mstride + p) * (dv + DK) * DK + (long)(16 * rb) * DK;
+        f32x4 acc[TPW];
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) srow[r][c0 + j] = acc[j];
-        const float *mp = seg_map + ((long)head * (mout ? nsegs : nsegs - 1) + p) * (dv + DK) * DK;
+        for (int u = 0; u < TPW; ++u) {
+            const int ct = wave + 4 * u;
+            if (ct >= NCT) break;
+            // D^T tile: lane (n, g) accumulates s_new[n][16 ct + 4 g + i]
+            acc[u] = *(const f32x4 *)(Np + (long)n * DK + 16 * ct + 4 * g);
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) acc[j] = mp[(long)row * DK + c0 + j];   // N_p
-        const float *M = mp + (long)dv * DK;
-        for (int h0 = 0; h0 < DK; h0 += MR) {
-            if (h0 > 0) __syncthreads();   // everyone is done with the previous half of M
-            for (int e = tid * 4; e < MR * DK; e += 256 * 4)
-                *(f32x4 *)(&sm[0][0] + e) = *(const f32x4 *)(M + (long)h0 * DK + e);
-            __syncthreads();
-#pragma unroll 8
-            for (int i = 0; i < MR; ++i) {
-                const float si = srow[r][h0 + i];
+            for (int t = 0; t < NCT; ++t) {
+                const f32x4 b = *(const f32x4 *)(sS + n * PM + 16 * t + 4 * g);   // s[n][16 t + 4 g + i]
 #pragma unroll
-                for (int j = 0; j < CPT; ++j) acc[j] = fmaf(si, sm[i][c0 + j], acc[j]);
+                for (int i = 0; i < 4; ++i)
+                    acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[(16 * t + 4 * g + i) * PM + 16 * ct + n], b[i],
+                                                                  acc[u], 0, 0, 0);
             }
         }
+        __syncthreads();   // every wave is done reading sS and sM
         if (last) {   // mout: the final state
-            float *sf = S_final + ((long)head * dv + row) * DK + c0;
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) sf[j] = acc[j];
+            for (int u = 0; u < TPW; ++u) {
+                const int ct = wave + 4 * u;
+                if (ct >= NCT) break;
+                *(f32x4 *)(S_final + ((long)head * dv + 16 * rb + n) * DK + 16 * ct + 4 * g) = acc[u];
+            }
             break;
+        }
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int ct = wave + 4 * u;
+            if (ct >= NCT) break;
+            *(f32x4 *)(sS + n * PM + 16 * ct + 4 * g) = acc[u];
         }
     }
 }
@@ -1641,12 +1685,12 @@ __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const
 // rows' output from zero and m_t (in mws, [tokens, H, DK]) the virtual rows'.
 // This adds S_p m_t, with S_p the composed incoming state of segment p, as
 // MFMA products D[v][t] = sum_c S_p[v][c] m_t[c] (bf16 inputs: S_p rounded
-// to bf16, as the chunk kernel rounds the state for its row products).  It streams m and out once
-// (HBM-bound): a workgroup takes 16 tokens per step, wave w a quarter of the
-// head's 16-row value tiles, and the next step's m and out are requested
-// before this step's products.
-// Workgroups: W per (sequence, head, segment), each taking every W-th step of
-// its segment.
+// to bf16, as the chunk kernel rounds the state for its row products).  It
+// streams m and out once (HBM-bound).  A workgroup stages S_p in LDS in the
+// operand type; each wave takes blocks of 16 tokens with every value tile,
+// NBK blocks per step with all their loads issued before the first product.
+// Workgroups: W per (sequence, head, segment); a segment's blocks are dealt
+// round-robin to its 4 W waves.
 template <typename In, int DK>
 __global__ void __launch_bounds__(256) seg_out_kernel(const In *__restrict__ mws, const float *__restrict__ seg_start,
                                                       In *__restrict__ out, const int *__restrict__ cu_seqlens,
@@ -1658,8 +1702,11 @@ __global__ void __launch_bounds__(256) seg_out_kernel(const In *__restrict__ mws
     constexpr bool K8 = !F32 && DK % 32 == 0;
     constexpr int KW = K8 ? 8 : 4;               // channels per lane per step
     constexpr int NKS = DK / (4 * KW);           // k steps
+    constexpr int PS = DK + 16 / (int)sizeof(In);   // LDS row pitch (elements)
+    constexpr int NBK = 2;
     typedef In VK __attribute__((ext_vector_type(KW)));
-    constexpr int MT = 2;                        // value tiles per wave, at most
+    typedef typename V4T<In>::type V4;
+    __shared__ __attribute__((aligned(16))) In sS[128 * PS];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
     const int w = blockIdx.x % W, hs = blockIdx.x / W;
     const int head = hs / (nsegs - 1), seg = 1 + hs % (nsegs - 1);
@@ -1677,35 +1724,23 @@ __global__ void __launch_bounds__(256) seg_out_kernel(const In *__restrict__ mws
     long c0, c1;
     seg_bounds((len + C - 1) / C, nsegs, lead, seg, c0, c1);
     const long s0 = tok0 + c0 * C, s1 = tok0 + min(c1 * C, len);
-    const int ndv = dv / 16, tpw = (ndv + 3) / 4;
-    const int t0 = wave * tpw, nt = min(ndv, t0 + tpw) - t0;   // this wave's value tiles [t0, t0 + nt)
-    if (s1 <= s0 || nt <= 0) return;
-    // S_p rows 16 tile + n, channels KW (4 s + g) .. + KW - 1 (A operand fragments)
+    if (s1 <= s0) return;
+    const int ndv = dv / 16;
+    // S_p [dv][DK] fp32 -> LDS in the operand type
     const float *sp = seg_start + ((long)head * nsegs + seg) * dv * DK;
-    VK ah[MT][NKS];
+    for (int e = 4 * (int)threadIdx.x; e < dv * DK; e += 4 * 256) {
+        const f32x4 x = *(const f32x4 *)(sp + e);
+        const int r = e / DK, c = e % DK;
 #pragma unroll
-    for (int u = 0; u < MT; ++u)
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-            float x[KW];
-#pragma unroll
-            for (int e0 = 0; e0 < KW; e0 += 4) {
-                const f32x4 y = u < nt ? *(const f32x4 *)(sp + (16 * (t0 + u) + n) * DK + KW * (4 * s + g) + e0) : zero4();
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[e0 + e] = y[e];
-            }
-#pragma unroll
-            for (int e = 0; e < KW; ++e) ah[u][s][e] = fromf<In>(x[e]);
-        }
+        for (int i = 0; i < 4; ++i) sS[r * PS + c + i] = fromf<In>(x[i]);
+    }
+    __syncthreads();
     const int HDK = H * DK, HDV = H * dv;
     const int es = (int)sizeof(In);
-    // NBK blocks of 16 tokens per step, every load of the step issued before
-    // the first product
-    constexpr int NBK = 4;
-    const long stride = 16L * W;
-    for (long b0 = s0 + 16L * w; b0 < s1; b0 += NBK * stride) {
+    const long stride = 16L * 4 * W;
+    for (long b0 = s0 + 16L * (4 * w + wave); b0 < s1; b0 += NBK * stride) {
         VK bm[NBK][NKS];
-        typename V4T<In>::type ov[NBK][MT];
+        V4 ov[NBK][8];
         __amdgpu_buffer_rsrc_t ro[NBK];
 #pragma unroll
         for (int j = 0; j < NBK; ++j) {
@@ -1717,29 +1752,29 @@ __global__ void __launch_bounds__(256) seg_out_kernel(const In *__restrict__ mws
             for (int s = 0; s < NKS; ++s) bm[j][s] = buf_load<VK>(rm, (n * HDK + KW * (4 * s + g)) * es, 0);
             ro[j] = buf_rsrc(out + (bb * H + h) * dv, nval * HDV * (unsigned)es);
 #pragma unroll
-            for (int u = 0; u < MT; ++u)
-                if (u < nt) ov[j][u] = buf_load<typename V4T<In>::type>(ro[j], (n * HDV + 16 * (t0 + u) + 4 * g) * es, 0);
+            for (int u = 0; u < 8; ++u)
+                if (u < ndv) ov[j][u] = buf_load<V4>(ro[j], (n * HDV + 16 * u + 4 * g) * es, 0);
         }
 #pragma unroll
         for (int j = 0; j < NBK; ++j)
 #pragma unroll
-            for (int u = 0; u < MT; ++u) {
-                if (u >= nt) break;
-                f32x4 acc = to_f32<In>(ov[j][u]);   // out[b0 + j stride + n][16 tile + 4 g + i]
+            for (int u = 0; u < 8; ++u) {
+                if (u >= ndv) break;
+                f32x4 acc = to_f32<In>(ov[j][u]);   // out[b0 + j stride + n][16 u + 4 g + i]
 #pragma unroll
                 for (int s = 0; s < NKS; ++s) {
+                    const VK a = *(const VK *)(sS + (16 * u + n) * PS + KW * (4 * s + g));
                     if constexpr (K8) {
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u][s], bm[j][s], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bm[j][s], acc, 0, 0, 0);
                     } else if constexpr (!F32) {
-                        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, ah[u][s]),
+                        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
                                                                         __builtin_bit_cast(i16x4, bm[j][s]), acc, 0, 0, 0);
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ah[u][s][e], bm[j][s][e], acc, 0, 0, 0);
+                        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], bm[j][s][e], acc, 0, 0, 0);
                     }
                 }
-                buf_store(to_op<In>(acc), ro[j], (n * HDV + 16 * (t0 + u) + 4 * g) * es, 0);
+                buf_store(to_op<In>(acc), ro[j], (n * HDV + 16 * u + 4 * g) * es, 0);
             }
     }
 }
@@ -1802,8 +1837,8 @@ hipError_t launch_chunk_t(const ChunkArgs &a)
                 e = hipGetLastError();
                 if (e != hipSuccess) return e;
                 const long units = nheads * (a.nsegs - 1);
-                // about one resident round of workgroups (four per compute unit)
-                const long W = units >= 4L * a.cus ? 1 : (4L * a.cus) / units;
+                // about one resident round of workgroups (two per compute unit)
+                const long W = units >= 2L * a.cus ? 1 : (2L * a.cus) / units;
                 hipLaunchKernelGGL((seg_out_kernel<In, DK>), dim3((unsigned)(units * W)), dim3(256), 0, a.stream,
                                    (const In *)a.mws, (const float *)a.seg_start, (In *)a.out, a.cu_seqlens, a.T,
                                    a.H, a.dv, C, a.nsegs, a.lead, (int)W);
