@@ -16,7 +16,8 @@ Extra fields measure the other entry points on their own workloads:
   fused_prep    mid sizes from raw q, k and bf16 gate pre-activations, against
                 separate preparation passes feeding the plain kernel (ms)
   long_context  B=1, H=16, T=65536 with an initial state (tokens/s)
-  varlen        8 packed sequences of U[2048, 16384] tokens x 16 heads (tokens/s)
+  varlen        8 packed sequences of U[2048, 16384] tokens x 16 heads (tokens/s), with
+                the library's device-side split of the longest sequences
   small_configs the tiny fp32 and small bf16 prefills, bound by launch latency
                 (microseconds per launch and tokens/s, no roofline)
 
@@ -332,15 +333,29 @@ def bench_varlen(args, torch, kda, kda_synth, stream, steps=3):
     sf = torch.empty((N, H, dv, dk), dtype=torch.float32, device="cuda")
     h = stream.cuda_stream
 
+    # the library's schedule for packed sequences (the one-pass schedule with
+    # the device-side split, nseg = 0; workspace allocated before the timed
+    # region), and the single pass for reference
+    sched = kda.SCHED_MAP_OUTPUTS
+    wsb = kda.kda_chunk_segmented_workspace_bytes_ex(N, Tt, H, dk, dv, 0, sched, False)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+
     def launch():
+        kda.kda_chunk_fwd_varlen_ex(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out, sf, p.cu_seqlens, N, Tt, H, dk,
+                                    dv, C, sched, 0, ws, wsb, h)
+
+    def launch_single():
         kda.kda_chunk_fwd_varlen(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, out, sf, p.cu_seqlens, N, Tt, H, dk,
                                  dv, C, h)
 
     wall, kms = time_launches(launch, stream, steps, 1, torch)
+    _, kms1 = time_launches(launch_single, stream, steps, 1, torch)
     nbytes = prefill_bytes(Tt * H, dk, dv, N * H, s0=True, sfinal=True)
-    del p, out, sf
+    del p, out, sf, ws
     return dict(workload=f"varlen prefill: {N} packed sequences (T_total={Tt}) x H=16 dk=dv=128 bf16 C=64",
-                tokens_per_s=Tt * steps / wall, kernel_ms=kms,
+                schedule="one-pass with the device-side split (the sequences much longer than the rest run as a "
+                         "lead segment and a mapped one)",
+                tokens_per_s=Tt * steps / wall, kernel_ms=kms, single_pass_kernel_ms=kms1,
                 hbm_gbs=round(nbytes / (kms * 1e-3) / 1e9, 1),
                 hbm_frac=round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
 

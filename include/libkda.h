@@ -279,7 +279,15 @@ kda_status_t kda_chunk_fwd_varlen_segmented_f32(const float *q, const float *k, 
  *   it), and a bf16 output is rounded twice (o0, then the sum).  The
  *   workspace also holds m, T_total * H * dk values of the input type:
  *   kda_chunk_segmented_workspace_bytes_ex() gives its size.  Same results as
- *   the two-pass schedule up to rounding.
+ *   the two-pass schedule up to rounding.  With packed sequences, nseg = 0
+ *   asks for two segments per sequence split on the device from cu_seqlens:
+ *   the makespan target (in chunks) is the longer of the second-longest
+ *   sequence and the balanced share (workgroups per head) H sum(chunks) /
+ *   compute units, and only a sequence longer than the target by more than an
+ *   eighth is split, its first `target` chunks as segment 0 and the rest as
+ *   its mapped segment 1, which runs on the compute units that shorter
+ *   sequences free.  (One long sequence among shorter ones then no longer
+ *   sets the time alone.)  Its workspace is that of nseg = 2.
  */
 enum {
     KDA_GATE_CHANNEL = 0,
@@ -337,7 +345,8 @@ size_t kda_chunk_segmented_workspace_bytes(int nseq, int H, int dk, int dv, int 
  * Without KDA_SCHED_MAP_OUTPUTS, kda_chunk_segmented_workspace_bytes(); with
  * it: 4 * nseq * H * nseg * (dv + dk) dk rounded up to 256, plus
  * 4 * nseq * H * nseg * dv * dk rounded up to 256, plus T_total * H * dk
- * values of the input type.  0 for nseg = 1 or invalid arguments.
+ * values of the input type; nseg = 0 with KDA_SCHED_MAP_OUTPUTS counts as 2.
+ * 0 for nseg = 1 or invalid arguments.
  */
 size_t kda_chunk_segmented_workspace_bytes_ex(int nseq, int T_total, int H, int dk, int dv, int nseg,
                                               int variant, int fp32_inputs);

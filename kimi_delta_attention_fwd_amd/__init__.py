@@ -453,7 +453,9 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, C=64, output
     """Chunk prefill of N packed sequences ([1, T_total, H, d] tensors, device cu_seqlens [N+1]).
 
     ``segments`` > 1 cuts every sequence into that many segments run in
-    parallel, with ``schedule`` "two-pass" or "one-pass".
+    parallel, with ``schedule`` "two-pass" or "one-pass"; "auto" splits only
+    the sequences much longer than the rest, on the device (the one-pass
+    schedule with nseg = 0).
     """
     import torch
     f32 = _mode(q)
@@ -471,9 +473,12 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, C=64, output
                    cu_seqlens=torch.int32))
     out = torch.empty((1, T_total, H, dv), dtype=q.dtype, device=q.device)
     sf = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device) if output_final_state else None
-    nseg = int(segments)
-    sched = _schedule(schedule, 1, 1, H, dk, dv, C, f32)
-    if nseg == 1:
+    if segments == "auto":
+        nseg, sched = 0, SCHED_MAP_OUTPUTS
+    else:
+        nseg = int(segments)
+        sched = _schedule(schedule, 1, 1, H, dk, dv, C, f32)
+    if nseg == 1 or N == 0:
         fn = kda_chunk_fwd_varlen_f32 if f32 else kda_chunk_fwd_varlen
         fn(q, k, v, log_alpha, beta, S0, out, sf, cu_seqlens, N, T_total, H, dk, dv, C, stream)
     elif sched:

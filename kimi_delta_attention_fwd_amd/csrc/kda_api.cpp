@@ -329,6 +329,10 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
     if (!valid_variant(variant)) return fail(KDA_ERR_BAD_SHAPE, "invalid variant %d", variant | (mout ? kSchedMapOut : 0));
     if (mout && scratch) return fail(KDA_ERR_UNSUPPORTED, "the allocation-free entry point has no one-pass schedule");
     const int gate = variant & 3;
+    // nseg = 0 with the one-pass schedule and packed sequences: two segments,
+    // only the sequences much longer than the rest split, on the device
+    const bool plan = varlen && mout && nseg == 0 && !scratch;
+    if (plan) nseg = 2;
     if (nseg < 1 || nseg > kMaxSegments)
         return fail(KDA_ERR_BAD_SHAPE, "segment count must be in [1, %d] (got %d)", kMaxSegments, nseg);
     if (nseq < 0 || T < 0 || T_total < 0)
@@ -430,7 +434,7 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
     a.cus = device_cus();
     a.mws = nullptr;
     if (a.mout) {
-        a.lead = seg_lead_mout((long)nheads, dk, dv, BV, nseg, device_cus());
+        a.lead = plan ? -(16 * device_cus() + dv / BV) : seg_lead_mout((long)nheads, dk, dv, BV, nseg, device_cus());
         a.seg_map = (float *)workspace;
         a.seg_start = (float *)((char *)workspace + mout_map_bytes(nheads, dk, dv, nseg));
         a.mws = (char *)workspace + mout_map_bytes(nheads, dk, dv, nseg) + mout_start_bytes(nheads, dk, dv, nseg);
@@ -665,6 +669,7 @@ int kda_chunk_auto_schedule(int B, int T, int H, int dk, int dv, int C, int fp32
 size_t kda_chunk_segmented_workspace_bytes_ex(int nseq, int T_total, int H, int dk, int dv, int nseg, int variant,
                                               int fp32_inputs)
 {
+    if ((variant & kSchedMapOut) && nseg == 0) nseg = 2;   // the device-side split of packed sequences
     if (nseq <= 0 || T_total < 0 || H <= 0 || !supported_d(dk) || !supported_d(dv) || nseg < 1 ||
         nseg > kMaxSegments || !valid_variant(variant & ~kSchedMapOut))
         return 0;

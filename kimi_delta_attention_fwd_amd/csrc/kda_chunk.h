@@ -577,6 +577,38 @@ __device__ __forceinline__ void seg_bounds(long n, int nsegs, int lead, int seg,
     }
 }
 
+// Packed sequences split on the device (the one-pass schedule with two
+// segments and lead = -(16 cus + nvA)): the makespan target, in chunk steps,
+// is the longer of the second-longest sequence and the balanced share
+// nvA H sum(n) / cus; a sequence longer than the target by more than an
+// eighth runs its first `target` chunks as segment 0 and the rest as its
+// mapped segment 1 (whose workgroups start as shorter sequences free their
+// compute units); every other sequence is segment 0 whole.  Returns the
+// chunks of segment 0 of sequence seq.  Every workgroup computes the same plan
+// from the same offsets (clamped to [0, T] as the kernels clamp them).
+__device__ long plan_split(const int *__restrict__ cu_seqlens, int N, int T, int C, int H, int code, int seq)
+{
+    const int cus = (-code) >> 4, nvA = (-code) & 15;
+    long nmax = 0, n2 = 0, sum = 0, mine = 0;
+    long a0 = min(max((long)cu_seqlens[0], 0L), (long)T);
+    for (int i = 0; i < N; ++i) {
+        const long a1 = min(max((long)cu_seqlens[i + 1], a0), (long)T);
+        const long n = (a1 - a0 + C - 1) / C;
+        a0 = a1;
+        sum += n;
+        if (n > nmax) {
+            n2 = nmax;
+            nmax = n;
+        } else if (n > n2) {
+            n2 = n;
+        }
+        if (i == seq) mine = n;
+    }
+    const long share = ((long)nvA * H * sum + cus - 1) / cus;
+    const long tgt = max(n2, share);
+    return mine > tgt + tgt / 8 ? tgt : mine;
+}
+
 // Variants (uniform arguments, read only when VAR): gate 0 = per-channel log_alpha [.., H, DK],
 // 1 = one log_alpha per token and head [.., H] shared by all key channels,
 // 2 = no decay (log_alpha not read); add = 1 replaces the delta write by the
@@ -664,10 +696,12 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     // mout: the map launch of the schedule without a second pass maps every
     // segment after the first and writes their outputs from a zero incoming
     // state (real rows, into out) and those of the virtual rows (into mws)
-    const bool mout = MAP && mout_arg != 0 && lead > 0;
+    const bool mout = MAP && mout_arg != 0 && lead != 0;
     const int nmap = mout ? nsegs - 1 : nsegs - 2;   // mapped segments per sequence beside the lead one
-    if (MAP && lead > 0) {
-        const int nA = (int)(gridDim.x / (nvA + nmap * nvB)) * nvA;
+    int nheads_grid = 0;   // (sequence, head) pairs of the launch, for the device-side split
+    if (MAP && lead != 0) {
+        nheads_grid = (int)(gridDim.x / (nvA + nmap * nvB));
+        const int nA = nheads_grid * nvA;
         int unit;
         if ((int)blockIdx.x < nA) {
             place(blockIdx.x, nvA, xcd_map & 1, unit, vb);
@@ -706,7 +740,13 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         // (10 (nsegs - 1) + lead)) each from the end, segment 0 the rest (about
         // lead / 10 L; none when the sequence is short).
         long c0, c1;
-        seg_bounds((len + C - 1) / C, nsegs, lead, seg, c0, c1);
+        if (lead < 0) {   // two segments, split on the device
+            const long l0 = plan_split(cu_seqlens, nheads_grid / H, T, C, H, lead, seq);
+            c0 = seg == 0 ? 0 : l0;
+            c1 = seg == 0 ? l0 : (len + C - 1) / C;
+        } else {
+            seg_bounds((len + C - 1) / C, nsegs, lead, seg, c0, c1);
+        }
         tok0 += c0 * C;
         len = (CI)max(0L, min((long)len - c0 * C, (c1 - c0) * C));
     }
@@ -1584,10 +1624,14 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 // mout (the schedule without a second pass): every segment p >= 1 has a map,
 // at slot p of nsegs per head, and the last one carries the state on to
 // S_final (skipped when S_final is NULL).
+//
+// Device-side split of packed sequences (lead < 0): a sequence the plan left
+// whole has an identity map; its final state is its incoming slot 1, copied.
 template <int DK>
 __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const float *seg_map,
                                                           float *seg_start, int dv, int nsegs, int p0,
-                                                          int mout, float *S_final)
+                                                          int mout, float *S_final, const int *cu_seqlens,
+                                                          int T, int C, int H, int lead)
 {
     constexpr int NCT = DK / 16;                 // key-channel tiles
     constexpr int TPW = (NCT + 3) / 4;           // tiles per wave, at most
@@ -1627,7 +1671,14 @@ __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const
             if (e < DK * DK) *(f32x4 *)(sM + (e / DK) * PM + e % DK) = ml[j];
         }
     };
-    const bool more = p0 + 1 < nsegs || (mout && S_final);
+    bool whole = false;   // a packed sequence the device-side split left whole
+    if (lead < 0 && cu_seqlens) {
+        const int seq = head / H, N = (int)(gridDim.x / nrb) / H;
+        const long a0 = min(max((long)cu_seqlens[seq], 0L), (long)T);
+        const long a1 = min(max((long)cu_seqlens[seq + 1], a0), (long)T);
+        whole = plan_split(cu_seqlens, N, T, C, H, lead, seq) >= (a1 - a0 + C - 1) / C;
+    }
+    const bool more = !whole && (p0 + 1 < nsegs || (mout && S_final));
     if (more) load_map(p0);
     for (int p = p0;; ++p) {
         __syncthreads();   // the rows of slot p are in sS
@@ -1637,6 +1688,15 @@ __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const
             *(f32x4 *)(seg_start + (((long)head * nsegs + p) * dv + 16 * rb + r) * DK + c) = *(const f32x4 *)(sS + r * PM + c);
         }
         const bool last = p + 1 >= nsegs;
+        if (whole) {   // the incoming slot is the final state
+            if (mout && S_final) {
+                for (int e = 4 * tid; e < 16 * DK; e += 4 * 256) {
+                    const int r = e / DK, c = e % DK;
+                    *(f32x4 *)(S_final + ((long)head * dv + 16 * rb + r) * DK + c) = *(const f32x4 *)(sS + r * PM + c);
+                }
+            }
+            break;
+        }
         if (last && !(mout && S_final)) break;
         store_map();        // M_p (the threads' own loads)
         const bool next = !last && (p + 2 < nsegs || (mout && S_final));
@@ -1722,7 +1782,12 @@ __global__ void __launch_bounds__(256) seg_out_kernel(const In *__restrict__ mws
         len = T;
     }
     long c0, c1;
-    seg_bounds((len + C - 1) / C, nsegs, lead, seg, c0, c1);
+    if (lead < 0) {   // two segments, split on the device
+        c0 = plan_split(cu_seqlens, (int)(gridDim.x / W) / H, T, C, H, lead, seq);
+        c1 = (len + C - 1) / C;
+    } else {
+        seg_bounds((len + C - 1) / C, nsegs, lead, seg, c0, c1);
+    }
     const long s0 = tok0 + c0 * C, s1 = tok0 + min(c1 * C, len);
     if (s1 <= s0) return;
     const int ndv = dv / 16;
@@ -1821,7 +1886,7 @@ hipError_t launch_chunk_t(const ChunkArgs &a)
             return hipErrorInvalidConfiguration;   // the virtual rows fill whole value blocks
         } else {
             const long nvB = (a.dv + DK) / BV;
-            const bool lead = a.lead > 0;
+            const bool lead = a.lead != 0;   // (negative: the device-side split of packed sequences)
             hipError_t e;
             if (lead && a.mout) {
                 // no second pass: the map launch (segment 0's pass, and every later
@@ -1833,12 +1898,16 @@ hipError_t launch_chunk_t(const ChunkArgs &a)
                 if (e != hipSuccess) return e;
                 const long ncomp = (long)a.nseq * a.H * (a.dv / 16);
                 hipLaunchKernelGGL((seg_compose_kernel<DK>), dim3((unsigned)ncomp), dim3(256), 0, a.stream, a.S0,
-                                   (const float *)a.seg_map, a.seg_start, a.dv, a.nsegs, 1, 1, a.S_final);
+                                   (const float *)a.seg_map, a.seg_start, a.dv, a.nsegs, 1, 1, a.S_final,
+                                   a.cu_seqlens, a.T, C, a.H, a.lead);
                 e = hipGetLastError();
                 if (e != hipSuccess) return e;
                 const long units = nheads * (a.nsegs - 1);
-                // about one resident round of workgroups (two per compute unit)
-                const long W = units >= 2L * a.cus ? 1 : (2L * a.cus) / units;
+                // about one resident round of workgroups (two per compute unit);
+                // with the device-side split only the split sequences have work,
+                // and the others' workgroups exit at once
+                long W = units >= 2L * a.cus ? 1 : (2L * a.cus) / units;
+                if (a.lead < 0 && W < 16) W = 16;
                 hipLaunchKernelGGL((seg_out_kernel<In, DK>), dim3((unsigned)(units * W)), dim3(256), 0, a.stream,
                                    (const In *)a.mws, (const float *)a.seg_start, (In *)a.out, a.cu_seqlens, a.T,
                                    a.H, a.dv, C, a.nsegs, a.lead, (int)W);
@@ -1856,7 +1925,8 @@ hipError_t launch_chunk_t(const ChunkArgs &a)
             const long ncomp = (long)a.nseq * a.H * (a.dv / 16);
             if (ncomp > 0) {
                 hipLaunchKernelGGL((seg_compose_kernel<DK>), dim3((unsigned)ncomp), dim3(256), 0, a.stream, a.S0,
-                                   (const float *)a.seg_map, a.seg_start, a.dv, a.nsegs, lead ? 1 : 0, 0, nullptr);
+                                   (const float *)a.seg_map, a.seg_start, a.dv, a.nsegs, lead ? 1 : 0, 0, nullptr,
+                                   nullptr, 0, C, a.H, 0);
                 e = hipGetLastError();
                 if (e != hipSuccess) return e;
             }

@@ -667,6 +667,23 @@ def test_one_pass_varlen_variants_and_deep_decay(dev):
         assert_close(f"one-pass deep {dtype}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
 
 
+@pytest.mark.parametrize("lengths", [[700, 64, 130, 0, 90, 1], [200, 200, 200], [1000, 990, 30]])
+def test_one_pass_varlen_device_split(dev, lengths):
+    """Packed sequences with segments="auto": the one-pass schedule whose
+    split is planned on the device (here the 700-token sequence is split and
+    the others run whole; with equal or two equally long sequences nothing is
+    split and every map is the identity)."""
+    for dtype, C in (("bf16", 32), ("f32", 32)):
+        note(f"case one-pass device split: lengths {lengths} H2 d64 {dtype} C{C}")
+        p = kda_synth.prefill_varlen(lengths, 2, 64, 64, dtype=dtype, s0_sigma=0.1, seed=71, device=dev)
+        out, sf = kda.chunk_fwd_varlen(p.q, p.k, p.v, p.log_alpha, p.beta, p.cu_seqlens, S0=p.S0, C=C,
+                                       segments="auto")
+        torch.cuda.synchronize()
+        o_ref, s_ref = oracle.forward_varlen(f64(p.q), f64(p.k), f64(p.v), f64(p.log_alpha), f64(p.beta),
+                                             np.array(p.cu_host), S0=f64(p.S0))
+        assert_close(f"one-pass device split {dtype}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
+
+
 def test_one_pass_in_place_no_final_state_and_determinism(dev):
     note("case one-pass in place: S_final == S0, S_final not requested, two runs bitwise")
     B, T, H, dk, dv, C, nseg = 1, 800, 2, 128, 128, 64, 3
@@ -958,11 +975,15 @@ def test_varlen_malformed_offsets_stay_in_bounds(dev):
                      o_ref[:, lo:hi], s_ref, TOL["bf16"])
 
 
-def test_varlen_workload_sampled(dev):
+@pytest.mark.parametrize("segments", [1, "auto"])
+def test_varlen_workload_sampled(dev, segments):
+    """The varlen workload in one pass, and with the device-side split of its
+    longest sequence (what bench.py times), on one sampled head per sequence."""
     w = kda_synth.WORKLOADS["varlen"]
-    note("case varlen workload: 8 sequences U[2048,16384] x H16 d128 bf16 C64 (sampled heads)")
+    note(f"case varlen workload: 8 sequences U[2048,16384] x H16 d128 bf16 C64 (sampled heads), segments={segments}")
     p = kda_synth.workload("varlen", device=dev)
-    out, sf = kda.chunk_fwd_varlen(p.q, p.k, p.v, p.log_alpha, p.beta, p.cu_seqlens, S0=p.S0, C=w["C"])
+    out, sf = kda.chunk_fwd_varlen(p.q, p.k, p.v, p.log_alpha, p.beta, p.cu_seqlens, S0=p.S0, C=w["C"],
+                                   segments=segments)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all() and torch.isfinite(sf).all()
     errs_o, errs_s = [], []
