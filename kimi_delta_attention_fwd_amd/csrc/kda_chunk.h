@@ -647,8 +647,9 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     // and the delta write (the usual projection outputs), folded in
     const int gate = VAR == 1 ? gate_arg : 0, add = VAR == 1 ? add_arg : 0;
     const int prep = VAR == 2 ? 1 : (VAR == 1 ? prep_arg : 0);
-    // the raw-input kernel keeps the unpaired layouts (about 1.5% slower with them)
-    typedef ChunkCfg<In, DK, BV, C, VAR != 2> K;
+    // every kernel takes the paired operand layouts (the raw-input one too:
+    // 1.0% faster there on the current kernel, with the paired Ktil^T)
+    typedef ChunkCfg<In, DK, BV, C> K;
     typedef typename V4T<In>::type V4;
     // Chunk indices and lengths are 32-bit (cheaper scalar arithmetic, and
     // fewer scalar registers for the kernel to spill into vector lanes); the
@@ -756,7 +757,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 
     // Ktil^T in the paired order along the tokens (its contraction with E in
     // the state update); not in the map pass, where it timed slower
-    constexpr bool PAIRT = !K::F32 && K::KC == 32 && VAR != 2 && !MAP;
+    constexpr bool PAIRT = !K::F32 && K::KC == 32 && !MAP;
     // The off-diagonal A tiles enter the bf16 solve as one bf16 part.  The
     // raw-input kernel rounds them when it stores them (half the LDS bytes;
     // 1.4% faster there, 1% slower on varlen in the plain kernel, which
