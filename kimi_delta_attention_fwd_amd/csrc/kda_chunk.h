@@ -1804,6 +1804,13 @@ __global__ void __launch_bounds__(256) seg_out_kernel(const In *__restrict__ mws
     const int HDK = H * DK, HDV = H * dv;
     const int es = (int)sizeof(In);
     const long stride = 16L * 4 * W;
+    // bf16 with two or more value tiles: the tiles go in pairs whose A rows are
+    // interleaved (tile 2P row r is S_p row 32 P + 8 (r >> 2) + (r & 3), tile
+    // 2P + 1 the same plus 4), so that lane (n, g) holds 8 consecutive outputs
+    // 32 P + 8 g .. + 7 of token n: 16-byte loads and stores of out
+    const bool pairo = !F32 && ndv >= 2;
+    auto arow = [&](int u, int r) { return pairo ? 32 * (u >> 1) + 8 * (r >> 2) + 4 * (u & 1) + (r & 3) : 16 * u + r; };
+    typedef In V8 __attribute__((ext_vector_type(8)));
     for (long b0 = s0 + 16L * (4 * w + wave); b0 < s1; b0 += NBK * stride) {
         VK bm[NBK][NKS];
         V4 ov[NBK][8];
@@ -1817,19 +1824,33 @@ __global__ void __launch_bounds__(256) seg_out_kernel(const In *__restrict__ mws
 #pragma unroll
             for (int s = 0; s < NKS; ++s) bm[j][s] = buf_load<VK>(rm, (n * HDK + KW * (4 * s + g)) * es, 0);
             ro[j] = buf_rsrc(out + (bb * H + h) * dv, nval * HDV * (unsigned)es);
+            if constexpr (!F32) {
+                if (pairo) {
+#pragma unroll
+                    for (int P = 0; P < 4; ++P)
+                        if (2 * P < ndv) {
+                            const V8 x = buf_load<V8>(ro[j], (n * HDV + 32 * P + 8 * g) * es, 0);
+                            ov[j][2 * P] = __builtin_shufflevector(x, x, 0, 1, 2, 3);
+                            ov[j][2 * P + 1] = __builtin_shufflevector(x, x, 4, 5, 6, 7);
+                        }
+                    continue;
+                }
+            }
 #pragma unroll
             for (int u = 0; u < 8; ++u)
                 if (u < ndv) ov[j][u] = buf_load<V4>(ro[j], (n * HDV + 16 * u + 4 * g) * es, 0);
         }
 #pragma unroll
-        for (int j = 0; j < NBK; ++j)
+        for (int j = 0; j < NBK; ++j) {
+            f32x4 res[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 if (u >= ndv) break;
-                f32x4 acc = to_f32<In>(ov[j][u]);   // out[b0 + j stride + n][16 u + 4 g + i]
+                f32x4 acc = to_f32<In>(ov[j][u]);   // out[b0 + j stride + n][arow(u, 4 g + i)]
+                const In *ar = sS + arow(u, n) * PS;
 #pragma unroll
                 for (int s = 0; s < NKS; ++s) {
-                    const VK a = *(const VK *)(sS + (16 * u + n) * PS + KW * (4 * s + g));
+                    const VK a = *(const VK *)(ar + KW * (4 * s + g));
                     if constexpr (K8) {
                         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bm[j][s], acc, 0, 0, 0);
                     } else if constexpr (!F32) {
@@ -1840,8 +1861,24 @@ __global__ void __launch_bounds__(256) seg_out_kernel(const In *__restrict__ mws
                         for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], bm[j][s][e], acc, 0, 0, 0);
                     }
                 }
-                buf_store(to_op<In>(acc), ro[j], (n * HDV + 16 * u + 4 * g) * es, 0);
+                res[u] = acc;
             }
+            if constexpr (!F32) {
+                if (pairo) {
+#pragma unroll
+                    for (int P = 0; P < 4; ++P)
+                        if (2 * P < ndv) {
+                            const V4 lo = to_op<In>(res[2 * P]), hi = to_op<In>(res[2 * P + 1]);
+                            buf_store(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), ro[j],
+                                      (n * HDV + 32 * P + 8 * g) * es, 0);
+                        }
+                    continue;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (u < ndv) buf_store(to_op<In>(res[u]), ro[j], (n * HDV + 16 * u + 4 * g) * es, 0);
+        }
     }
 }
 
