@@ -1656,7 +1656,14 @@ __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const
     }
     // map loads: element 4 (tid + 256 j) of M, row-major [DK][DK]
     f32x4 ml[NLDX];
+    f32x4 nl[TPW];   // and this wave's tiles of N_p's rows 16 rb ..
     auto load_map = [&](int p) __attribute__((always_inline)) {
+        const float *Np = seg_map + ((long)head * mstride + p) * (dv + DK) * DK + (long)(16 * rb) * DK;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int ct = wave + 4 * u;
+            if (ct < NCT) nl[u] = *(const f32x4 *)(Np + (long)n * DK + 16 * ct + 4 * g);
+        }
         const float *M = seg_map + ((long)head * mstride + p) * (dv + DK) * DK + (long)dv * DK;
         if constexpr (NLD > 0) {
 #pragma unroll
@@ -1700,17 +1707,19 @@ __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const
         }
         if (last && !(mout && S_final)) break;
         store_map();        // M_p (the threads' own loads)
+        f32x4 ncur[TPW];
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) ncur[u] = nl[u];
         const bool next = !last && (p + 2 < nsegs || (mout && S_final));
         if (next) load_map(p + 1);   // in flight across this step
         __syncthreads();
-        const float *Np = seg_map + ((long)head * mstride + p) * (dv + DK) * DK + (long)(16 * rb) * DK;
         f32x4 acc[TPW];
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             const int ct = wave + 4 * u;
             if (ct >= NCT) break;
             // D^T tile: lane (n, g) accumulates s_new[n][16 ct + 4 g + i]
-            acc[u] = *(const f32x4 *)(Np + (long)n * DK + 16 * ct + 4 * g);
+            acc[u] = ncur[u];
 #pragma unroll
             for (int t = 0; t < NCT; ++t) {
                 const f32x4 b = *(const f32x4 *)(sS + n * PM + 16 * t + 4 * g);   // s[n][16 t + 4 g + i]
