@@ -633,6 +633,13 @@ __device__ long plan_split(const int *__restrict__ cu_seqlens, int N, int T, int
 // and q is not read.  With a lead segment the launch's first workgroups run
 // segment 0 as a plain pass instead (a runtime flag, folded away when MAP is
 // false): from S0, writing its outputs and seg_start[(head, 1)].
+// MAP = true with mout_arg (the schedule without a second pass, lead != 0):
+// every segment after the first is mapped, at slot seg of nsegs per head, and
+// its maps also read q and write outputs from the zero incoming state: the real
+// rows' into out, the virtual rows' (their readouts S q) into mws [tokens, H,
+// DK].  lead < 0 (-(16 cus + value blocks per head)): packed sequences in two
+// segments, split on the device (plan_split).  (hard_block_fn's `map` argument
+// means "no outputs, q not read" and receives noout.)
 template <typename In, int DK, int BV, int C, bool MAP, int VAR>
 __global__ void __launch_bounds__((ChunkCfg<In, DK, BV, C>::NT), 1)
 chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,

@@ -14,7 +14,8 @@ struct ChunkArgs {
     const int *cu_seqlens;   // device; NULL for the dense [B, T, H, d] layout
     int nseq, T, H, dk, dv, C, BV;   // T: tokens per sequence, or T_total with cu_seqlens
     // segment-parallel schedule (nsegs > 1): caller-owned workspace,
-    // seg_map [nseq*H][nsegs-1][dv+dk][dk] and seg_start [nseq*H][nsegs][dv][dk] fp32
+    // seg_map [nseq*H][nsegs-1][dv+dk][dk] (mout: [nseq*H][nsegs][dv+dk][dk], slot 0
+    // unused) and seg_start [nseq*H][nsegs][dv][dk] fp32
     int nsegs;
     float *seg_map, *seg_start;
     // lead > 0: segment 0 is about lead / 10 times as long as each later one and
