@@ -1315,11 +1315,12 @@ def test_stream_copy_is_exact(dev, n16):
 
 
 def test_graph_capture_replays_match_eager(dev):
-    """Decode steps, a multi-token launch and chunk prefills (single pass and
-    segmented, whose three launches share a workspace) captured in one HIP
-    graph: every replay gives the eager result bit for bit, with eager work
-    and synchronisation between the replays."""
-    note("case HIP graph: 3 decode steps, multi T4, chunk single pass + 3 segments")
+    """Decode steps, a multi-token launch and chunk prefills (single pass, the
+    two segmented schedules, whose three launches share a workspace, and the
+    device-side split of packed sequences) captured in one HIP graph: every
+    replay gives the eager result bit for bit, with eager work and
+    synchronisation between the replays."""
+    note("case HIP graph: 3 decode steps, multi T4, chunk single pass + 3 segments two- and one-pass + varlen split")
     bf = torch.bfloat16
     N, H, dk, dv = 8, 4, 128, 128
     d = kda_synth.decode(N, H, dk, dv, 3, seed=71, device=dev)
@@ -1328,11 +1329,19 @@ def test_graph_capture_replays_match_eager(dev):
     S_dec, S_multi = torch.empty_like(d.S0), torch.empty_like(pm.S0)
     outs = [torch.empty((N, H, dv), dtype=bf, device=dev) for _ in range(3)]
     out_m = torch.empty((N, 4, H, dv), dtype=bf, device=dev)
-    out_c = [torch.empty_like(pc.v) for _ in range(2)]
-    sf_c = [torch.empty_like(pc.S0) for _ in range(2)]
+    out_c = [torch.empty_like(pc.v) for _ in range(3)]
+    sf_c = [torch.empty_like(pc.S0) for _ in range(3)]
     nseg = 3
     ws_bytes = kda.kda_chunk_segmented_workspace_bytes(1, 2, 64, 64, nseg)
     ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device=dev)
+    one = kda.variant(schedule="one-pass")
+    ws1_bytes = kda.kda_chunk_segmented_workspace_bytes_ex(1, 300, 2, 64, 64, nseg, one, False)
+    ws1 = torch.empty(ws1_bytes // 4 + 64, dtype=torch.float32, device=dev)
+    pv = kda_synth.prefill_varlen([500, 40, 90], 2, 64, 64, dtype="bf16", s0_sigma=0.1, seed=74, device=dev)
+    Tv, Nv = pv.cu_host[-1], len(pv.cu_host) - 1
+    out_v, sf_v = torch.empty_like(pv.v), torch.empty_like(pv.S0)
+    wsv_bytes = kda.kda_chunk_segmented_workspace_bytes_ex(Nv, Tv, 2, 64, 64, 0, one, False)
+    wsv = torch.empty(wsv_bytes // 4 + 64, dtype=torch.float32, device=dev)
 
     def work():   # on the current stream (the capture stream inside the graph context)
         for t in range(3):
@@ -1341,8 +1350,12 @@ def test_graph_capture_replays_match_eager(dev):
         kda.kda_chunk_fwd(pc.q, pc.k, pc.v, pc.log_alpha, pc.beta, pc.S0, out_c[0], sf_c[0], 1, 300, 2, 64, 64, 64)
         kda.kda_chunk_fwd_segmented(pc.q, pc.k, pc.v, pc.log_alpha, pc.beta, pc.S0, out_c[1], sf_c[1],
                                     1, 300, 2, 64, 64, 64, nseg, ws, ws_bytes)
+        kda.kda_chunk_fwd_ex(pc.q, pc.k, pc.v, pc.log_alpha, pc.beta, pc.S0, out_c[2], sf_c[2],
+                             1, 300, 2, 64, 64, 64, one, nseg, ws1, ws1_bytes)
+        kda.kda_chunk_fwd_varlen_ex(pv.q, pv.k, pv.v, pv.log_alpha, pv.beta, pv.S0, out_v, sf_v, pv.cu_seqlens, Nv,
+                                    Tv, 2, 64, 64, 32, one, 0, wsv, wsv_bytes)
 
-    results = lambda: [S_dec, S_multi, out_m] + outs + out_c + sf_c
+    results = lambda: [S_dec, S_multi, out_m] + outs + out_c + sf_c + [out_v, sf_v]
     S_dec.copy_(d.S0)
     S_multi.copy_(pm.S0)
     work()
@@ -1354,9 +1367,10 @@ def test_graph_capture_replays_match_eager(dev):
     for replay in range(3):
         S_dec.copy_(d.S0)   # eager work between the replays
         S_multi.copy_(pm.S0)
-        for x in [out_m] + outs + out_c + sf_c:
+        for x in [out_m] + outs + out_c + sf_c + [out_v, sf_v]:
             x.fill_(float("nan"))
-        ws.fill_(7.0)
+        for w in (ws, ws1, wsv):
+            w.fill_(7.0)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
