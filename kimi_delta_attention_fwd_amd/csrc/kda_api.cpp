@@ -253,8 +253,15 @@ int seg_lead_mout(long nheads, int dk, int dv, int bv, int nseg, int cus)
 // Schedule without a second pass (mout): the map launch takes max(L0 + 1,
 // rounds (L + 1)) steps (its map chunks, which also form the outputs, cost
 // about a full chunk), the composition as above, and the epilogue streams m
-// and out once: about one step per 16 MB (fitted to B=1 H=16 T=65536 d=128,
-// 8 segments: 1.15 ms, and 7 and 9 segments within 5%).
+// and out once: about one step per 20 MB.  Fitted to measured runs (ms, the
+// model's segment count marked *): B=1 H=16 T=65536 d=128: one-pass 8* 1.11,
+// two-pass 9 1.23; B=2 H=16 T=32768 d=128: one-pass 4* 0.97, two-pass 5 1.04
+// (the one shape where the schedule comparison misses: the models put the
+// two within 1% and pick the two-pass one);
+// B=1 H=16 T=65536 d=64: one-pass 8* 0.52, two-pass 16 0.59; B=1 H=8
+// T=131072 d=128: one-pass 8* 1.24, two-pass 16 1.43; fp32 B=1 H=16 T=65536
+// d=128: one-pass 8* 3.69, two-pass 9 4.07 (one segment fewer or more: slower
+// in every case).
 double auto_cost(bool f32, int B, int T, int H, int dk, int dv, int C, bool mout, int &best_s)
 {
     best_s = 1;
@@ -277,7 +284,7 @@ double auto_cost(bool f32, int B, int T, int H, int dk, int dv, int C, bool mout
             const long L0 = nch - (s - 1) * L > 0 ? nch - (s - 1) * L : 0;
             const long g1 = nheads * ((s - 1) * nvB + nvA);
             const double map = (double)map_launch_rounds(g1, nheads * nvA, cus) * (double)(L + 1);
-            const double epi = (double)B * (double)T * (double)H * (double)(dk + 2 * dv) * (f32 ? 4.0 : 2.0) / 16e6;
+            const double epi = (double)B * (double)T * (double)H * (double)(dk + 2 * dv) * (f32 ? 4.0 : 2.0) / 20e6;
             cost = (map > (double)(L0 + 1) ? map : (double)(L0 + 1)) + 0.3 * std::pow(dk / 64.0, 1.5) * s + epi + 1.0;
         } else {
             const int lead = seg_lead(nheads, dk, dv, bv, s, cus);

@@ -218,6 +218,26 @@ def test_auto_segments_model(lib):
     assert kda.kda_chunk_auto_segments(1, 64, 1, 48, 64, 64, False) == 1
 
 
+def test_auto_schedule_model(lib):
+    """The one-pass schedule's model picks the measured best segment count on
+    every shape timed on one MI355X (ms: B1 T65536 H16 d128 one-pass 7/8/9 =
+    1.33/1.11/1.43; B1 T65536 H16 d64 0.58/0.52/0.76; B2 T32768 H16 d128
+    4 -> 0.97 against 1.14 and 1.04 for 3 and 5; B1 T131072 H8 d128 8 -> 1.24;
+    fp32 B1 T65536 H16 d128 8 -> 3.69), and kda_chunk_auto_schedule picks it
+    over the two-pass schedule where it measured faster, except B2 T32768 H16,
+    where the two models come within 1% (measured 0.97 against 1.04 ms)."""
+    one = 16
+    for (B, T, H, d, f32), nseg, sched in (((1, 65536, 16, 128, False), 8, one), ((1, 65536, 16, 64, False), 8, one),
+                                           ((2, 32768, 16, 128, False), 4, 0), ((1, 131072, 8, 128, False), 8, one),
+                                           ((1, 65536, 16, 128, True), 8, one), ((2, 1024, 4, 64, False), 8, one)):
+        assert kda.kda_chunk_auto_segments_ex(B, T, H, d, d, 64, f32, one) == nseg, (B, T, H, d, f32)
+        assert kda.kda_chunk_auto_schedule(B, T, H, d, d, 64, f32) == sched, (B, T, H, d, f32)
+    # without the schedule bit: the two-pass model
+    assert kda.kda_chunk_auto_segments_ex(1, 65536, 16, 128, 128, 64, False, 0) == 9
+    # the mid workload fills the GPU in one pass: no segmented schedule
+    assert kda.kda_chunk_auto_schedule(4, 8192, 32, 128, 128, 64, False) == 0
+
+
 def test_segmented_validation(lib):
     assert seg(lib, nseg=0) == 2
     assert seg(lib, nseg=1025) == 2
