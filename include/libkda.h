@@ -287,7 +287,8 @@ kda_status_t kda_chunk_fwd_varlen_segmented_f32(const float *q, const float *k, 
  *   eighth is split, its first `target` chunks as segment 0 and the rest as
  *   its mapped segment 1, which runs on the compute units that shorter
  *   sequences free.  (One long sequence among shorter ones then no longer
- *   sets the time alone.)  Its workspace is that of nseg = 2.
+ *   sets the time alone.)  The plan is made once per call by one workgroup
+ *   and kept in the workspace: that of nseg = 2 plus 4 * N bytes.
  */
 enum {
     KDA_GATE_CHANNEL = 0,
@@ -345,7 +346,8 @@ size_t kda_chunk_segmented_workspace_bytes(int nseq, int H, int dk, int dv, int 
  * Without KDA_SCHED_MAP_OUTPUTS, kda_chunk_segmented_workspace_bytes(); with
  * it: 4 * nseq * H * nseg * (dv + dk) dk rounded up to 256, plus
  * 4 * nseq * H * nseg * dv * dk rounded up to 256, plus T_total * H * dk
- * values of the input type; nseg = 0 with KDA_SCHED_MAP_OUTPUTS counts as 2.
+ * values of the input type; nseg = 0 with KDA_SCHED_MAP_OUTPUTS (packed
+ * sequences split on the device) is nseg = 2 plus 4 * nseq bytes for the plan.
  * 0 for nseg = 1 or invalid arguments.
  */
 size_t kda_chunk_segmented_workspace_bytes_ex(int nseq, int T_total, int H, int dk, int dv, int nseg,

@@ -380,7 +380,8 @@ kda_status_t chunk_common(bool f32, bool varlen, const void *q, const void *k, c
                                      Buf{S_final, S_final ? ns * 4 : 0, "S_final"},
                                      Buf{S0, S0 ? ns * 4 : 0, "S0"});
     if (st != KDA_OK) return st;
-    const uint64_t wsb = mout ? mout_workspace_bytes(nheads, ntok * H, dk, dv, nseg, f32 ? 4 : 2)
+    // (the device-side split also keeps its plan, one int per sequence, after m)
+    const uint64_t wsb = mout ? mout_workspace_bytes(nheads, ntok * H, dk, dv, nseg, f32 ? 4 : 2) + (plan ? 4u * (uint64_t)nseq : 0u)
                               : seg_workspace_bytes(nheads, dk, dv, nseg);
     if (nseg > 1 && scratch) {
         // the library's own fixed-size array: it aliases nothing the caller owns
@@ -676,13 +677,15 @@ int kda_chunk_auto_schedule(int B, int T, int H, int dk, int dv, int C, int fp32
 size_t kda_chunk_segmented_workspace_bytes_ex(int nseq, int T_total, int H, int dk, int dv, int nseg, int variant,
                                               int fp32_inputs)
 {
-    if ((variant & kSchedMapOut) && nseg == 0) nseg = 2;   // the device-side split of packed sequences
+    const bool plan = (variant & kSchedMapOut) && nseg == 0;   // the device-side split of packed sequences
+    if (plan) nseg = 2;
     if (nseq <= 0 || T_total < 0 || H <= 0 || !supported_d(dk) || !supported_d(dv) || nseg < 1 ||
         nseg > kMaxSegments || !valid_variant(variant & ~kSchedMapOut))
         return 0;
     const uint64_t nheads = (uint64_t)nseq * (uint64_t)H;
     if (variant & kSchedMapOut)
-        return (size_t)mout_workspace_bytes(nheads, (uint64_t)T_total * (uint64_t)H, dk, dv, nseg, fp32_inputs ? 4 : 2);
+        return (size_t)(mout_workspace_bytes(nheads, (uint64_t)T_total * (uint64_t)H, dk, dv, nseg, fp32_inputs ? 4 : 2) +
+                        (plan ? 4u * (uint64_t)nseq : 0u));
     return (size_t)seg_workspace_bytes(nheads, dk, dv, nseg);
 }
 

@@ -583,30 +583,53 @@ __device__ __forceinline__ void seg_bounds(long n, int nsegs, int lead, int seg,
 // nvA H sum(n) / cus; a sequence longer than the target by more than an
 // eighth runs its first `target` chunks as segment 0 and the rest as its
 // mapped segment 1 (whose workgroups start as shorter sequences free their
-// compute units); every other sequence is segment 0 whole.  Returns the
-// chunks of segment 0 of sequence seq.  Every workgroup computes the same plan
-// from the same offsets (clamped to [0, T] as the kernels clamp them).
-__device__ long plan_split(const int *__restrict__ cu_seqlens, int N, int T, int C, int H, int code, int seq)
+// compute units); every other sequence is segment 0 whole.  One workgroup
+// writes plan[i], the chunks of segment 0 of sequence i, for the launches
+// that follow (offsets clamped to [0, T] as the kernels clamp them; any value
+// there is safe: the kernels clamp each segment to their own sequence).
+// (A template only so that every translation unit may hold its copy.)
+template <int UNUSED = 0>
+__global__ void __launch_bounds__(256) seg_plan_kernel(const int *__restrict__ cu_seqlens, int N, int T, int C,
+                                                       int H, int code, int *__restrict__ plan)
 {
-    const int cus = (-code) >> 4, nvA = (-code) & 15;
-    long nmax = 0, n2 = 0, sum = 0, mine = 0;
-    long a0 = min(max((long)cu_seqlens[0], 0L), (long)T);
-    for (int i = 0; i < N; ++i) {
+    __shared__ long s_sum[256], s_m1[256], s_m2[256];
+    const int tid = threadIdx.x;
+    auto chunks = [&](int i) {
+        const long a0 = min(max((long)cu_seqlens[i], 0L), (long)T);
         const long a1 = min(max((long)cu_seqlens[i + 1], a0), (long)T);
-        const long n = (a1 - a0 + C - 1) / C;
-        a0 = a1;
+        return (a1 - a0 + C - 1) / C;
+    };
+    long sum = 0, m1 = 0, m2 = 0;   // this thread's sum and two largest
+    for (int i = tid; i < N; i += 256) {
+        const long n = chunks(i);
         sum += n;
-        if (n > nmax) {
-            n2 = nmax;
-            nmax = n;
-        } else if (n > n2) {
-            n2 = n;
+        if (n > m1) {
+            m2 = m1;
+            m1 = n;
+        } else if (n > m2) {
+            m2 = n;
         }
-        if (i == seq) mine = n;
     }
-    const long share = ((long)nvA * H * sum + cus - 1) / cus;
-    const long tgt = max(n2, share);
-    return mine > tgt + tgt / 8 ? tgt : mine;
+    s_sum[tid] = sum;
+    s_m1[tid] = m1;
+    s_m2[tid] = m2;
+    __syncthreads();
+    for (int d = 128; d > 0; d >>= 1) {
+        if (tid < d) {
+            const long a1 = s_m1[tid], a2 = s_m2[tid], b1 = s_m1[tid + d], b2 = s_m2[tid + d];
+            s_sum[tid] += s_sum[tid + d];
+            s_m1[tid] = max(a1, b1);
+            s_m2[tid] = a1 >= b1 ? max(a2, b1) : max(a1, b2);
+        }
+        __syncthreads();
+    }
+    const int cus = (-code) >> 4, nvA = (-code) & 15;
+    const long share = ((long)nvA * H * s_sum[0] + cus - 1) / cus;
+    const long tgt = max(s_m2[0], share);
+    for (int i = tid; i < N; i += 256) {
+        const long n = chunks(i);
+        plan[i] = (int)(n > tgt + tgt / 8 ? tgt : n);
+    }
 }
 
 // Variants (uniform arguments, read only when VAR): gate 0 = per-channel log_alpha [.., H, DK],
@@ -638,7 +661,7 @@ __device__ long plan_split(const int *__restrict__ cu_seqlens, int N, int T, int
 // its maps also read q and write outputs from the zero incoming state: the real
 // rows' into out, the virtual rows' (their readouts S q) into mws [tokens, H,
 // DK].  lead < 0 (-(16 cus + value blocks per head)): packed sequences in two
-// segments, split on the device (plan_split).  (hard_block_fn's `map` argument
+// segments, split on the device (seg_plan_kernel; the plan follows m in mws).  (hard_block_fn's `map` argument
 // means "no outputs, q not read" and receives noout.)
 template <typename In, int DK, int BV, int C, bool MAP, int VAR>
 __global__ void __launch_bounds__((ChunkCfg<In, DK, BV, C>::NT), 1)
@@ -749,7 +772,7 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
         // lead / 10 L; none when the sequence is short).
         long c0, c1;
         if (lead < 0) {   // two segments, split on the device
-            const long l0 = plan_split(cu_seqlens, nheads_grid / H, T, C, H, lead, seq);
+            const long l0 = ((const int *)(mws + (long)T * H * DK))[seq];   // the plan, after m
             c0 = seg == 0 ? 0 : l0;
             c1 = seg == 0 ? l0 : (len + C - 1) / C;
         } else {
@@ -1633,13 +1656,13 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
 // at slot p of nsegs per head, and the last one carries the state on to
 // S_final (skipped when S_final is NULL).
 //
-// Device-side split of packed sequences (lead < 0): a sequence the plan left
-// whole has an identity map; its final state is its incoming slot 1, copied.
+// Device-side split of packed sequences (plan non-NULL): a sequence the plan
+// left whole has an identity map; its final state is its incoming slot 1, copied.
 template <int DK>
 __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const float *seg_map,
                                                           float *seg_start, int dv, int nsegs, int p0,
                                                           int mout, float *S_final, const int *cu_seqlens,
-                                                          int T, int C, int H, int lead)
+                                                          int T, int C, int H, const int *plan)
 {
     constexpr int NCT = DK / 16;                 // key-channel tiles
     constexpr int TPW = (NCT + 3) / 4;           // tiles per wave, at most
@@ -1687,11 +1710,11 @@ __global__ void __launch_bounds__(256) seg_compose_kernel(const float *S0, const
         }
     };
     bool whole = false;   // a packed sequence the device-side split left whole
-    if (lead < 0 && cu_seqlens) {
-        const int seq = head / H, N = (int)(gridDim.x / nrb) / H;
+    if (plan) {
+        const int seq = head / H;
         const long a0 = min(max((long)cu_seqlens[seq], 0L), (long)T);
         const long a1 = min(max((long)cu_seqlens[seq + 1], a0), (long)T);
-        whole = plan_split(cu_seqlens, N, T, C, H, lead, seq) >= (a1 - a0 + C - 1) / C;
+        whole = plan[seq] >= (a1 - a0 + C - 1) / C;
     }
     const bool more = !whole && (p0 + 1 < nsegs || (mout && S_final));
     if (more) load_map(p0);
@@ -1800,7 +1823,7 @@ __global__ void __launch_bounds__(256) seg_out_kernel(const In *__restrict__ mws
     }
     long c0, c1;
     if (lead < 0) {   // two segments, split on the device
-        c0 = plan_split(cu_seqlens, (int)(gridDim.x / W) / H, T, C, H, lead, seq);
+        c0 = ((const int *)(mws + (long)T * H * DK))[seq];   // the plan, after m
         c1 = (len + C - 1) / C;
     } else {
         seg_bounds((len + C - 1) / C, nsegs, lead, seg, c0, c1);
@@ -1947,13 +1970,20 @@ hipError_t launch_chunk_t(const ChunkArgs &a)
                 // segment's map with its outputs from a zero state), the
                 // composition (through S_final), then the output epilogue
                 const long unitsB = nheads * (a.nsegs - 1);
+                const int *plan = a.lead < 0 ? (const int *)((const In *)a.mws + (long)a.T * a.H * DK) : nullptr;
+                if (plan) {   // packed sequences: the device-side split, once
+                    hipLaunchKernelGGL(seg_plan_kernel<0>, dim3(1), dim3(256), 0, a.stream, a.cu_seqlens, a.nseq, a.T, C,
+                                       a.H, a.lead, (int *)plan);
+                    e = hipGetLastError();
+                    if (e != hipSuccess) return e;
+                }
                 e = launch_chunk_grid<In, DK, BV, C, true>(a, nheads * nvA + unitsB * nvB,
                                                             (nheads % 8 == 0 ? 1 : 0) | (unitsB % 8 == 0 ? 2 : 0));
                 if (e != hipSuccess) return e;
                 const long ncomp = (long)a.nseq * a.H * (a.dv / 16);
                 hipLaunchKernelGGL((seg_compose_kernel<DK>), dim3((unsigned)ncomp), dim3(256), 0, a.stream, a.S0,
                                    (const float *)a.seg_map, a.seg_start, a.dv, a.nsegs, 1, 1, a.S_final,
-                                   a.cu_seqlens, a.T, C, a.H, a.lead);
+                                   a.cu_seqlens, a.T, C, a.H, plan);
                 e = hipGetLastError();
                 if (e != hipSuccess) return e;
                 const long units = nheads * (a.nsegs - 1);
@@ -1980,7 +2010,7 @@ hipError_t launch_chunk_t(const ChunkArgs &a)
             if (ncomp > 0) {
                 hipLaunchKernelGGL((seg_compose_kernel<DK>), dim3((unsigned)ncomp), dim3(256), 0, a.stream, a.S0,
                                    (const float *)a.seg_map, a.seg_start, a.dv, a.nsegs, lead ? 1 : 0, 0, nullptr,
-                                   nullptr, 0, C, a.H, 0);
+                                   nullptr, 0, C, a.H, nullptr);
                 e = hipGetLastError();
                 if (e != hipSuccess) return e;
             }

@@ -320,6 +320,10 @@ def test_one_pass_workspace_bytes(lib):
         assert kda.kda_chunk_segmented_workspace_bytes_ex(nseq, T, H, dk, dv, nseg, 16, f32) == want
         assert kda.kda_chunk_segmented_workspace_bytes_ex(nseq, T, H, dk, dv, nseg, 0, f32) == \
             kda.kda_chunk_segmented_workspace_bytes(nseq, H, dk, dv, nseg)
+    # nseg = 0 (packed sequences split on the device): two segments and the plan, one int per sequence
+    assert kda.kda_chunk_segmented_workspace_bytes_ex(5, 1000, 2, 64, 64, 0, 16, False) == \
+        kda.kda_chunk_segmented_workspace_bytes_ex(5, 1000, 2, 64, 64, 2, 16, False) + 4 * 5
+    assert kda.kda_chunk_segmented_workspace_bytes_ex(5, 1000, 2, 64, 64, 0, 0, False) == 0
     assert kda.kda_chunk_segmented_workspace_bytes_ex(1, 100, 2, 64, 64, 1, 16, False) == 0
     assert kda.kda_chunk_segmented_workspace_bytes_ex(1, 100, 2, 48, 64, 4, 16, False) == 0
     assert kda.kda_chunk_segmented_workspace_bytes_ex(1, 100, 2, 64, 64, 4, 32, False) == 0

@@ -684,6 +684,23 @@ def test_one_pass_varlen_device_split(dev, lengths):
         assert_close(f"one-pass device split {dtype}", f64(out), f64(sf), o_ref, s_ref, TOL[dtype])
 
 
+def test_one_pass_varlen_device_split_many_sequences(dev):
+    """The plan of the device-side split made by one workgroup over more
+    sequences than it has threads (reductions across threads): 600 short
+    sequences and two long ones, one of which is split."""
+    rng = np.random.default_rng(81)
+    lengths = [int(x) for x in rng.integers(0, 40, size=600)]
+    lengths[123] = 2000
+    lengths[480] = 700
+    note(f"case one-pass device split, {len(lengths)} sequences (two long: 2000 and 700 tokens) H1 d32 bf16 C32")
+    p = kda_synth.prefill_varlen(lengths, 1, 32, 32, dtype="bf16", s0_sigma=0.1, seed=82, device=dev)
+    out, sf = kda.chunk_fwd_varlen(p.q, p.k, p.v, p.log_alpha, p.beta, p.cu_seqlens, S0=p.S0, C=32, segments="auto")
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.forward_varlen(f64(p.q), f64(p.k), f64(p.v), f64(p.log_alpha), f64(p.beta),
+                                         np.array(p.cu_host), S0=f64(p.S0))
+    assert_close("one-pass device split, many sequences", f64(out), f64(sf), o_ref, s_ref, TOL["bf16"])
+
+
 def test_one_pass_in_place_no_final_state_and_determinism(dev):
     note("case one-pass in place: S_final == S0, S_final not requested, two runs bitwise")
     B, T, H, dk, dv, C, nseg = 1, 800, 2, 128, 128, 64, 3
