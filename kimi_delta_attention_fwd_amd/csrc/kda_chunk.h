@@ -794,10 +794,12 @@ chunk_fwd_kernel(const In *__restrict__ q, const In *__restrict__ k, const In *_
     // rounds them in the solve instead: the same bits either way).
     constexpr bool ABF = !K::F32 && VAR == 2;
     // The operand waves form the diagonal P tiles along with the diagonal A
-    // tiles (always with a single state wave; with more, except in the
-    // raw-input kernel, where that timed 1.4% slower: there the state waves
-    // take them with their off-diagonal pairs)
-    constexpr bool DPOP = K::NBV == 1 || VAR != 2;
+    // tiles (always with a single state wave; with more, in the plain kernel
+    // and the variants' map pass).  The raw-input kernel and the variants'
+    // single pass leave them to the state waves, with their off-diagonal
+    // pairs: 1.4% and 2.7% faster there, and the variant kernel then fits its
+    // registers without a spill.
+    constexpr bool DPOP = K::NBV == 1 || VAR == 0 || (VAR == 1 && MAP);
     // LDS column of channel c of a [token, d_k] operand
     auto kcol = [&](int c) { return K::PAIRK ? K::pair_pos(c) : c; };
     // Fragments of one row of a [token, d_k] operand: x[t] = channels

@@ -108,11 +108,12 @@ def kernel_metadata():
 
 # Instantiations on the measured paths, by the start of their mangled names:
 # chunk_fwd_kernel<In, DK, BV, C, MAP, VAR> (bf16, d_k = 128, BV = 64, C = 64:
-# the plain single pass, the raw-input single pass, the plain map pass; fp32
-# at d_k = 64), the composition and output epilogue of the segmented
-# schedules, and the decode kernels.
+# the plain single pass, the variant and raw-input single passes, the plain
+# map pass; fp32 at d_k = 64), the composition and output epilogue of the
+# segmented schedules, and the decode kernels.
 HOT = [
     "_ZN3kda16chunk_fwd_kernelIDF16bLi128ELi64ELi64ELb0ELi0E",
+    "_ZN3kda16chunk_fwd_kernelIDF16bLi128ELi64ELi64ELb0ELi1E",
     "_ZN3kda16chunk_fwd_kernelIDF16bLi128ELi64ELi64ELb0ELi2E",
     "_ZN3kda16chunk_fwd_kernelIDF16bLi128ELi64ELi64ELb1ELi0E",
     "_ZN3kda16chunk_fwd_kernelIfLi64ELi64ELi64ELb0ELi0E",
