@@ -1057,6 +1057,37 @@ def test_prep_workload_sampled(dev, dtype):
     assert_close(f"prep sampled {dtype}", o_gpu, s_gpu, o_ref, s_ref, TOL[dtype])
 
 
+@pytest.mark.parametrize("segments", [1, 4])
+def test_scalar_gate_workload_sampled(dev, segments):
+    """The general variant kernel at the mid sizes, with one decay per token
+    and head (the scalar gate): the single pass, and the one-pass segmented
+    schedule with 4 segments (the variant map pass, its outputs and the
+    epilogue), sampled heads against the oracle with the gate broadcast over
+    the key channels."""
+    w = kda_synth.WORKLOADS["mid"]
+    B, T, H, dk, dv, C = w["B"], w["T"], w["H"], w["dk"], w["dv"], w["C"]
+    note(f"case scalar gate at mid sizes: B4 H32 T8192 d128, {segments} segment(s) (4 sampled heads)")
+    p = kda_synth.workload("mid", device=dev)
+    la = p.log_alpha[..., 0].contiguous()   # [B, T, H]
+    out = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    sf = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    var = kda.variant(gate="scalar", schedule="one-pass" if segments > 1 else "two-pass")
+    ws, wsb = None, 0
+    if segments > 1:
+        wsb = kda.kda_chunk_segmented_workspace_bytes_ex(B, B * T, H, dk, dv, segments, var, False)
+        assert wsb > 0
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    kda.kda_chunk_fwd_ex(p.q, p.k, p.v, la, p.beta, None, out, sf, B, T, H, dk, dv, C, var, segments, ws, wsb)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(sf).all()
+    pairs = [(0, 5), (1, 17), (2, 30), (3, 8)]
+    ref = kda_synth.Prefill(p.q, p.k, p.v, la[..., None].expand(B, T, H, dk), p.beta, None)
+    o_ref, s_ref = sampled(ref, pairs)
+    o_gpu = np.stack([f64(out[b, :, h]) for b, h in pairs])[:, :, None]
+    s_gpu = np.stack([f64(sf[b, h]) for b, h in pairs])[:, None]
+    assert_close(f"scalar gate sampled, {segments} segment(s)", o_gpu, s_gpu, o_ref, s_ref, TOL["bf16"])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_decode_multi_workload_sampled(dev, dtype):
     """The multi-token launch the bench times: the decode workload's sizes
